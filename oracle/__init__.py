@@ -1,0 +1,118 @@
+"""CPU oracle for the SSM layer -- TEST INFRASTRUCTURE ONLY.
+
+A double-precision reference for the recurrence of the Mamba layer that "The
+Mamba in the Llama" distils from attention, and for the speculative verify /
+roll-back protocol of the QbitAI article's speculative-decoding walkthrough.
+Only `tests/`, `__graft_entry__.smoke()` and the bench's `cpu_baseline` leg
+may import this package.  It shares no code with the GPU library.
+
+All arrays are float64 numpy arrays in the token-row layouts
+  x [batch][T][H][P], B and C [batch][T][G][N], dt [batch][T][H], A and D [H],
+  state [batch][H][N][P], y [batch][T][H][P].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "libssm_oracle.so")
+# no contraction, no fast math: the loops run exactly as written
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99"]
+
+
+def build(src: str = _SRC, out: str = _LIB, extra: list[str] | None = None) -> str:
+    cmd = ["gcc", *CFLAGS, *(extra or []), "-o", out, src, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle library; `path` loads a specific build."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.ssm_oracle_scan.argtypes = [ctypes.c_int] * 6 + [dp] * 6 + [ip, dp, dp, ctypes.c_int]
+    lib.ssm_oracle_scan.restype = ctypes.c_int
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _dptr(a):
+    if a is None:
+        return None
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def scan(x, B, C, dt, A, D, state, ntok=None, want_y=True, nthreads=None, lib=None):
+    """Advance `state` in place over tokens [0, ntok[b]) of each sequence; return y or None."""
+    lib = lib or load()
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert B.shape == (Bt, T, G, N) and dt.shape == (Bt, T, H)
+    assert state.shape == (Bt, H, N, P)
+    x, B, dt = (np.ascontiguousarray(v, dtype=np.float64) for v in (x, B, dt))
+    C = None if C is None else np.ascontiguousarray(C, dtype=np.float64)
+    A = np.ascontiguousarray(A, dtype=np.float64)
+    D = np.ascontiguousarray(D, dtype=np.float64)
+    y = np.zeros((Bt, T, H, P)) if want_y else None
+    nt = None
+    if ntok is not None:
+        nt = np.ascontiguousarray(np.broadcast_to(np.asarray(ntok, dtype=np.int32), (Bt,)))
+    rc = lib.ssm_oracle_scan(Bt, T, H, P, N, G, _dptr(x), _dptr(B), _dptr(C), _dptr(dt),
+                             _dptr(A), _dptr(D),
+                             None if nt is None else nt.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+                             _dptr(state), _dptr(y), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return y
+
+
+def prefill(x, B, C, dt, A, D, h0=None, nthreads=None, lib=None):
+    """Full-sequence scan from zeros (or from h0): returns (y, final state)."""
+    Bt, T, H, P = x.shape
+    N = B.shape[3]
+    state = np.zeros((Bt, H, N, P)) if h0 is None else np.array(h0, dtype=np.float64, copy=True)
+    y = scan(x, B, C, dt, A, D, state, nthreads=nthreads, lib=lib)
+    return y, state
+
+
+def verify(state, x, B, C, dt, A, D, nthreads=None, lib=None):
+    """y for K draft tokens from the committed state; the state is left as it was."""
+    work = np.array(state, dtype=np.float64, copy=True)
+    return scan(x, B, C, dt, A, D, work, nthreads=nthreads, lib=lib)
+
+
+def commit(state, x, B, dt, A, D, accepted, nthreads=None, lib=None):
+    """State after the first accepted[b] draft tokens of each sequence (a new array)."""
+    K = x.shape[1]
+    acc = np.asarray(accepted, dtype=np.int32)
+    if np.any(acc < 0) or np.any(acc > K):
+        raise ValueError("accepted length outside 0..K")
+    out = np.array(state, dtype=np.float64, copy=True)
+    scan(x, B, None, dt, A, D, out, ntok=acc, want_y=False, nthreads=nthreads, lib=lib)
+    return out

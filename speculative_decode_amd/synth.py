@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs for the SSM layer, shared by tests, the bench and smoke.
+
+This module draws random numbers and rounds them to the storage dtype. It holds
+none of the layer's arithmetic: no discretisation, no recurrence, no readout.
+Both the GPU path and the CPU oracle receive exactly the arrays made here.
+
+Recipe (the layer of "The Mamba in the Llama", with x from the V projection,
+B from K, C from Q; the pages give no trained weights, so every tensor is drawn):
+  * per layer:   A_h = -exp(U(0, ln 16))  (so A in [-16, -1]),  D_h ~ N(0, 1)
+  * per token:   x ~ N(0,1)/4 [T][H][P],  B ~ N(0,1)/4 [T][G][N],
+                 C ~ N(0,1)/4 [T][G][N],  dt = softplus(z), z ~ N(-1, 0.5) [T][H]
+  * draw order:  x, B, C, z for each block of tokens, sequences in order
+  * rounding:    fp64 -> fp32 (round to nearest), then for bf16 inputs
+                 fp32 -> bf16 with round-to-nearest-even on the bit pattern.
+A and D always stay fp32.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even); return the uint16 bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    return r
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) exactly to float64."""
+    u = b.astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Tensor:
+    """One input tensor: `store` is what the device receives (float32, or uint16 bf16
+    bits), `f64` is the same values widened exactly to double for the oracle."""
+
+    store: np.ndarray
+    f64: np.ndarray
+    dtype: str
+
+
+def quantize(v64: np.ndarray, dtype: str) -> Tensor:
+    v32 = v64.astype(np.float32)
+    if dtype == F32:
+        return Tensor(v32, v32.astype(np.float64), F32)
+    if dtype == BF16:
+        bits = f32_to_bf16_bits(v32)
+        return Tensor(bits, bf16_bits_to_f64(bits), BF16)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+@dataclasses.dataclass
+class Layer:
+    A: Tensor  # [H] fp32
+    D: Tensor  # [H] fp32
+
+
+@dataclasses.dataclass
+class Tokens:
+    """Per-token projected inputs for `batch` sequences of `T` tokens."""
+
+    x: Tensor   # [batch][T][H][P]
+    B: Tensor   # [batch][T][G][N]
+    C: Tensor   # [batch][T][G][N]
+    dt: Tensor  # [batch][T][H]
+
+    @property
+    def T(self) -> int:
+        return self.x.store.shape[1]
+
+
+def softplus(z: np.ndarray) -> np.ndarray:
+    # numerically safe log(1 + e^z) in fp64; part of the input recipe, not of the layer
+    return np.logaddexp(0.0, z)
+
+
+def draw_layer(rng: np.random.Generator, H: int) -> Layer:
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), size=H))
+    D = rng.normal(0.0, 1.0, size=H)
+    return Layer(quantize(A, F32), quantize(D, F32))
+
+
+def draw_tokens(rng: np.random.Generator, batch: int, T: int, H: int, P: int, N: int,
+                G: int, dtype: str) -> Tokens:
+    x = rng.normal(0.0, 1.0, size=(batch, T, H, P)) / 4.0
+    B = rng.normal(0.0, 1.0, size=(batch, T, G, N)) / 4.0
+    C = rng.normal(0.0, 1.0, size=(batch, T, G, N)) / 4.0
+    z = rng.normal(-1.0, 0.5, size=(batch, T, H))
+    return Tokens(quantize(x, dtype), quantize(B, dtype), quantize(C, dtype),
+                  quantize(softplus(z), dtype))
+
+
+def draw_accept_uniform(rng: np.random.Generator, batch: int, K: int) -> np.ndarray:
+    """Accepted lengths j ~ U{0..K} (inclusive), int32."""
+    return rng.integers(0, K + 1, size=batch).astype(np.int32)
+
+
+def draw_accept_geometric(rng: np.random.Generator, batch: int, K: int, p: float = 0.3) -> np.ndarray:
+    """Accepted lengths j = min(Geom(p) - 1, K): P(j=k) = p (1-p)^k for k < K."""
+    return np.minimum(rng.geometric(p, size=batch) - 1, K).astype(np.int32)
+
+
+def integer_tokens(rng: np.random.Generator, batch: int, T: int, H: int, P: int, N: int,
+                   G: int, dtype: str, lo: int = -1, hi: int = 1) -> Tokens:
+    """Small-integer x, B, C with dt = 1: every product and partial sum of the
+    causal-linear-attention special case is exact in fp32 and bf16."""
+    x = rng.integers(lo, hi + 1, size=(batch, T, H, P)).astype(np.float64)
+    B = rng.integers(lo, hi + 1, size=(batch, T, G, N)).astype(np.float64)
+    C = rng.integers(lo, hi + 1, size=(batch, T, G, N)).astype(np.float64)
+    dt = np.ones((batch, T, H))
+    return Tokens(quantize(x, dtype), quantize(B, dtype), quantize(C, dtype), quantize(dt, dtype))
+
+
+def concat_tokens(parts: list[Tokens]) -> Tokens:
+    """Join token blocks along the token axis (same batch and shapes)."""
+    def cat(name):
+        ts = [getattr(p, name) for p in parts]
+        return Tensor(np.concatenate([t.store for t in ts], axis=1),
+                      np.concatenate([t.f64 for t in ts], axis=1), ts[0].dtype)
+    return Tokens(cat("x"), cat("B"), cat("C"), cat("dt"))
+
+
+def slice_tokens(t: Tokens, b0: int, b1: int, t0: int, t1: int) -> Tokens:
+    def sl(v: Tensor) -> Tensor:
+        return Tensor(np.ascontiguousarray(v.store[b0:b1, t0:t1]),
+                      np.ascontiguousarray(v.f64[b0:b1, t0:t1]), v.dtype)
+    return Tokens(sl(t.x), sl(t.B), sl(t.C), sl(t.dt))
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shapes of one synthetic workload (a Llama-3-8B-derived hybrid layer or a tiny case)."""
+
+    name: str
+    batch: int
+    H: int
+    P: int
+    N: int
+    G: int
+    dtype: str
+    K: int = 0            # drafts per verify round
+    L: int = 0            # prefill length (fixed) or 0 when ctx_range is used
+    ctx_range: tuple = () # (lo, hi) inclusive per-sequence prefill lengths
+    chunk: int = 256
+    layers: int = 1
+    accept: str = "uniform"  # or "geometric"
+    seed: int = 1000
+
+
+WORKLOADS = {
+    # tiny fp32 case: every step cheap enough for the oracle at once
+    "tiny_f32": Workload("tiny_f32", batch=1, H=2, P=16, N=16, G=1, dtype=F32, K=4, L=64,
+                         chunk=256, seed=1001),
+    # one Llama-3-8B-shaped sequence: 32 heads, P=N=128, 8 B/C groups
+    "llama8b_single": Workload("llama8b_single", batch=1, H=32, P=128, N=128, G=8, dtype=BF16,
+                               K=4, L=1024, seed=1002),
+    # batched verify: 16 sequences with prior contexts U{256..4096}
+    "llama8b_batched": Workload("llama8b_batched", batch=16, H=32, P=128, N=128, G=8,
+                                dtype=BF16, K=8, ctx_range=(256, 4096), seed=1003),
+    # one long prefill scan
+    "llama8b_long_prefill": Workload("llama8b_long_prefill", batch=1, H=32, P=128, N=128, G=8,
+                                     dtype=BF16, L=8192, chunk=256, seed=1004),
+    # hybrid decode step: 24 SSM layers, batch 32, expanded state N=256
+    "hybrid_decode": Workload("hybrid_decode", batch=32, H=32, P=128, N=256, G=8, dtype=BF16,
+                              K=4, L=1024, layers=24, accept="geometric", seed=1005),
+}
