@@ -1,0 +1,193 @@
+/*
+ * mil_ssm.h -- C ABI of the MI355X (gfx950) library for the selective SSM layer
+ * of "The Mamba in the Llama: Distilling and Accelerating Hybrid Models", in its
+ * two inference modes: a chunked full-sequence prefill, and the speculative
+ * verify / commit step that advances a cached state through K draft tokens and
+ * rolls back to the accepted prefix by recomputing from the cached state.
+ *
+ * The layer (one sequence b, head h, group g = h / (H/G); abstract of the paper:
+ * attention is distilled into a linear RNN reusing the attention projections, so
+ * x comes from V, B from K and C from Q; skycaiji.com summary, method paragraph:
+ * a continuous-time SSM with an expanded state, discretised per token):
+ *     h_t = exp(dt_t * A_h) * h_{t-1} + (dt_t * B_t) x_t^T      (N x P, fp32)
+ *     y_t = C_t^T h_t + D_h * x_t                               (P, fp32)
+ *
+ * The decoding protocol (QbitAI article "Llama 3+Mamba 强强联手", speculative-
+ * decoding walkthrough): a draft model proposes K tokens; the Mamba layer takes
+ * them one after another; the state moves forward only through the accepted
+ * ones; no intermediate state is stored; on a rejection the state goes back to
+ * the last accepted token and drafting restarts from there.
+ *
+ * Conventions for every function below:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory and keeps no global state.
+ *   - Token tensors are row-major with the last dimension contiguous:
+ *       x  [seq][T][H][P],  B, C [seq][T][G][N],  dt [seq][T][H]   (dtype of the cache)
+ *       A, D [H] fp32,  y [seq][T][H][P] fp32.
+ *     dt is the step size after any softplus (dt > 0); A is the continuous decay
+ *     rate (A <= 0 for a stable layer; any finite value is accepted).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the functions return without synchronising, except mil_ssm_cache_status.
+ *   - Argument errors are reported synchronously as a status code before any
+ *     work is enqueued; nothing is modified then.  A failing HIP launch returns
+ *     MIL_E_HIP.  No function throws or aborts.
+ *   - Calls on one cache must be issued from one host thread in order; calls on
+ *     different caches are independent and reentrant.
+ */
+#ifndef MIL_SSM_H
+#define MIL_SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *mil_stream_t;
+
+enum mil_status {
+    MIL_OK = 0,
+    MIL_E_INVALID = 1,     /* null pointer, bad size, bad dtype, value out of range */
+    MIL_E_ALIGN = 2,       /* a device buffer is not aligned as required (256 B for the cache) */
+    MIL_E_ORDER = 3,       /* call out of protocol order (see mil_ssm_verify / mil_ssm_commit) */
+    MIL_E_UNSUPPORTED = 4, /* a shape this build has no kernel for (see mil_ssm_supported) */
+    MIL_E_HIP = 5,         /* the HIP runtime reported an error */
+    MIL_E_WORKSPACE = 6    /* workspace missing or too small */
+};
+
+enum mil_dtype {
+    MIL_F32 = 0,  /* x, B, C, dt stored as IEEE fp32 */
+    MIL_BF16 = 1  /* x, B, C, dt stored as bfloat16 */
+};
+
+/* Layer shape.  H % G == 0; heads h and h' share B and C when h/(H/G) == h'/(H/G). */
+typedef struct {
+    int32_t batch;   /* number of sequence slots in a cache */
+    int32_t nheads;  /* H */
+    int32_t headdim; /* P: columns of the state, width of x and y per head */
+    int32_t dstate;  /* N: rows of the state, width of B and C per group */
+    int32_t ngroups; /* G */
+} mil_ssm_dims;
+
+/*
+ * Byte layout of a cache buffer (all offsets from its start, each a multiple of 256).
+ *   state   fp32 [batch][H][N][P]: head block (slot, h) starts at
+ *           state_off + (slot*H + h) * state_head_stride; p is contiguous.
+ *   pend_x  [batch][k_max][H][P], pend_B [batch][k_max][G][N], pend_dt [batch][k_max][H]
+ *           (cache dtype): accepted draft tokens not yet folded into `state`.
+ *   pos     int32 [batch]: tokens the sequence has absorbed (prefill + accepted drafts).
+ *   pending int32 [batch]: how many rows of pend_* are accepted but not yet folded in.
+ *   err     int32 [batch]: 0, or MIL_DEVERR_ACCEPT after an out-of-range accepted length.
+ * The logical state of slot b is `state` advanced through its `pending` rows.
+ */
+typedef struct {
+    int64_t bytes;
+    int64_t state_off, state_head_stride;
+    int64_t pend_x_off, pend_B_off, pend_dt_off;
+    int64_t pos_off, pending_off, err_off;
+} mil_ssm_layout;
+
+#define MIL_DEVERR_ACCEPT 1
+
+/* Host-side cache descriptor.  The caller provides the storage; mil_ssm_cache_init
+ * fills it.  It holds the device buffer address, the shape and the protocol phase. */
+typedef struct {
+    uint64_t opaque[24];
+} mil_ssm_cache;
+
+#define MIL_KMAX_LIMIT 16          /* largest K (drafts per round) and k_max supported */
+#define MIL_PREFILL_CONTINUE 1u    /* prefill: start from the slot's logical state instead of zeros */
+#define MIL_COMMIT_MATERIALIZE 1u  /* commit: fold the accepted tokens into `state` now */
+
+/* Text for a status code (static storage). */
+const char *mil_status_string(int status);
+
+/* MIL_OK if this build has kernels for the shape and dtype, else MIL_E_UNSUPPORTED
+ * (or MIL_E_INVALID for a malformed shape).  Supported: P and N in {16,32,64,128,256},
+ * H % G == 0, batch >= 1, dtype MIL_F32 or MIL_BF16. */
+int mil_ssm_supported(const mil_ssm_dims *dims, int32_t dtype);
+
+/* Fill *out with the layout of a cache for `dims`, k_max (1..MIL_KMAX_LIMIT) and dtype. */
+int mil_ssm_cache_layout(const mil_ssm_dims *dims, int32_t k_max, int32_t dtype, mil_ssm_layout *out);
+
+/* Bytes a cache needs (0 if the arguments are invalid). */
+size_t mil_ssm_cache_bytes(const mil_ssm_dims *dims, int32_t k_max, int32_t dtype);
+
+/* Carve a caller-owned device buffer (256-B aligned, >= mil_ssm_cache_bytes) into a
+ * cache and enqueue zeroing of the state, pos, pending and err arrays.  The descriptor
+ * starts in the READY phase.  The buffer must outlive every call that uses the cache. */
+int mil_ssm_cache_init(mil_ssm_cache *cache, const mil_ssm_dims *dims, int32_t k_max, int32_t dtype,
+                       void *dev_buf, size_t bytes, mil_stream_t stream);
+
+/* Describe a buffer that already holds a cache of this shape (for instance a byte copy
+ * of one set up by mil_ssm_cache_init, used to snapshot and restore sequences).  Same
+ * checks as mil_ssm_cache_init; nothing is enqueued and the contents are not touched.
+ * The descriptor starts in the READY phase. */
+int mil_ssm_cache_attach(mil_ssm_cache *cache, const mil_ssm_dims *dims, int32_t k_max, int32_t dtype,
+                         void *dev_buf, size_t bytes);
+
+/* Workspace bytes mil_ssm_prefill needs for nseq sequences of L tokens with chunk length `chunk`. */
+size_t mil_ssm_prefill_workspace_bytes(const mil_ssm_dims *dims, int32_t nseq, int32_t L, int32_t chunk);
+
+/*
+ * Full-sequence scan of L tokens for slots [slot0, slot0+nseq).
+ * Computes y for every token (skipped when y is NULL) and sets each slot's logical
+ * state to h_L.  It starts from zeros, or with MIL_PREFILL_CONTINUE from the slot's
+ * logical state (pending rows are folded in first).  pos becomes L (or pos + L);
+ * pending becomes 0.  The sequence is cut into chunks of `chunk` tokens (the last may
+ * be shorter): within a chunk the layer is evaluated in its matrix (quadratic) form on
+ * the matrix cores, and a short sequential pass carries the state across chunks.
+ * chunk must be 64, 128 or 256.  ws: device workspace of at least
+ * mil_ssm_prefill_workspace_bytes(); it is scratch and may be reused after the call's
+ * work completes in stream order.
+ * Order: the cache must be READY (not between verify and commit) -> MIL_E_ORDER.
+ */
+int mil_ssm_prefill(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L, int32_t chunk,
+                    const void *x, const void *B, const void *C, const void *dt,
+                    const float *A, const float *D, float *y,
+                    void *ws, size_t ws_bytes, uint32_t flags, mil_stream_t stream);
+
+/*
+ * Speculative verify of K draft tokens (1 <= K <= k_max) for every slot of the cache.
+ * x, B, C, dt hold the drafts, [batch][K][...]; y [batch][K][H][P] receives, for each
+ * draft k, the output the layer gives when drafts 0..k follow the slot's logical state.
+ * The logical state is NOT changed (a draft is folded in only by a later commit).
+ * Each (slot, head) state block is read from HBM once; pending accepted rows from the
+ * previous round are folded in on the way and the result is written back once.
+ * Order: READY -> VERIFIED.  A second verify without a commit returns MIL_E_ORDER.
+ */
+int mil_ssm_verify(mil_ssm_cache *cache, int32_t K,
+                   const void *x, const void *B, const void *C, const void *dt,
+                   const float *A, const float *D, float *y, mil_stream_t stream);
+
+/*
+ * Accept the first accepted[b] drafts of slot b (device int32 [batch], each 0..K) from
+ * the round verified just before.  x, B, dt are the same draft buffers given to that
+ * verify (C is not needed).  The logical state of slot b becomes the state after its
+ * accepted drafts; pos[b] += accepted[b].  The accepted rows are copied into the cache,
+ * so the draft buffers may be reused once this call is enqueued.  By default the rows are
+ * folded into `state` by the next verify or prefill; MIL_COMMIT_MATERIALIZE folds them in
+ * now (same arithmetic, bit-identical state).  An accepted[b] outside 0..K sets
+ * err[b] = MIL_DEVERR_ACCEPT and leaves slot b's logical state and pos unchanged.
+ * A and D are needed only with MIL_COMMIT_MATERIALIZE (may be NULL otherwise).
+ * Order: VERIFIED -> READY (MIL_E_ORDER otherwise); K must equal the verified K.
+ */
+int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted,
+                   const void *x, const void *B, const void *dt,
+                   const float *A, const float *D, uint32_t flags, mil_stream_t stream);
+
+/* Synchronise `stream`, then report device-side errors: *bad_slot = first slot with
+ * err != 0, or -1.  Returns MIL_OK, or MIL_E_INVALID when a slot has an error.
+ * With clear != 0 the err words are zeroed afterwards. */
+int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t clear, mil_stream_t stream);
+
+/* Protocol phase of a cache descriptor: 0 = uninitialised, 1 = READY, 2 = VERIFIED. */
+int mil_ssm_cache_phase(const mil_ssm_cache *cache);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIL_SSM_H */

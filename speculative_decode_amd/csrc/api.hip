@@ -1,0 +1,270 @@
+// C ABI entry points: argument and protocol checks, cache carving, dispatch to the
+// kernel launchers.  Every check runs before any work is enqueued.
+#include <string.h>
+
+#include "ssm_internal.h"
+
+using namespace mil;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+int check_dims(const mil_ssm_dims *d) {
+    if (!d) return MIL_E_INVALID;
+    if (d->batch < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1)
+        return MIL_E_INVALID;
+    if (d->nheads % d->ngroups != 0) return MIL_E_INVALID;
+    if (!pow2_in(d->headdim, 16, 256) || !pow2_in(d->dstate, 16, 256)) return MIL_E_UNSUPPORTED;
+    return MIL_OK;
+}
+
+int check_dtype(int32_t dtype) { return (dtype == MIL_F32 || dtype == MIL_BF16) ? MIL_OK : MIL_E_INVALID; }
+
+
+CacheImpl *impl(mil_ssm_cache *c) {
+    if (!c) return nullptr;
+    CacheImpl *ci = reinterpret_cast<CacheImpl *>(c->opaque);
+    return ci->magic == kCacheMagic ? ci : nullptr;
+}
+const CacheImpl *impl(const mil_ssm_cache *c) {
+    if (!c) return nullptr;
+    const CacheImpl *ci = reinterpret_cast<const CacheImpl *>(c->opaque);
+    return ci->magic == kCacheMagic ? ci : nullptr;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MIL_OK : MIL_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mil_status_string(int status) {
+    switch (status) {
+        case MIL_OK: return "ok";
+        case MIL_E_INVALID: return "invalid argument";
+        case MIL_E_ALIGN: return "misaligned device buffer";
+        case MIL_E_ORDER: return "call out of protocol order";
+        case MIL_E_UNSUPPORTED: return "unsupported shape";
+        case MIL_E_HIP: return "HIP runtime error";
+        case MIL_E_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int mil_ssm_supported(const mil_ssm_dims *dims, int32_t dtype) {
+    int st = check_dims(dims);
+    if (st != MIL_OK) return st;
+    st = check_dtype(dtype);
+    if (st != MIL_OK) return st;
+    for (int kt : {4, 8, 16})
+        if (!verify_supported(dims->headdim, dims->dstate, kt)) return MIL_E_UNSUPPORTED;
+    return MIL_OK;
+}
+
+int mil_ssm_cache_layout(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mil_ssm_layout *out) {
+    int st = check_dims(d);
+    if (st != MIL_OK) return st;
+    if ((st = check_dtype(dtype)) != MIL_OK) return st;
+    if (!out || k_max < 1 || k_max > MIL_KMAX_LIMIT) return MIL_E_INVALID;
+    const int64_t e = elt_bytes(dtype);
+    const int64_t Bt = d->batch, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+    mil_ssm_layout L;
+    int64_t off = 0;
+    L.state_off = off;
+    L.state_head_stride = round_up(N * P * 4, kAlign);
+    off += Bt * H * L.state_head_stride;
+    L.pend_x_off = off = round_up(off, kAlign);
+    off += Bt * k_max * H * P * e;
+    L.pend_B_off = off = round_up(off, kAlign);
+    off += Bt * k_max * G * N * e;
+    L.pend_dt_off = off = round_up(off, kAlign);
+    off += Bt * k_max * H * e;
+    L.pos_off = off = round_up(off, kAlign);
+    off += Bt * 4;
+    L.pending_off = off = round_up(off, kAlign);
+    off += Bt * 4;
+    L.err_off = off = round_up(off, kAlign);
+    off += Bt * 4;
+    L.bytes = round_up(off, kAlign);
+    *out = L;
+    return MIL_OK;
+}
+
+size_t mil_ssm_cache_bytes(const mil_ssm_dims *d, int32_t k_max, int32_t dtype) {
+    mil_ssm_layout L;
+    return mil_ssm_cache_layout(d, k_max, dtype, &L) == MIL_OK ? (size_t)L.bytes : 0;
+}
+
+namespace {
+int describe(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype, void *dev_buf,
+             size_t bytes) {
+    if (!cache || !dev_buf) return MIL_E_INVALID;
+    mil_ssm_layout L;
+    int st = mil_ssm_cache_layout(d, k_max, dtype, &L);
+    if (st != MIL_OK) return st;
+    if ((st = mil_ssm_supported(d, dtype)) != MIL_OK) return st;
+    if (!aligned(dev_buf, kAlign)) return MIL_E_ALIGN;
+    if ((int64_t)bytes < L.bytes) return MIL_E_INVALID;
+    memset(cache->opaque, 0, sizeof(cache->opaque));
+    CacheImpl *c = reinterpret_cast<CacheImpl *>(cache->opaque);
+    c->dims = *d;
+    c->k_max = k_max;
+    c->dtype = dtype;
+    c->verified_k = 0;
+    c->base = static_cast<char *>(dev_buf);
+    c->bytes = L.bytes;
+    c->lay = L;
+    return MIL_OK;
+}
+}  // namespace
+
+int mil_ssm_cache_attach(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
+                         void *dev_buf, size_t bytes) {
+    const int st = describe(cache, d, k_max, dtype, dev_buf, bytes);
+    if (st != MIL_OK) return st;
+    CacheImpl *c = reinterpret_cast<CacheImpl *>(cache->opaque);
+    c->magic = kCacheMagic;
+    c->phase = kReady;
+    return MIL_OK;
+}
+
+int mil_ssm_cache_init(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
+                       void *dev_buf, size_t bytes, mil_stream_t stream) {
+    const int st = describe(cache, d, k_max, dtype, dev_buf, bytes);
+    if (st != MIL_OK) return st;
+    CacheImpl *c = reinterpret_cast<CacheImpl *>(cache->opaque);
+    const mil_ssm_layout &L = c->lay;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // zero the state block and the three counter arrays (the pending token rows are
+    // never read before a commit writes them)
+    hipError_t e = launch_fill_zero(c->base + L.state_off, (L.pend_x_off - L.state_off) / 4, s);
+    if (e == hipSuccess) e = launch_fill_zero(c->base + L.pos_off, (L.bytes - L.pos_off) / 4, s);
+    if (e != hipSuccess) return MIL_E_HIP;
+    c->magic = kCacheMagic;
+    c->phase = kReady;
+    return MIL_OK;
+}
+
+size_t mil_ssm_prefill_workspace_bytes(const mil_ssm_dims *d, int32_t nseq, int32_t L, int32_t chunk) {
+    if (check_dims(d) != MIL_OK || nseq < 1 || L < 1) return 0;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return 0;
+    return (size_t)prefill_workspace_bytes(*d, nseq, L, chunk);
+}
+
+int mil_ssm_prefill(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L, int32_t chunk,
+                    const void *x, const void *B, const void *C, const void *dt, const float *A,
+                    const float *D, float *y, void *ws, size_t ws_bytes, uint32_t flags,
+                    mil_stream_t stream) {
+    CacheImpl *c = impl(cache);
+    if (!c) return MIL_E_INVALID;
+    if (c->phase != kReady) return MIL_E_ORDER;
+    if (flags & ~MIL_PREFILL_CONTINUE) return MIL_E_INVALID;
+    if (nseq < 1 || slot0 < 0 || slot0 + nseq > c->dims.batch || L < 1) return MIL_E_INVALID;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return MIL_E_INVALID;
+    if (!x || !B || !C || !dt || !A || !D) return MIL_E_INVALID;
+    const int eb = elt_bytes(c->dtype);
+    if (!aligned(x, eb) || !aligned(B, eb) || !aligned(C, eb) || !aligned(dt, eb) || !aligned(A, 4) ||
+        !aligned(D, 4) || (y && !aligned(y, 4)))
+        return MIL_E_ALIGN;
+    const int64_t need = prefill_workspace_bytes(c->dims, nseq, L, chunk);
+    if (!ws || (int64_t)ws_bytes < need) return MIL_E_WORKSPACE;
+    if (!aligned(ws, kAlign)) return MIL_E_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool cont = (flags & MIL_PREFILL_CONTINUE) != 0;
+    hipError_t e = hipSuccess;
+    if (cont) {
+        // fold pending accepted rows of every slot (a no-op where pending == 0)
+        e = launch_verify(*c, 0, nullptr, nullptr, nullptr, nullptr, A, D, nullptr, s);
+        if (e == hipSuccess) e = launch_clear_pending(*c, s);
+    }
+    if (e == hipSuccess) e = launch_prefill(*c, slot0, nseq, L, chunk, x, B, C, dt, A, D, y, ws, cont, s);
+    if (e == hipSuccess) e = launch_prefill_counters(*c, slot0, nseq, L, cont, s);
+    return hip_status(e);
+}
+
+int mil_ssm_verify(mil_ssm_cache *cache, int32_t K, const void *x, const void *B, const void *C,
+                   const void *dt, const float *A, const float *D, float *y, mil_stream_t stream) {
+    CacheImpl *c = impl(cache);
+    if (!c) return MIL_E_INVALID;
+    if (c->phase != kReady) return MIL_E_ORDER;
+    if (K < 1 || K > c->k_max) return MIL_E_INVALID;
+    if (!x || !B || !C || !dt || !A || !D || !y) return MIL_E_INVALID;
+    const int eb = elt_bytes(c->dtype);
+    if (!aligned(x, eb) || !aligned(B, eb) || !aligned(C, eb) || !aligned(dt, eb) || !aligned(A, 4) ||
+        !aligned(D, 4) || !aligned(y, 4))
+        return MIL_E_ALIGN;
+    hipError_t e = launch_verify(*c, K, x, B, C, dt, A, D, y, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return MIL_E_HIP;
+    c->phase = kVerified;
+    c->verified_k = K;
+    return MIL_OK;
+}
+
+int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, const void *x,
+                   const void *B, const void *dt, const float *A, const float *D, uint32_t flags,
+                   mil_stream_t stream) {
+    CacheImpl *c = impl(cache);
+    if (!c) return MIL_E_INVALID;
+    if (c->phase != kVerified) return MIL_E_ORDER;
+    if (flags & ~MIL_COMMIT_MATERIALIZE) return MIL_E_INVALID;
+    if (K != c->verified_k) return MIL_E_INVALID;
+    if (!accepted || !x || !B || !dt) return MIL_E_INVALID;
+    const bool mat = (flags & MIL_COMMIT_MATERIALIZE) != 0;
+    if (mat && (!A || !D)) return MIL_E_INVALID;
+    const int eb = elt_bytes(c->dtype);
+    // x and B rows are copied as 32-bit words
+    if (!aligned(accepted, 4) || !aligned(x, 4) || !aligned(B, 4) || !aligned(dt, eb))
+        return MIL_E_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch_commit(*c, K, accepted, x, B, dt, s);
+    if (e == hipSuccess && mat) {
+        e = launch_verify(*c, 0, nullptr, nullptr, nullptr, nullptr, A, D, nullptr, s);
+        if (e == hipSuccess) e = launch_clear_pending(*c, s);
+    }
+    if (e != hipSuccess) return MIL_E_HIP;
+    c->phase = kReady;
+    c->verified_k = 0;
+    return MIL_OK;
+}
+
+int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t clear, mil_stream_t stream) {
+    const CacheImpl *c = impl(cache);
+    if (!c || !bad_slot) return MIL_E_INVALID;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int Bt = c->dims.batch;
+    int32_t *host = static_cast<int32_t *>(malloc(sizeof(int32_t) * Bt));
+    if (!host) return MIL_E_INVALID;
+    hipError_t e = hipMemcpyAsync(host, cache_err(*c), sizeof(int32_t) * Bt, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        free(host);
+        return MIL_E_HIP;
+    }
+    *bad_slot = -1;
+    for (int b = 0; b < Bt; ++b)
+        if (host[b] != 0) {
+            *bad_slot = b;
+            break;
+        }
+    free(host);
+    if (clear) {
+        e = launch_fill_zero(cache_err(*c), Bt, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return MIL_E_HIP;
+    }
+    return *bad_slot < 0 ? MIL_OK : MIL_E_INVALID;
+}
+
+int mil_ssm_cache_phase(const mil_ssm_cache *cache) {
+    const CacheImpl *c = impl(cache);
+    return c ? c->phase : kUninit;
+}
+
+}  // extern "C"

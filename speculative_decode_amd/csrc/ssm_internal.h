@@ -1,0 +1,67 @@
+// Internal declarations shared by the host ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mil_ssm.h"
+
+namespace mil {
+
+constexpr uint32_t kCacheMagic = 0x4d494c53u;  // "MILS"
+enum Phase : int32_t { kUninit = 0, kReady = 1, kVerified = 2 };
+
+// Host-side view of a cache descriptor (lives inside mil_ssm_cache::opaque).
+struct CacheImpl {
+    uint32_t magic;
+    int32_t phase;
+    mil_ssm_dims dims;
+    int32_t k_max;
+    int32_t dtype;
+    int32_t verified_k;
+    int32_t pad_;
+    char *base;
+    int64_t bytes;
+    mil_ssm_layout lay;
+};
+static_assert(sizeof(CacheImpl) <= sizeof(mil_ssm_cache), "cache descriptor too large");
+
+inline float *cache_state(const CacheImpl &c) { return reinterpret_cast<float *>(c.base + c.lay.state_off); }
+inline void *cache_pend_x(const CacheImpl &c) { return c.base + c.lay.pend_x_off; }
+inline void *cache_pend_B(const CacheImpl &c) { return c.base + c.lay.pend_B_off; }
+inline void *cache_pend_dt(const CacheImpl &c) { return c.base + c.lay.pend_dt_off; }
+inline int32_t *cache_pos(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.pos_off); }
+inline int32_t *cache_pending(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.pending_off); }
+inline int32_t *cache_err(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.err_off); }
+inline int elt_bytes(int32_t dtype) { return dtype == MIL_BF16 ? 2 : 4; }
+
+// ---- launchers (each returns the launch's hipError_t) ----
+
+// Zero `words` 32-bit words starting at p (a plain fill kernel, safe under graph capture).
+hipError_t launch_fill_zero(void *p, int64_t words, hipStream_t s);
+
+// Fold every slot's pending rows into the stored state, then, when K > 0, emit y for
+// K drafts from that state.  K == 0 is the fold alone (x/B/C/dt/y unused).
+hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B, const void *C,
+                         const void *dt, const float *A, const float *D, float *y, hipStream_t s);
+bool verify_supported(int P, int N, int kt);
+
+// Check accepted[b] in 0..K, copy the accepted draft rows into the pending area,
+// set pending[b] = accepted[b], pos[b] += accepted[b]; a bad value sets err[b] and pending[b] = 0.
+hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, const void *x,
+                         const void *B, const void *dt, hipStream_t s);
+
+// pending[b] = 0 for every slot (after a fold that has consumed them).
+hipError_t launch_clear_pending(const CacheImpl &c, hipStream_t s);
+
+// Set pos[slot] = L (or += L when cont) and pending[slot] = 0 for slots [slot0, slot0+nseq).
+hipError_t launch_prefill_counters(const CacheImpl &c, int slot0, int nseq, int L, bool cont,
+                                   hipStream_t s);
+
+// Chunked prefill (three phases: chunk states, inter-chunk pass, chunk outputs).
+int64_t prefill_workspace_bytes(const mil_ssm_dims &d, int nseq, int L, int chunk);
+hipError_t launch_prefill(const CacheImpl &c, int slot0, int nseq, int L, int chunk, const void *x,
+                          const void *B, const void *C, const void *dt, const float *A,
+                          const float *D, float *y, void *ws, bool cont, hipStream_t s);
+
+}  // namespace mil

@@ -1,0 +1,13 @@
+// Instantiations of the verify / fold kernel for bf16 token inputs.
+#include "verify_kernel.h"
+
+namespace mil {
+
+hipError_t dispatch_verify_bf16(const VerifyParams &vp, int kt, int batch, hipStream_t s) {
+    if (kt == 4) return dispatch_rows<uint16_t, 4>(vp, batch, s);
+    if (kt == 8) return dispatch_rows<uint16_t, 8>(vp, batch, s);
+    if (kt == 16) return dispatch_rows<uint16_t, 16>(vp, batch, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mil

@@ -1,0 +1,157 @@
+"""Python face of the C ABI: a cache object and prefill / verify / commit calls.
+
+Torch supplies device memory and the current stream; every computation happens in
+the HIP library behind `mil_ssm_*`.  Names follow the layer of "The Mamba in the
+Llama" (x from V, B from K, C from Q, step size dt, decay rate A, skip D) and the
+speculative protocol of the QbitAI article's walkthrough (K drafts, accepted length j).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.float32: L.MIL_F32, torch.bfloat16: L.MIL_BF16}
+_TORCH = {L.MIL_F32: torch.float32, L.MIL_BF16: torch.bfloat16}
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, str):
+        return {"f32": L.MIL_F32, "bf16": L.MIL_BF16}[dtype]
+    if isinstance(dtype, torch.dtype):
+        return _DTYPES[dtype]
+    return int(dtype)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p | None:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def cache_layout(batch, H, P, N, G, k_max, dtype) -> L.Layout:
+    d = L.Dims(batch, H, P, N, G)
+    lay = L.Layout()
+    L.check(L.lib().mil_ssm_cache_layout(ctypes.byref(d), k_max, _dtype_code(dtype), ctypes.byref(lay)),
+            "mil_ssm_cache_layout")
+    return lay
+
+
+def supported(batch, H, P, N, G, dtype) -> bool:
+    d = L.Dims(batch, H, P, N, G)
+    return L.lib().mil_ssm_supported(ctypes.byref(d), _dtype_code(dtype)) == L.MIL_OK
+
+
+class SSMCache:
+    """Per-layer state cache for `batch` sequence slots (fp32 state [batch][H][N][P],
+    head blocks 256-B aligned) plus the pending accepted-token rows and counters."""
+
+    def __init__(self, batch, H, P, N, G, k_max, dtype, device="cuda"):
+        self.batch, self.H, self.P, self.N, self.G, self.k_max = batch, H, P, N, G, k_max
+        self.dtype_code = _dtype_code(dtype)
+        self.torch_dtype = _TORCH[self.dtype_code]
+        self.device = torch.device(device)
+        self.dims = L.Dims(batch, H, P, N, G)
+        self.layout = cache_layout(batch, H, P, N, G, k_max, self.dtype_code)
+        nbytes = self.layout.bytes
+        # over-allocate so that the carved base is 256-B aligned whatever the allocator does
+        self._raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        off = (-self._raw.data_ptr()) % 256
+        self.buffer = self._raw[off:off + nbytes]
+        self.desc = L.CacheDesc()
+        L.check(L.lib().mil_ssm_cache_init(ctypes.byref(self.desc), ctypes.byref(self.dims), k_max,
+                                          self.dtype_code, _ptr(self.buffer), nbytes, _stream(self.device)),
+                "mil_ssm_cache_init")
+
+    # ---- views into the cache buffer (for inspection and tests) ----
+    def state(self) -> torch.Tensor:
+        """fp32 view [batch][H][N][P] of the stored state (before pending rows are folded)."""
+        lay = self.layout
+        stride = lay.state_head_stride // 4
+        flat = self.buffer[lay.state_off:lay.state_off + self.batch * self.H * lay.state_head_stride]
+        f = flat.view(torch.float32)
+        return f.as_strided((self.batch, self.H, self.N, self.P),
+                            (self.H * stride, stride, self.P, 1))
+
+    def _i32(self, off) -> torch.Tensor:
+        return self.buffer[off:off + 4 * self.batch].view(torch.int32)
+
+    def pos(self) -> torch.Tensor:
+        return self._i32(self.layout.pos_off)
+
+    def pending(self) -> torch.Tensor:
+        return self._i32(self.layout.pending_off)
+
+    def err(self) -> torch.Tensor:
+        return self._i32(self.layout.err_off)
+
+    def phase(self) -> int:
+        return L.lib().mil_ssm_cache_phase(ctypes.byref(self.desc))
+
+    def status(self, clear: bool = False) -> int:
+        """Synchronise and return the first slot with a device-side error, or -1."""
+        bad = ctypes.c_int32(-1)
+        st = L.lib().mil_ssm_cache_status(ctypes.byref(self.desc), ctypes.byref(bad), int(clear),
+                                          _stream(self.device))
+        if st not in (L.MIL_OK, L.MIL_E_INVALID):
+            L.check(st, "mil_ssm_cache_status")
+        return bad.value
+
+    def _check_tokens(self, what, *ts):
+        for t in ts:
+            if t is None:
+                continue
+            if t.dtype != self.torch_dtype:
+                raise TypeError(f"{what}: expected {self.torch_dtype}, got {t.dtype}")
+            if not t.is_contiguous() or t.device != self.device:
+                raise ValueError(f"{what}: tensors must be contiguous and on {self.device}")
+
+    # ---- the three calls ----
+    def workspace_bytes(self, nseq, L_tokens, chunk=256) -> int:
+        return L.lib().mil_ssm_prefill_workspace_bytes(ctypes.byref(self.dims), nseq, L_tokens, chunk)
+
+    def prefill(self, x, B, C, dt, A, D, slot0=0, y=None, chunk=256, cont=False, ws=None, want_y=True):
+        """Scan x [nseq][L][H][P], B/C [nseq][L][G][N], dt [nseq][L][H] into slots
+        [slot0, slot0+nseq).  Returns y [nseq][L][H][P] fp32 (or None when want_y is False)."""
+        nseq, Lt = x.shape[0], x.shape[1]
+        self._check_tokens("prefill", x, B, C, dt)
+        if want_y and y is None:
+            y = torch.empty((nseq, Lt, self.H, self.P), dtype=torch.float32, device=self.device)
+        need = self.workspace_bytes(nseq, Lt, chunk)
+        if need == 0:
+            raise L.MilError(L.MIL_E_INVALID, "mil_ssm_prefill_workspace_bytes")
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
+        off = (-ws.data_ptr()) % 256
+        wsv = ws[off:]
+        st = L.lib().mil_ssm_prefill(ctypes.byref(self.desc), slot0, nseq, Lt, chunk, _ptr(x), _ptr(B), _ptr(C),
+                                     _ptr(dt), _ptr(A), _ptr(D), _ptr(y if want_y else None), _ptr(wsv),
+                                     wsv.numel(), L.MIL_PREFILL_CONTINUE if cont else 0, _stream(self.device))
+        L.check(st, "mil_ssm_prefill")
+        return y
+
+    def verify(self, x, B, C, dt, A, D, y=None):
+        """Outputs y [batch][K][H][P] for K drafts from each slot's logical state."""
+        K = x.shape[1]
+        self._check_tokens("verify", x, B, C, dt)
+        if y is None:
+            y = torch.empty((self.batch, K, self.H, self.P), dtype=torch.float32, device=self.device)
+        st = L.lib().mil_ssm_verify(ctypes.byref(self.desc), K, _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
+                                    _ptr(D), _ptr(y), _stream(self.device))
+        L.check(st, "mil_ssm_verify")
+        return y
+
+    def commit(self, accepted, x, B, dt, A=None, D=None, materialize=False):
+        """Keep the first accepted[b] drafts of each slot (device int32 [batch])."""
+        K = x.shape[1]
+        self._check_tokens("commit", x, B, dt)
+        if accepted.dtype != torch.int32 or accepted.device != self.device:
+            raise TypeError("accepted must be an int32 tensor on the cache's device")
+        st = L.lib().mil_ssm_commit(ctypes.byref(self.desc), K, _ptr(accepted), _ptr(x), _ptr(B), _ptr(dt),
+                                    _ptr(A), _ptr(D), L.MIL_COMMIT_MATERIALIZE if materialize else 0,
+                                    _stream(self.device))
+        L.check(st, "mil_ssm_commit")

@@ -1,0 +1,328 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Each test draws seeded synthetic inputs (speculative_decode_amd.synth), runs the GPU
+path, runs the oracle on exactly the same (bf16-rounded or fp32) values widened to
+double, and compares with the slice-normwise metric of gpu_util (1e-5 for fp32
+inputs, 2e-3 for bf16).  Integer cases and the roll-back invariants are compared
+bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (TOL, dev, dev_layer, dev_tokens, head_slice, state_err, y_err)
+from speculative_decode_amd import synth
+from speculative_decode_amd.ssm import SSMCache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from speculative_decode_amd import _lib
+    _lib.lib()  # a missing library is a failure, not a skip
+
+
+def sync_np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def logical_state(cache: SSMCache) -> np.ndarray:
+    """Stored state; only meaningful when no rows are pending."""
+    torch.cuda.synchronize()
+    assert int(cache.pending().max().item()) == 0
+    return cache.state().cpu().numpy().astype(np.float64)
+
+
+def make_layer_and_tokens(rng, batch, T, H, P, N, G, dtype, a_mode="cfg"):
+    layer = synth.draw_layer(rng, H)
+    if a_mode == "zero":
+        layer = synth.Layer(synth.quantize(np.zeros(H), synth.F32), layer.D)
+    elif a_mode == "tiny":
+        layer = synth.Layer(synth.quantize(np.full(H, -1e-3), synth.F32), layer.D)
+    tok = synth.draw_tokens(rng, batch, T, H, P, N, G, dtype)
+    return layer, tok
+
+
+# --------------------------------------------------------------------------- prefill
+
+PREFILL_CASES = []
+for dtype in (synth.F32, synth.BF16):
+    for L in (1, 63, 64, 65, 255, 256, 257, 1000):
+        for chunk in (64, 256):
+            PREFILL_CASES.append((dtype, L, chunk, "cfg"))
+    for a_mode in ("zero", "tiny"):
+        for (L, chunk) in ((300, 64), (1000, 128), (600, 256)):
+            PREFILL_CASES.append((dtype, L, chunk, a_mode))
+
+
+@pytest.mark.parametrize("dtype,L,chunk,a_mode", PREFILL_CASES)
+def test_prefill_matches_oracle(dtype, L, chunk, a_mode):
+    rng = np.random.default_rng(7000 + L + chunk)
+    Bt, H, P, N, G = 2, 4, 32, 32, 2
+    layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, dtype, a_mode)
+    cache = SSMCache(Bt, H, P, N, G, 4, dtype)
+    A, D = dev_layer(layer)
+    y = sync_np(cache.prefill(*dev_tokens(tok), A, D, chunk=chunk))
+    ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
+    ey, es = y_err(y, ry), state_err(logical_state(cache), rs)
+    print(f"prefill {dtype} L={L} chunk={chunk} A={a_mode}: y {ey:.2e} state {es:.2e}")
+    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    assert cache.pos().cpu().tolist() == [L] * Bt
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 16, 16, 1), (2, 4, 64, 16, 4), (1, 2, 128, 64, 1), (1, 4, 256, 32, 2),
+                                   (1, 2, 16, 256, 2)])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_prefill_shapes(shape, dtype):
+    Bt, H, P, N, G = shape
+    rng = np.random.default_rng(sum(shape))
+    layer, tok = make_layer_and_tokens(rng, Bt, 300, H, P, N, G, dtype)
+    cache = SSMCache(Bt, H, P, N, G, 4, dtype)
+    y = sync_np(cache.prefill(*dev_tokens(tok), *dev_layer(layer), chunk=128))
+    ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
+    assert y_err(y, ry) <= TOL[dtype]
+    assert state_err(logical_state(cache), rs) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_integer_linear_attention_is_exact(dtype):
+    """A = 0, dt = 1, inputs in {-1, 0, 1}: every value is an exact small integer, so
+    prefill, verify and the folded state must match the oracle exactly."""
+    rng = np.random.default_rng(31)
+    Bt, L, K, H, P, N, G = 2, 150, 4, 4, 32, 16, 2
+    tok = synth.integer_tokens(rng, Bt, L + K, H, P, N, G, dtype)
+    layer = synth.Layer(synth.quantize(np.zeros(H), synth.F32),
+                        synth.quantize(rng.integers(-2, 3, size=H).astype(np.float64), synth.F32))
+    pre = synth.slice_tokens(tok, 0, Bt, 0, L)
+    drf = synth.slice_tokens(tok, 0, Bt, L, L + K)
+    cache = SSMCache(Bt, H, P, N, G, K, dtype)
+    A, D = dev_layer(layer)
+    y = sync_np(cache.prefill(*dev_tokens(pre), A, D, chunk=64))
+    ry, rs = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64)
+    assert np.array_equal(y.astype(np.float64), ry)
+    assert np.array_equal(logical_state(cache), rs)
+    yv = sync_np(cache.verify(*dev_tokens(drf), A, D))
+    assert np.array_equal(yv.astype(np.float64),
+                          oracle.verify(rs, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, layer.A.f64, layer.D.f64))
+    j = np.array([3, 1], dtype=np.int32)
+    dx, dB, dC, ddt = dev_tokens(drf)
+    cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt, A, D, materialize=True)
+    assert np.array_equal(logical_state(cache),
+                          oracle.commit(rs, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j))
+
+
+def test_prefill_continue_after_pending_rows():
+    """prefill L1, verify K, commit j (deferred), prefill L2 with CONTINUE == prefill of
+    L1 + j accepted drafts + L2."""
+    rng = np.random.default_rng(41)
+    Bt, L1, K, L2, H, P, N, G = 2, 100, 4, 157, 4, 32, 32, 2
+    dtype = synth.BF16
+    layer, tok = make_layer_and_tokens(rng, Bt, L1 + K + L2, H, P, N, G, dtype)
+    a = synth.slice_tokens(tok, 0, Bt, 0, L1)
+    d = synth.slice_tokens(tok, 0, Bt, L1, L1 + K)
+    c = synth.slice_tokens(tok, 0, Bt, L1 + K, L1 + K + L2)
+    cache = SSMCache(Bt, H, P, N, G, K, dtype)
+    A, D = dev_layer(layer)
+    cache.prefill(*dev_tokens(a), A, D, chunk=64)
+    dx, dB, dC, ddt = dev_tokens(d)
+    cache.verify(dx, dB, dC, ddt, A, D)
+    j = np.array([2, 4], dtype=np.int32)
+    cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt)
+    y2 = sync_np(cache.prefill(*dev_tokens(c), A, D, chunk=64, cont=True))
+    _, h1 = oracle.prefill(a.x.f64, a.B.f64, a.C.f64, a.dt.f64, layer.A.f64, layer.D.f64)
+    h1 = oracle.commit(h1, d.x.f64, d.B.f64, d.dt.f64, layer.A.f64, layer.D.f64, j)
+    ry, rs = oracle.prefill(c.x.f64, c.B.f64, c.C.f64, c.dt.f64, layer.A.f64, layer.D.f64, h0=h1)
+    assert y_err(y2, ry) <= TOL[dtype]
+    assert state_err(logical_state(cache), rs) <= TOL[dtype]
+    assert cache.pos().cpu().tolist() == [L1 + int(j[0]) + L2, L1 + int(j[1]) + L2]
+
+
+# --------------------------------------------------------------------------- verify / commit
+
+def test_tiny_f32_protocol_against_oracle():
+    """The tiny fp32 workload: prefill 64 tokens, then rounds of verify K=4 and commit
+    j ~ U{0..4}; every y and the final state against the oracle at 1e-5."""
+    w = synth.WORKLOADS["tiny_f32"]
+    rng = np.random.default_rng(w.seed)
+    layer = synth.draw_layer(rng, w.H)
+    pre = synth.draw_tokens(rng, w.batch, w.L, w.H, w.P, w.N, w.G, w.dtype)
+    cache = SSMCache(w.batch, w.H, w.P, w.N, w.G, w.K, w.dtype)
+    A, D = dev_layer(layer)
+    y = sync_np(cache.prefill(*dev_tokens(pre), A, D, chunk=w.chunk))
+    ry, ref = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64)
+    assert y_err(y, ry) <= 1e-5
+    assert state_err(logical_state(cache), ref) <= 1e-5
+    total = w.L
+    for r in range(8):
+        drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
+        j = synth.draw_accept_uniform(rng, w.batch, w.K)
+        dx, dB, dC, ddt = dev_tokens(drf)
+        yv = sync_np(cache.verify(dx, dB, dC, ddt, A, D))
+        ey = y_err(yv, oracle.verify(ref, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, layer.A.f64, layer.D.f64))
+        assert ey <= 1e-5, (r, ey)
+        cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt, A, D, materialize=(r == 7))
+        ref = oracle.commit(ref, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j)
+        total += int(j[0])
+    assert state_err(logical_state(cache), ref) <= 1e-5
+    assert cache.pos().cpu().tolist() == [total]
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("shape", [(3, 4, 16, 16, 2), (2, 4, 32, 64, 1), (2, 2, 128, 128, 1), (2, 4, 64, 256, 2),
+                                   (1, 2, 256, 32, 2)])
+@pytest.mark.parametrize("K,k_max", [(1, 1), (4, 4), (5, 8), (8, 8), (16, 16)])
+def test_verify_rounds_against_oracle(dtype, shape, K, k_max):
+    """Several rounds with ragged accepted lengths per sequence: y of every round and
+    pos exactly; the final folded state against the oracle."""
+    Bt, H, P, N, G = shape
+    rng = np.random.default_rng(100 * K + Bt * H + P + N)
+    layer, pre = make_layer_and_tokens(rng, Bt, 37, H, P, N, G, dtype)
+    cache = SSMCache(Bt, H, P, N, G, k_max, dtype)
+    A, D = dev_layer(layer)
+    cache.prefill(*dev_tokens(pre), A, D, chunk=64, want_y=False)
+    _, ref = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64)
+    pos = np.full(Bt, 37)
+    for r in range(4):
+        drf = synth.draw_tokens(rng, Bt, K, H, P, N, G, dtype)
+        j = synth.draw_accept_uniform(rng, Bt, K)
+        if r == 1:
+            j[:] = K
+        if r == 2:
+            j[:] = 0
+        dx, dB, dC, ddt = dev_tokens(drf)
+        yv = sync_np(cache.verify(dx, dB, dC, ddt, A, D))
+        ry = oracle.verify(ref, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, layer.A.f64, layer.D.f64)
+        assert y_err(yv, ry) <= TOL[dtype], r
+        cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt, A, D, materialize=(r == 3))
+        ref = oracle.commit(ref, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j)
+        pos += j
+    assert np.array_equal(cache.pos().cpu().numpy(), pos)
+    assert state_err(logical_state(cache), ref) <= TOL[dtype]
+
+
+def _prefilled_cache(rng, Bt, H, P, N, G, k_max, dtype, L=50):
+    layer, pre = make_layer_and_tokens(rng, Bt, L, H, P, N, G, dtype)
+    cache = SSMCache(Bt, H, P, N, G, k_max, dtype)
+    A, D = dev_layer(layer)
+    cache.prefill(*dev_tokens(pre), A, D, chunk=64, want_y=False)
+    return layer, pre, cache, A, D
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_rollback_is_bit_exact(dtype):
+    """Keeping j of K drafts gives the same raw state bits as verifying only those j
+    drafts, and as j single-token rounds (one state step, one order, everywhere)."""
+    Bt, H, P, N, G, K = 1, 4, 128, 128, 2, 8
+    for j in range(K + 1):
+        states = []
+        seed = 500 + j
+        layer, _, _, _, _ = _prefilled_cache(np.random.default_rng(seed), Bt, H, P, N, G, K, dtype)
+        drf = synth.draw_tokens(np.random.default_rng(seed + 1), Bt, K, H, P, N, G, dtype)
+        for mode in ("all_K", "only_j", "single"):
+            _, _, cache, A, D = _prefilled_cache(np.random.default_rng(seed), Bt, H, P, N, G, K, dtype)
+            jj = torch.tensor([j], dtype=torch.int32, device="cuda")
+            if mode == "all_K":
+                dx, dB, dC, ddt = dev_tokens(drf)
+                cache.verify(dx, dB, dC, ddt, A, D)
+                cache.commit(jj, dx, dB, ddt, A, D, materialize=True)
+            elif mode == "only_j" and j > 0:
+                d = synth.slice_tokens(drf, 0, Bt, 0, j)
+                dx, dB, dC, ddt = dev_tokens(d)
+                cache.verify(dx, dB, dC, ddt, A, D)
+                cache.commit(jj, dx, dB, ddt, A, D, materialize=True)
+            elif mode == "single":
+                one = torch.tensor([1], dtype=torch.int32, device="cuda")
+                for i in range(j):
+                    d = synth.slice_tokens(drf, 0, Bt, i, i + 1)
+                    dx, dB, dC, ddt = dev_tokens(d)
+                    cache.verify(dx, dB, dC, ddt, A, D)
+                    cache.commit(one, dx, dB, ddt, A, D, materialize=(i == j - 1))
+            torch.cuda.synchronize()
+            states.append(cache.state().contiguous().view(torch.int32).cpu().numpy())
+        assert np.array_equal(states[0], states[1]), j
+        assert np.array_equal(states[0], states[2]), j
+
+
+def test_commit_zero_then_same_drafts_gives_same_y():
+    rng = np.random.default_rng(61)
+    Bt, H, P, N, G, K = 2, 4, 128, 128, 2, 4
+    layer, _, cache, A, D = _prefilled_cache(rng, Bt, H, P, N, G, K, synth.BF16)
+    # leave pending rows so that the first verify has something to fold
+    d0 = synth.draw_tokens(rng, Bt, K, H, P, N, G, synth.BF16)
+    dx, dB, dC, ddt = dev_tokens(d0)
+    cache.verify(dx, dB, dC, ddt, A, D)
+    cache.commit(torch.tensor([3, 2], dtype=torch.int32, device="cuda"), dx, dB, ddt)
+    d1 = synth.draw_tokens(rng, Bt, K, H, P, N, G, synth.BF16)
+    dx, dB, dC, ddt = dev_tokens(d1)
+    y1 = cache.verify(dx, dB, dC, ddt, A, D).clone()
+    cache.commit(torch.zeros(Bt, dtype=torch.int32, device="cuda"), dx, dB, ddt)
+    y2 = cache.verify(dx, dB, dC, ddt, A, D).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    cache.commit(torch.zeros(Bt, dtype=torch.int32, device="cuda"), dx, dB, ddt)
+
+
+def test_repeated_runs_are_bitwise_equal():
+    outs = []
+    for _ in range(2):
+        rng = np.random.default_rng(71)
+        Bt, H, P, N, G, K = 2, 8, 128, 128, 2, 8
+        layer, pre, cache, A, D = _prefilled_cache(rng, Bt, H, P, N, G, K, synth.BF16, L=700)
+        y = cache.prefill(*dev_tokens(pre), A, D, chunk=256)
+        d = synth.draw_tokens(rng, Bt, K, H, P, N, G, synth.BF16)
+        yv = cache.verify(*dev_tokens(d), A, D)
+        torch.cuda.synchronize()
+        outs.append((y.cpu(), yv.cpu(), cache.state().contiguous().cpu()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_bad_accepted_length_sets_error_and_changes_nothing():
+    rng = np.random.default_rng(81)
+    Bt, H, P, N, G, K = 3, 4, 64, 32, 2, 4
+    layer, pre, cache, A, D = _prefilled_cache(rng, Bt, H, P, N, G, K, synth.BF16)
+    _, ref = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64)
+    drf = synth.draw_tokens(rng, Bt, K, H, P, N, G, synth.BF16)
+    dx, dB, dC, ddt = dev_tokens(drf)
+    cache.verify(dx, dB, dC, ddt, A, D)
+    j = np.array([K + 1, -1, 2], dtype=np.int32)
+    cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt, A, D, materialize=True)
+    assert cache.status() == 0
+    assert cache.err().cpu().tolist() == [1, 1, 0]
+    assert cache.pos().cpu().tolist() == [50, 50, 52]
+    ref = oracle.commit(ref, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, np.array([0, 0, 2]))
+    assert state_err(logical_state(cache), ref) <= TOL[synth.BF16]
+    assert cache.status(clear=True) == 0
+    assert cache.status() == -1
+    # the protocol goes on
+    cache.verify(dx, dB, dC, ddt, A, D)
+    cache.commit(torch.zeros(Bt, dtype=torch.int32, device="cuda"), dx, dB, ddt)
+
+
+def test_protocol_order_errors():
+    from speculative_decode_amd._lib import MilError, MIL_E_ORDER
+    rng = np.random.default_rng(91)
+    Bt, H, P, N, G, K = 1, 2, 16, 16, 1, 4
+    layer, pre, cache, A, D = _prefilled_cache(rng, Bt, H, P, N, G, K, synth.F32)
+    d = synth.draw_tokens(rng, Bt, K, H, P, N, G, synth.F32)
+    dx, dB, dC, ddt = dev_tokens(d)
+    with pytest.raises(MilError) as e:
+        cache.commit(torch.zeros(1, dtype=torch.int32, device="cuda"), dx, dB, ddt)
+    assert e.value.status == MIL_E_ORDER
+    cache.verify(dx, dB, dC, ddt, A, D)
+    with pytest.raises(MilError) as e:
+        cache.verify(dx, dB, dC, ddt, A, D)
+    assert e.value.status == MIL_E_ORDER
+    with pytest.raises(MilError) as e:
+        cache.prefill(*dev_tokens(pre), A, D)
+    assert e.value.status == MIL_E_ORDER
+    with pytest.raises(TypeError):
+        cache.commit(torch.zeros(1, dtype=torch.int32, device="cuda"), dx.to(torch.bfloat16), dB, ddt)
+    cache.commit(torch.zeros(1, dtype=torch.int32, device="cuda"), dx, dB, ddt)
