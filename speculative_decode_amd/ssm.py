@@ -55,6 +55,8 @@ class SSMCache:
         self.dtype_code = _dtype_code(dtype)
         self.torch_dtype = _TORCH[self.dtype_code]
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.dims = L.Dims(batch, H, P, N, G)
         self.layout = cache_layout(batch, H, P, N, G, k_max, self.dtype_code)
         nbytes = self.layout.bytes
@@ -110,6 +112,19 @@ class SSMCache:
             if not t.is_contiguous() or t.device != self.device:
                 raise ValueError(f"{what}: tensors must be contiguous and on {self.device}")
 
+    def _check_shapes(self, what, nseq, T, x, B, C, dt, A, D, y):
+        """The ABI takes bare pointers, so sizes are checked here before any call."""
+        want = {"x": (nseq, T, self.H, self.P), "B": (nseq, T, self.G, self.N), "C": (nseq, T, self.G, self.N),
+                "dt": (nseq, T, self.H), "A": (self.H,), "D": (self.H,), "y": (nseq, T, self.H, self.P)}
+        for name, t in (("x", x), ("B", B), ("C", C), ("dt", dt), ("A", A), ("D", D), ("y", y)):
+            if t is None:
+                continue
+            if tuple(t.shape) != want[name]:
+                raise ValueError(f"{what}: {name} has shape {tuple(t.shape)}, expected {want[name]}")
+            if name in ("A", "D", "y") and (t.dtype != torch.float32 or not t.is_contiguous()
+                                            or t.device != self.device):
+                raise TypeError(f"{what}: {name} must be a contiguous float32 tensor on {self.device}")
+
     # ---- the three calls ----
     def workspace_bytes(self, nseq, L_tokens, chunk=256) -> int:
         return L.lib().mil_ssm_prefill_workspace_bytes(ctypes.byref(self.dims), nseq, L_tokens, chunk)
@@ -121,6 +136,9 @@ class SSMCache:
         self._check_tokens("prefill", x, B, C, dt)
         if want_y and y is None:
             y = torch.empty((nseq, Lt, self.H, self.P), dtype=torch.float32, device=self.device)
+        self._check_shapes("prefill", nseq, Lt, x, B, C, dt, A, D, y if want_y else None)
+        if not 0 <= slot0 <= self.batch - nseq:
+            raise ValueError("prefill: slots out of range")
         need = self.workspace_bytes(nseq, Lt, chunk)
         if need == 0:
             raise L.MilError(L.MIL_E_INVALID, "mil_ssm_prefill_workspace_bytes")
@@ -140,6 +158,7 @@ class SSMCache:
         self._check_tokens("verify", x, B, C, dt)
         if y is None:
             y = torch.empty((self.batch, K, self.H, self.P), dtype=torch.float32, device=self.device)
+        self._check_shapes("verify", self.batch, K, x, B, C, dt, A, D, y)
         st = L.lib().mil_ssm_verify(ctypes.byref(self.desc), K, _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
                                     _ptr(D), _ptr(y), _stream(self.device))
         L.check(st, "mil_ssm_verify")
@@ -151,6 +170,9 @@ class SSMCache:
         self._check_tokens("commit", x, B, dt)
         if accepted.dtype != torch.int32 or accepted.device != self.device:
             raise TypeError("accepted must be an int32 tensor on the cache's device")
+        if tuple(accepted.shape) != (self.batch,) or not accepted.is_contiguous():
+            raise ValueError(f"commit: accepted must have shape ({self.batch},)")
+        self._check_shapes("commit", self.batch, K, x, B, None, dt, A, D, None)
         st = L.lib().mil_ssm_commit(ctypes.byref(self.desc), K, _ptr(accepted), _ptr(x), _ptr(B), _ptr(dt),
                                     _ptr(A), _ptr(D), L.MIL_COMMIT_MATERIALIZE if materialize else 0,
                                     _stream(self.device))
