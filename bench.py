@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSM layer's hot path on one MI355X.
+
+Default workload (`llama8b_single`): one Llama-3-8B-shaped sequence (32 heads, P = N =
+128, 8 B/C groups, bf16 token inputs, fp32 state).  One step is the whole path once:
+  prefill of a 1024-token prompt (chunk 256)  ->  verify K = 4 drafts  ->  commit j ~ U{0..4}
+on a fresh cache slot; steps rotate through independent caches and inputs whose total
+size exceeds the 256 MB Infinity Cache, so every step reads its inputs from HBM.
+
+Printed JSON line:
+  value                verified tokens/s = batch*K / (verify + commit time per step)
+  prefill_tokens_per_s batch*L / (prefill time per step)
+  hbm_gbs              verify's algorithmic bytes / verify kernel time
+  ms_per_step          whole step (prefill + verify + commit), HIP events
+  roofline             for the kernel with the largest time per step (HIP events around
+                       its launches, recorded by the library's trace hook)
+  cpu_baseline         the CPU oracle on a bounded sample of the same step
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
+KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "speculative_decode_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------- algorithmic work
+
+def elt(dtype):
+    return 2 if dtype == "bf16" else 4
+
+
+def prefill_work(w, L):
+    """Algorithmic bytes and flops of one sequence's prefill, per phase.
+    Bytes count what the method must move (inputs, fp32 y, final state); the chunk
+    states in the workspace are the implementation's, not the method's."""
+    e = elt(w.dtype)
+    hpg = w.H // w.G
+    inp_state = L * (w.H * w.P + w.G * w.N + w.H) * e           # x, B, dt
+    inp_out = L * (w.H * w.P + 2 * w.G * w.N + w.H) * e         # x, B, C, dt
+    y = L * w.H * w.P * 4
+    st = w.H * w.N * w.P * 4
+    fl_state = fl_out = 0
+    for c0 in range(0, L, w.chunk):
+        q = min(w.chunk, L - c0)
+        fl_state += w.H * 2 * q * w.N * w.P                    # B^T (w X)
+        fl_out += w.H * (q * q * w.N / hpg + q * q * w.P + 2 * q * w.N * w.P)  # causal C B^T, M X, C h_in
+    return {"prefill_state": (inp_state, fl_state), "prefill_pass": (st, 2 * (L // w.chunk + 1) * w.H * w.N * w.P),
+            "prefill_out": (inp_out + y, fl_out), "all": (inp_out + y + st, fl_state + fl_out)}
+
+
+def verify_work(w, batch, K, pending):
+    """Algorithmic bytes and flops of one verify launch: state read once, written once
+    where rows are folded, token rows of the folded and draft tokens, fp32 y."""
+    e = elt(w.dtype)
+    S = w.H * w.N * w.P * 4
+    byt = batch * S + sum(S for m in pending if m > 0)
+    byt += sum((m + K) * (w.H * w.P + w.G * w.N + w.H) * e for m in pending) + batch * K * w.G * w.N * e
+    byt += batch * K * w.H * w.P * 4
+    fl = sum(w.H * w.N * w.P * (3 * m + 5 * K) for m in pending)
+    return byt, fl
+
+
+def commit_work(w, j):
+    e = elt(w.dtype)
+    return sum(2 * a * (w.H * w.P + w.G * w.N + w.H) * e for a in j) + 4 * 3 * len(j), 0
+
+
+# --------------------------------------------------------------------------- GPU run
+
+def run_gpu(args, w):
+    import torch
+
+    from speculative_decode_amd import _lib as L
+    from speculative_decode_amd import synth
+    from speculative_decode_amd.ssm import SSMCache
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    rng = np.random.default_rng(w.seed)
+    layer = synth.draw_layer(rng, w.H)
+
+    def to_dev(t):
+        if t.dtype == synth.BF16:
+            return torch.from_numpy(np.ascontiguousarray(t.store).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(t.store)).to(dev)
+
+    A, D = to_dev(layer.A), to_dev(layer.D)
+    Lp, K, Bt = w.L, w.K, w.batch
+    # enough independent (cache, prompt, drafts) sets to exceed the 256 MB Infinity Cache
+    nch = (Lp + w.chunk - 1) // w.chunk
+    per_set = Bt * (prefill_work(w, Lp)["all"][0] + nch * w.H * w.N * w.P * 4)  # inputs, y, state, workspace
+    R = args.rotate or max(2, min(64, int(np.ceil(320e6 / per_set))))
+    sets = []
+    for r in range(R):
+        pre = synth.draw_tokens(rng, Bt, Lp, w.H, w.P, w.N, w.G, w.dtype)
+        drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
+        j = synth.draw_accept_uniform(rng, Bt, K)
+        cache = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
+        ws = torch.empty(cache.workspace_bytes(Bt, Lp, w.chunk) + 256, dtype=torch.uint8, device=dev)
+        y = torch.empty((Bt, Lp, w.H, w.P), dtype=torch.float32, device=dev)
+        yv = torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev)
+        sets.append(dict(cache=cache, pre=[to_dev(t) for t in (pre.x, pre.B, pre.C, pre.dt)],
+                         drf=[to_dev(t) for t in (drf.x, drf.B, drf.C, drf.dt)],
+                         j=torch.from_numpy(j).to(dev), jn=j, ws=ws, y=y, yv=yv))
+    lib = L.lib()
+
+    def step(s):
+        st = sets[s % R]
+        c = st["cache"]
+        x, B, C, dt = st["pre"]
+        c.prefill(x, B, C, dt, A, D, y=st["y"], chunk=w.chunk, ws=st["ws"])
+        evs["mid"][s].record()
+        dx, dB, dC, ddt = st["drf"]
+        c.verify(dx, dB, dC, ddt, A, D, y=st["yv"])
+        c.commit(st["j"], dx, dB, ddt)
+
+    import ctypes
+
+    def set_trace(s, name):
+        c = sets[s % R]["cache"]
+        if name is None:
+            lib.mil_ssm_cache_trace(ctypes.byref(c.desc), 0, None, None)
+        else:
+            a, b = evs["ta"][s], evs["tb"][s]
+            lib.mil_ssm_cache_trace(ctypes.byref(c.desc), L.TRACE[name], ctypes.c_void_p(a.cuda_event),
+                                    ctypes.c_void_p(b.cuda_event))
+
+    n_ev = max(args.steps, args.warmup, len(KERNELS) * 4)
+    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in ("beg", "mid", "end", "ta", "tb")}
+    for e in evs["ta"] + evs["tb"]:
+        e.record()  # creates the underlying hipEvent so that its handle can be passed down
+    torch.cuda.synchronize()
+
+    # warmup, then one pass per kernel to find the one with the largest time per step
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ktime = {}
+    for i, name in enumerate(KERNELS):
+        for rep in range(4):
+            s = i * 4 + rep
+            set_trace(s, name)
+            step(s)
+            set_trace(s, None)
+        torch.cuda.synchronize()
+        ktime[name] = float(np.mean([evs["ta"][i * 4 + r].elapsed_time(evs["tb"][i * 4 + r]) for r in range(4)]))
+    dominant = max(ktime, key=ktime.get)
+
+    # timed region: K steps, the dominant kernel traced on every step
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        set_trace(s, dominant)
+        evs["beg"][s].record()
+        step(s)
+        evs["end"][s].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in range(args.steps):
+        set_trace(s, None)
+    pre_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["mid"][s]) for s in range(args.steps)]))
+    vc_ms = float(np.mean([evs["mid"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+    step_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+    dom_ms = float(np.mean([evs["ta"][s].elapsed_time(evs["tb"][s]) for s in range(args.steps)]))
+
+    # algorithmic work per launch of each kernel (pending rows: the previous commit of
+    # each slot was folded by the prefill that starts every step, so verify folds none)
+    pw = prefill_work(w, Lp)
+    work = {k: (pw[k][0] * Bt, pw[k][1] * Bt) for k in ("prefill_state", "prefill_pass", "prefill_out")}
+    work["verify"] = verify_work(w, Bt, K, [0] * Bt)
+    jmean = float(np.mean([st["jn"].mean() for st in sets]))
+    work["commit"] = commit_work(w, [jmean] * Bt)
+    return dict(R=R, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant, dom_ms=dom_ms,
+                ktime=ktime, work=work, verify_ms=ktime["verify"], device=torch.cuda.get_device_name(dev))
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def run_cpu_baseline(w, budget_s=12.0, max_steps=8):
+    import oracle
+    from speculative_decode_amd import synth
+    rng = np.random.default_rng(w.seed + 77)
+    layer = synth.draw_layer(rng, w.H)
+    threads = oracle.default_threads()
+    t_pre = t_vc = 0.0
+    steps = 0
+    while steps < max_steps and (t_pre + t_vc) < budget_s:
+        pre = synth.draw_tokens(rng, w.batch, w.L, w.H, w.P, w.N, w.G, w.dtype)
+        drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
+        j = synth.draw_accept_uniform(rng, w.batch, w.K)
+        a = time.perf_counter()
+        _, h = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64, nthreads=threads)
+        b = time.perf_counter()
+        oracle.verify(h, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, layer.A.f64, layer.D.f64, nthreads=threads)
+        oracle.commit(h, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j, nthreads=threads)
+        c = time.perf_counter()
+        t_pre += b - a
+        t_vc += c - b
+        steps += 1
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=w.batch * w.K * steps / t_vc, unit="verified tokens/s", cores=threads, kind="oracle",
+                prefill_tokens_per_s=w.batch * w.L * steps / t_pre, cpu=cpu,
+                sample=f"{steps} whole steps (prefill {w.L} + verify {w.K} + commit) of the same shapes, "
+                       f"fp64 oracle, {t_pre + t_vc:.1f} s")
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_single")
+    ap.add_argument("--rotate", type=int, default=0, help="independent cache/input sets (0: enough for >320 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the run, time a plain elementwise copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the SSM path has no cross-GPU step in this build)", file=sys.stderr)
+        sys.exit(2)
+    from speculative_decode_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    if w.L <= 0 or w.K <= 0:
+        print(f"workload {args.workload} has no prefill+verify step; use llama8b_single or tiny_f32", file=sys.stderr)
+        sys.exit(2)
+    args.steps = max(1, args.steps)
+    g = run_gpu(args, w)
+
+    if args.copy_mib:
+        import torch
+        n = args.copy_mib * 1024 * 1024 // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+
+    K, Bt, L = w.K, w.batch, w.L
+    dom = g["dominant"]
+    byt, fl = g["work"][dom]
+    t = g["dom_ms"] * 1e-3
+    bf16 = w.dtype == "bf16"
+    if dom in ("prefill_out", "prefill_state") and bf16 and fl / byt > (BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3):
+        roof = dict(bound="mfma", achieved=fl / t / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
+    else:
+        roof = dict(bound="hbm", achieved=byt / t / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["kernel_ms"] = g["dom_ms"]
+    roof["flops_per_launch"] = fl
+    roof["bytes_per_launch"] = byt
+    roof["mfma_frac_bf16"] = fl / t / 1e12 / BF16_PEAK_TFLOPS
+    roof["hbm_frac"] = byt / t / 1e9 / HBM_PEAK_GBS
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get(f"{dom}/{args.workload}")
+            if ent and ent.get("source_sha") == source_hash():
+                roof["traffic"] = ent["bytes_per_launch"]
+        except (OSError, ValueError, KeyError):
+            pass
+    vb, _ = g["work"]["verify"]
+    kern = {k: dict(ms=g["ktime"][k], GBps=g["work"][k][0] / (g["ktime"][k] * 1e-3) / 1e9,
+                    TFLOPs=g["work"][k][1] / (g["ktime"][k] * 1e-3) / 1e12) for k in KERNELS}
+    out = {
+        "metric": "verified tokens/s + HBM GB/s (K-step SSM verify); prefill scan tokens/s",
+        "value": Bt * K / (g["vc_ms"] * 1e-3),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": g["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, f32 state/accumulate" if bf16 else "f32",
+        "data": "synthetic (seeded numpy PCG64; random layer parameters, no trained weights)",
+        "config": {"workload": w.name, "batch": Bt, "heads": w.H, "headdim": w.P, "dstate": w.N, "groups": w.G,
+                   "prefill_len": L, "chunk": w.chunk, "drafts_K": K, "accept": "j ~ U{0..K}",
+                   "rotating_sets": g["R"], "parallelism": "single GPU"},
+        "prefill_tokens_per_s": Bt * L / (g["pre_ms"] * 1e-3),
+        "verify_commit_ms": g["vc_ms"],
+        "prefill_ms": g["pre_ms"],
+        "hbm_gbs": vb / (g["ktime"]["verify"] * 1e-3) / 1e9,
+        "roofline": roof,
+        "kernels": kern,
+        "wall_s_timed": g["wall"],
+        "device": g["device"],
+        "source_sha": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_cpu_baseline(w)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -186,6 +186,23 @@ int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t 
 /* Protocol phase of a cache descriptor: 0 = uninitialised, 1 = READY, 2 = VERIFIED. */
 int mil_ssm_cache_phase(const mil_ssm_cache *cache);
 
+/* Kernels that can be traced with mil_ssm_cache_trace. */
+enum mil_trace_kernel {
+    MIL_TRACE_OFF = 0,
+    MIL_TRACE_VERIFY = 1,        /* verify: fold pending rows + K draft outputs */
+    MIL_TRACE_FOLD = 2,          /* fold-only pass (commit with MIL_COMMIT_MATERIALIZE, prefill continue) */
+    MIL_TRACE_COMMIT = 3,        /* accepted-length bookkeeping */
+    MIL_TRACE_PREFILL_STATE = 4, /* prefill phase 1: per-chunk states */
+    MIL_TRACE_PREFILL_PASS = 5,  /* prefill phase 2: sequential pass across chunks */
+    MIL_TRACE_PREFILL_OUT = 6    /* prefill phase 3: per-chunk outputs */
+};
+
+/* Profiling hook: until changed, every launch of `kernel` made through this descriptor
+ * is bracketed by hipEventRecord(ev_start) and hipEventRecord(ev_stop) on the call's
+ * stream (both are hipEvent_t handles created by the caller).  MIL_TRACE_OFF (or NULL
+ * events) turns it off.  Host-side only: nothing is enqueued by this call. */
+int mil_ssm_cache_trace(mil_ssm_cache *cache, int32_t kernel, void *ev_start, void *ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -267,4 +267,18 @@ int mil_ssm_cache_phase(const mil_ssm_cache *cache) {
     return c ? c->phase : kUninit;
 }
 
+int mil_ssm_cache_trace(mil_ssm_cache *cache, int32_t kernel, void *ev_start, void *ev_stop) {
+    CacheImpl *c = impl(cache);
+    if (!c || kernel < MIL_TRACE_OFF || kernel > MIL_TRACE_PREFILL_OUT) return MIL_E_INVALID;
+    if (kernel == MIL_TRACE_OFF || !ev_start || !ev_stop) {
+        c->trace_kernel = MIL_TRACE_OFF;
+        c->trace_start = c->trace_stop = nullptr;
+        return MIL_OK;
+    }
+    c->trace_kernel = kernel;
+    c->trace_start = static_cast<hipEvent_t>(ev_start);
+    c->trace_stop = static_cast<hipEvent_t>(ev_stop);
+    return MIL_OK;
+}
+
 }  // extern "C"

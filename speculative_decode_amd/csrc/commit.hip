@@ -110,7 +110,9 @@ hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, con
     p.K = K;
     p.k_max = c.k_max;
     p.dt_elt = e;
+    trace_begin(c, MIL_TRACE_COMMIT, s);
     hipLaunchKernelGGL(ssm_commit_kernel, dim3(c.dims.batch), dim3(256), 0, s, p);
+    trace_end(c, MIL_TRACE_COMMIT, s);
     return hipGetLastError();
 }
 

@@ -297,21 +297,27 @@ hipError_t launch_prefill(const CacheImpl &c, int slot0, int nseq, int L, int ch
 
     const int rows = min(p.N, 16384 / p.P);  // 64 state elements per thread
     const int slabs = p.N / rows;
+    trace_begin(c, MIL_TRACE_PREFILL_STATE, s);
     if (c.dtype == MIL_BF16)
         hipLaunchKernelGGL(chunk_state_valu<uint16_t>, dim3(p.nch, p.H, nseq * slabs), dim3(256), 0, s, p, rows, slabs);
     else
         hipLaunchKernelGGL(chunk_state_valu<float>, dim3(p.nch, p.H, nseq * slabs), dim3(256), 0, s, p, rows, slabs);
+    trace_end(c, MIL_TRACE_PREFILL_STATE, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t NP = (int64_t)p.N * p.P;
+    trace_begin(c, MIL_TRACE_PREFILL_PASS, s);
     hipLaunchKernelGGL(state_pass_kernel, dim3((unsigned)((NP + 255) / 256), p.H, nseq), dim3(256), 0, s, p);
+    trace_end(c, MIL_TRACE_PREFILL_PASS, s);
     e = hipGetLastError();
     if (e != hipSuccess || y == nullptr) return e;
     const dim3 g3((chunk + kTile - 1) / kTile, p.nch, p.H * nseq);
+    trace_begin(c, MIL_TRACE_PREFILL_OUT, s);
     if (c.dtype == MIL_BF16)
         hipLaunchKernelGGL(chunk_out_valu<uint16_t>, g3, dim3(256), 0, s, p);
     else
         hipLaunchKernelGGL(chunk_out_valu<float>, g3, dim3(256), 0, s, p);
+    trace_end(c, MIL_TRACE_PREFILL_OUT, s);
     return hipGetLastError();
 }
 

@@ -23,7 +23,18 @@ struct CacheImpl {
     char *base;
     int64_t bytes;
     mil_ssm_layout lay;
+    int32_t trace_kernel;  // mil_trace_kernel, MIL_TRACE_OFF when not tracing
+    int32_t pad2_;
+    hipEvent_t trace_start, trace_stop;
 };
+
+// Event records around one launch of kernel `id` when the descriptor traces it.
+inline void trace_begin(const CacheImpl &c, int id, hipStream_t s) {
+    if (c.trace_kernel == id && c.trace_start) (void)hipEventRecord(c.trace_start, s);
+}
+inline void trace_end(const CacheImpl &c, int id, hipStream_t s) {
+    if (c.trace_kernel == id && c.trace_stop) (void)hipEventRecord(c.trace_stop, s);
+}
 static_assert(sizeof(CacheImpl) <= sizeof(mil_ssm_cache), "cache descriptor too large");
 
 inline float *cache_state(const CacheImpl &c) { return reinterpret_cast<float *>(c.base + c.lay.state_off); }

@@ -33,8 +33,12 @@ hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B
     vp.k_max = c.k_max;
     const int kt = c.k_max <= 4 ? 4 : (c.k_max <= 8 ? 8 : 16);  // bounds both K and pending
     const int batch = c.dims.batch;
-    if (c.dtype == MIL_BF16) return dispatch_verify_bf16(vp, kt, batch, s);
-    return dispatch_verify_f32(vp, kt, batch, s);
+    const int id = K > 0 ? MIL_TRACE_VERIFY : MIL_TRACE_FOLD;
+    trace_begin(c, id, s);
+    const hipError_t e = c.dtype == MIL_BF16 ? dispatch_verify_bf16(vp, kt, batch, s)
+                                             : dispatch_verify_f32(vp, kt, batch, s);
+    trace_end(c, id, s);
+    return e;
 }
 
 }  // namespace mil
