@@ -182,10 +182,8 @@ int mil_ssm_prefill(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L
     if (cont) {
         // fold pending accepted rows of every slot (a no-op where pending == 0)
         e = launch_verify(*c, 0, nullptr, nullptr, nullptr, nullptr, A, D, nullptr, s);
-        if (e == hipSuccess) e = launch_clear_pending(*c, s);
     }
     if (e == hipSuccess) e = launch_prefill(*c, slot0, nseq, L, chunk, x, B, C, dt, A, D, y, ws, cont, s);
-    if (e == hipSuccess) e = launch_prefill_counters(*c, slot0, nseq, L, cont, s);
     return hip_status(e);
 }
 

@@ -22,8 +22,8 @@ struct CommitParams {
     const uint32_t *x, *B, *dt;        // drafts, viewed as 32-bit words
     uint32_t *px, *pB, *pdt;           // pending rows, viewed as 32-bit words
     int32_t *pos, *pending, *err;
-    int64_t x_row_words, B_row_words;  // words per token row (H*P, G*N elements)
-    int64_t dt_row_bytes;              // bytes per token row of dt (H elements)
+    int x_row_words, B_row_words;  // 32-bit words per token row (H*P, G*N elements)
+    int dt_elems;                  // elements per token row of dt (H)
     int K, k_max, dt_elt;
 };
 
@@ -40,25 +40,23 @@ __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
         }
         return;
     }
-    // x rows: [b][k][H*P] -> [b][k_max slot k][H*P]
-    for (int64_t i = threadIdx.x; i < (int64_t)j * p.x_row_words; i += blockDim.x) {
-        const int64_t k = i / p.x_row_words, w = i % p.x_row_words;
-        p.px[((int64_t)b * p.k_max + k) * p.x_row_words + w] = p.x[((int64_t)b * p.K + k) * p.x_row_words + w];
-    }
-    for (int64_t i = threadIdx.x; i < (int64_t)j * p.B_row_words; i += blockDim.x) {
-        const int64_t k = i / p.B_row_words, w = i % p.B_row_words;
-        p.pB[((int64_t)b * p.k_max + k) * p.B_row_words + w] = p.B[((int64_t)b * p.K + k) * p.B_row_words + w];
-    }
-    // dt rows can be an odd number of bf16 elements long: copy element by element
-    const int64_t dt_elems = p.dt_row_bytes / p.dt_elt;
-    for (int64_t i = threadIdx.x; i < (int64_t)j * dt_elems; i += blockDim.x) {
-        const int64_t k = i / dt_elems, e = i % dt_elems;
-        const int64_t src = ((int64_t)b * p.K + k) * dt_elems + e;
-        const int64_t dst = ((int64_t)b * p.k_max + k) * dt_elems + e;
-        if (p.dt_elt == 2)
-            reinterpret_cast<uint16_t *>(p.pdt)[dst] = reinterpret_cast<const uint16_t *>(p.dt)[src];
-        else
-            p.pdt[dst] = p.dt[src];
+    // accepted rows k < j: [b][k][row] -> [b][k][row] of the pending area (32-bit words)
+    const int xw = p.x_row_words, bw = p.B_row_words, de = p.dt_elems;
+    for (int k = 0; k < j; ++k) {
+        const uint32_t *xs = p.x + ((int64_t)b * p.K + k) * xw;
+        uint32_t *xd = p.px + ((int64_t)b * p.k_max + k) * xw;
+        for (int i = threadIdx.x; i < xw; i += blockDim.x) xd[i] = xs[i];
+        const uint32_t *bs = p.B + ((int64_t)b * p.K + k) * bw;
+        uint32_t *bd = p.pB + ((int64_t)b * p.k_max + k) * bw;
+        for (int i = threadIdx.x; i < bw; i += blockDim.x) bd[i] = bs[i];
+        // dt rows can be an odd number of bf16 elements long: copied element by element
+        const int64_t src = ((int64_t)b * p.K + k) * de, dst = ((int64_t)b * p.k_max + k) * de;
+        for (int i = threadIdx.x; i < de; i += blockDim.x) {
+            if (p.dt_elt == 2)
+                reinterpret_cast<uint16_t *>(p.pdt)[dst + i] = reinterpret_cast<const uint16_t *>(p.dt)[src + i];
+            else
+                p.pdt[dst + i] = p.dt[src + i];
+        }
     }
     if (threadIdx.x == 0) {
         p.pending[b] = j;
@@ -69,14 +67,6 @@ __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
 __global__ void clear_pending_kernel(int32_t *pending, int batch) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < batch) pending[i] = 0;
-}
-
-__global__ void prefill_counters_kernel(int32_t *pos, int32_t *pending, int slot0, int nseq, int L, int cont) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < nseq) {
-        pos[slot0 + i] = cont ? pos[slot0 + i] + L : L;
-        pending[slot0 + i] = 0;
-    }
 }
 
 }  // namespace
@@ -104,9 +94,9 @@ hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, con
     p.pending = cache_pending(c);
     p.err = cache_err(c);
     // H*P and G*N are multiples of 16 (P, N >= 16), so these rows are whole words
-    p.x_row_words = (int64_t)c.dims.nheads * c.dims.headdim * e / 4;
-    p.B_row_words = (int64_t)c.dims.ngroups * c.dims.dstate * e / 4;
-    p.dt_row_bytes = (int64_t)c.dims.nheads * e;
+    p.x_row_words = c.dims.nheads * c.dims.headdim * e / 4;
+    p.B_row_words = c.dims.ngroups * c.dims.dstate * e / 4;
+    p.dt_elems = c.dims.nheads;
     p.K = K;
     p.k_max = c.k_max;
     p.dt_elt = e;
@@ -119,12 +109,6 @@ hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, con
 hipError_t launch_clear_pending(const CacheImpl &c, hipStream_t s) {
     const int n = c.dims.batch;
     hipLaunchKernelGGL(clear_pending_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cache_pending(c), n);
-    return hipGetLastError();
-}
-
-hipError_t launch_prefill_counters(const CacheImpl &c, int slot0, int nseq, int L, bool cont, hipStream_t s) {
-    hipLaunchKernelGGL(prefill_counters_kernel, dim3((nseq + 255) / 256), dim3(256), 0, s, cache_pos(c),
-                       cache_pending(c), slot0, nseq, L, cont ? 1 : 0);
     return hipGetLastError();
 }
 

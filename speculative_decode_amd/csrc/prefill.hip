@@ -15,8 +15,8 @@
 // most one 16-token tile, or a direct sum of whole-tile totals, so each factor's
 // relative error is a few ulps of its own exponent.
 //
-// This file holds the reference-grade fp32 vector-ALU form used for fp32 inputs; the
-// bf16 path adds matrix-core versions of phases 1 and 3.
+// This file holds the fp32 vector-ALU form, used for fp32 inputs and for shapes the
+// matrix-core form (prefill_mfma.hip, bf16 inputs) does not cover.
 #include "ssm_internal.h"
 
 namespace mil {
@@ -37,7 +37,9 @@ struct PrefillParams {
     int64_t head_stride;   // floats
     float *ws_state;       // [nseq][nch][H][N][P]
     float *ws_tot;         // [nseq][nch][H]
+    int32_t *pos, *pending;  // cache counters (whole batch)
     int L, Q, nch, H, P, N, G;
+    int slot0, nseq, batch;
     int cont;
 };
 
@@ -118,6 +120,14 @@ __global__ __launch_bounds__(256) void chunk_state_valu(const PrefillParams p, i
 // writes the final state into the cache.
 __global__ __launch_bounds__(256) void state_pass_kernel(const PrefillParams p) {
     const int h = blockIdx.y, seq = blockIdx.z;
+    if (blockIdx.x == 0 && h == 0 && seq == 0) {
+        // counters: the prefilled slots absorb L tokens; nothing is pending afterwards
+        for (int i = threadIdx.x; i < p.batch; i += blockDim.x) {
+            const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
+            if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
+            if (mine || p.cont) p.pending[i] = 0;
+        }
+    }
     const int64_t NP = (int64_t)p.N * p.P;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= NP) return;
@@ -273,6 +283,10 @@ int64_t prefill_workspace_bytes(const mil_ssm_dims &d, int nseq, int L, int chun
 hipError_t launch_prefill(const CacheImpl &c, int slot0, int nseq, int L, int chunk, const void *x,
                           const void *B, const void *C, const void *dt, const float *A,
                           const float *D, float *y, void *ws, bool cont, hipStream_t s) {
+    const auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    if (c.dtype == MIL_BF16 && prefill_mfma_supported(chunk, c.dims.dstate, c.dims.headdim) && a16(x) &&
+        a16(B) && a16(C))
+        return launch_prefill_mfma(c, slot0, nseq, L, chunk, x, B, C, dt, A, D, y, ws, cont, s);
     PrefillParams p;
     p.x = x;
     p.B = B;
@@ -291,6 +305,11 @@ hipError_t launch_prefill(const CacheImpl &c, int slot0, int nseq, int L, int ch
     p.N = c.dims.dstate;
     p.G = c.dims.ngroups;
     p.cont = cont ? 1 : 0;
+    p.pos = cache_pos(c);
+    p.pending = cache_pending(c);
+    p.slot0 = slot0;
+    p.nseq = nseq;
+    p.batch = c.dims.batch;
     const int64_t states = (int64_t)nseq * p.nch * p.H * p.N * p.P * 4;
     p.ws_state = static_cast<float *>(ws);
     p.ws_tot = reinterpret_cast<float *>(static_cast<char *>(ws) + (states + 255) / 256 * 256);

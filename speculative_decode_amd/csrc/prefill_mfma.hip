@@ -1,0 +1,548 @@
+// Matrix-core (MFMA) form of the chunked prefill for bf16 token inputs.
+//
+// Same three phases as the vector-ALU form (chunk states, a short sequential pass
+// across chunks, chunk outputs), which is the layer of "The Mamba in the Llama"
+// (skycaiji.com summary, method paragraph: discretised linear RNN, expanded state,
+// hardware-aware decomposition) regrouped by chunk.  Within a chunk the dense parts
+// run on v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulation):
+//   phase 1   S^T[p][n]  = sum_s X[s][p] * (w_s B[s][n]),       w_s = dt_s decay(s, end)
+//   phase 3   Z = B_J C_I^T  (= G^T tile, G = C B^T),  M = mask(Z) * decay * dt,
+//             Y_I += M X_J  (+ D on the diagonal),  Y_I = exp(a_t) C_I h_in + ...
+// The token inputs are exact in bf16.  Operands derived in fp32 (w_s B, the masked M,
+// the carried state h_in) are split into hi + lo bf16 parts and both products are
+// accumulated, which keeps them to about 16 mantissa bits.
+//
+// Register layouts of the 32x32x16 instruction (lane l, half hf = l / 32):
+//   A: row l%32, k-slots (hf, v);  B: column l%32, k-slots (hf, v);  A and B pair by (hf, v).
+//   D: column l%32, register r holds row 8(r/4) + 4hf + r%4.
+// Phase 3 computes Z with B_J as A and C_I as B, so each lane's D registers hold one
+// output row t (= its column) and 16 source tokens s: exactly an A operand for M X
+// once the k-slot (hf, v) <-> s correspondence is applied to how X is read from LDS.
+#include "ssm_internal.h"
+
+namespace mil {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kT = 32;  // MFMA tile edge and decay tile (tokens)
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+__device__ __forceinline__ float bf2f(bf16 v) { return static_cast<float>(v); }
+// hi = nearest bf16 of v, lo = nearest bf16 of the remainder
+__device__ __forceinline__ void split(float v, bf16 &hi, bf16 &lo) {
+    hi = static_cast<bf16>(v);
+    lo = static_cast<bf16>(v - static_cast<float>(hi));
+}
+
+struct MParams {
+    const uint16_t *x, *B, *C, *dt;  // bf16 bit patterns
+    const float *A, *D;
+    float *y;
+    float *state;          // cache state of slot0
+    int64_t head_stride;   // floats
+    float *ws;             // [nseq][nch][H][P][N] fp32 chunk states, then h_in as hi/lo bf16
+    float *ws_tot;         // [nseq][nch][H]
+    int32_t *pos, *pending;
+    int L, Q, nch, H, P, N, G;
+    int slot0, nseq, batch, cont;
+    int PS, nslab;         // phase 1: state rows p per workgroup, slabs per chunk-head
+};
+
+// Work-item order with consecutive items on one XCD: workgroups are dealt to the 8 XCDs
+// round-robin, so item = xcd * (n/8) + k keeps the heads of one chunk (which share B and
+// C rows) in one L2.
+__device__ __forceinline__ int xcd_item(int n) {
+    const int b = blockIdx.x;
+    return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
+}
+
+// Per-token decay factors of one chunk (32-token tiles; sums local to a tile or over
+// whole-tile totals, so each exponent's rounding is relative to its own size).
+//   R[t]    = sum_{tile start..t} dtA          (inclusive, within t's tile)
+//   suf[s]  = sum_{s+1..tile end} dtA          (exclusive, within s's tile)
+//   tot[i]  = sum over tile i
+__device__ void chunk_factors(const float *dtA, int len, float *R, float *suf, float *tot, int tid, int nt) {
+    for (int t = tid; t < len; t += nt) {
+        const int ts = t / kT * kT, te = min(ts + kT, len) - 1;
+        float r = 0.f;
+        for (int q = ts; q <= t; ++q) r += dtA[q];
+        float l = 0.f;
+        for (int q = te; q > t; --q) l += dtA[q];
+        R[t] = r;
+        suf[t] = l;
+    }
+    __syncthreads();
+    const int ntile = (len + kT - 1) / kT;
+    if (tid < ntile) tot[tid] = R[min(tid * kT + kT, len) - 1];
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------------- phase 1
+// One workgroup (4 waves) per (seq, chunk, head, p-slab): S^T[p][n] for p in the slab.
+// Tokens go through LDS in blocks of 64: X^T (bf16) and (w B)^T split hi/lo.
+constexpr int kSB = 64;       // token block
+constexpr int kSBS = kSB + 8; // padded LDS row (elements), 16-B aligned rows
+
+template <int TPW>
+__global__ __launch_bounds__(256) void chunk_state_mfma(const MParams p) {
+    extern __shared__ __align__(16) char lds[];
+    const int PS = p.PS, N = p.N, H = p.H, P = p.P, G = p.G;
+    const int nitems = p.nseq * p.nch * H * p.nslab;
+    const int item = xcd_item(nitems);
+    const int slab = item % p.nslab;
+    const int h = (item / p.nslab) % H;
+    const int c = (item / p.nslab / H) % p.nch;
+    const int seq = item / p.nslab / H / p.nch;
+    const int g = h / (H / G);
+    const int c0 = c * p.Q, len = min(p.Q, p.L - c0), p0 = slab * PS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+
+    bf16 *sXT = reinterpret_cast<bf16 *>(lds);    // [PS][kSBS]
+    bf16 *sWh = sXT + PS * kSBS;                   // [N][kSBS]
+    bf16 *sWl = sWh + N * kSBS;                    // [N][kSBS]
+    float *sDtA = reinterpret_cast<float *>(sWl + N * kSBS);  // [256]
+    float *sW = sDtA + 256;                        // [256]
+    float *sR = sW + 256, *sSuf = sR + 256, *sTot = sSuf + 256;  // [256],[256],[8]
+
+    const size_t tok0 = (size_t)seq * p.L + c0;
+    const float Ah = p.A[h];
+    for (int s = tid; s < len; s += 256) sDtA[s] = bf2f(p.dt[(tok0 + s) * H + h]) * Ah;
+    __syncthreads();
+    chunk_factors(sDtA, len, sR, sSuf, sTot, tid, 256);
+    const int ntile = (len + kT - 1) / kT;
+    for (int s = tid; s < len; s += 256) {
+        // decay from s to the chunk end: rest of s's tile, then whole later tiles
+        float e = sSuf[s];
+        for (int q = s / kT + 1; q < ntile; ++q) e += sTot[q];
+        sW[s] = __expf(e) * bf2f(p.dt[(tok0 + s) * H + h]);
+    }
+    if (tid == 0 && slab == 0) {
+        float tt = 0.f;
+        for (int q = 0; q < ntile; ++q) tt += sTot[q];
+        p.ws_tot[((size_t)seq * p.nch + c) * H + h] = tt;
+    }
+
+    // output tiles of this wave: (pt, nt) pairs, TPW of them
+    const int ntiles = N / kT;
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
+
+    for (int sb = 0; sb < len; sb += kSB) {
+        __syncthreads();
+        // X^T block: thread item = (s quad, 8-column group); 4 rows of 8 bf16 -> 8 rows of 4
+        for (int it = tid; it < (kSB / 4) * (PS / 8); it += 256) {
+            const int sq = it / (PS / 8), pg = it % (PS / 8);
+            uint4 v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = sb + sq * 4 + r;
+                v[r] = s < len ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + s) * H + h) * P + p0 + pg * 8)
+                               : make_uint4(0, 0, 0, 0);
+            }
+            const uint16_t *e0 = reinterpret_cast<const uint16_t *>(&v[0]);
+            const uint16_t *e1 = reinterpret_cast<const uint16_t *>(&v[1]);
+            const uint16_t *e2 = reinterpret_cast<const uint16_t *>(&v[2]);
+            const uint16_t *e3 = reinterpret_cast<const uint16_t *>(&v[3]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint2 w;
+                w.x = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
+                w.y = (uint32_t)e2[i] | ((uint32_t)e3[i] << 16);
+                *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * kSBS + sq * 4) = w;
+            }
+        }
+        // (w B)^T block, split hi/lo
+        for (int it = tid; it < (kSB / 4) * (N / 8); it += 256) {
+            const int sq = it / (N / 8), ng = it % (N / 8);
+            float wv[4];
+            uint4 v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = sb + sq * 4 + r;
+                const bool ok = s < len;
+                wv[r] = ok ? sW[s] : 0.f;
+                v[r] = ok ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + s) * G + g) * N + ng * 8)
+                          : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                bf16x4 hi, lo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float b = bf2f(reinterpret_cast<const uint16_t *>(&v[r])[i]);
+                    bf16 a, z;
+                    split(wv[r] * b, a, z);
+                    hi[r] = a;
+                    lo[r] = z;
+                }
+                *reinterpret_cast<bf16x4 *>(sWh + (ng * 8 + i) * kSBS + sq * 4) = hi;
+                *reinterpret_cast<bf16x4 *>(sWl + (ng * 8 + i) * kSBS + sq * 4) = lo;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tile = wave * TPW + i;
+            const int pt = tile / ntiles, nt = tile % ntiles;
+#pragma unroll
+            for (int ks = 0; ks < kSB / 16; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sXT + (pt * kT + l32) * kSBS + ks * 16 + hf * 8);
+                const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(sWh + (nt * kT + l32) * kSBS + ks * 16 + hf * 8);
+                const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(sWl + (nt * kT + l32) * kSBS + ks * 16 + hf * 8);
+                acc[i] = mfma(a, bh, acc[i]);
+                acc[i] = mfma(a, bl, acc[i]);
+            }
+        }
+    }
+    // S^T tile -> workspace [p][n] (lane: column n, rows p)
+    float *out = p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int tile = wave * TPW + i;
+        const int pt = tile / ntiles, nt = tile % ntiles;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int pr = p0 + pt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+            out[(size_t)pr * N + nt * kT + l32] = acc[i][r];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------- phase 2
+// Sequential pass across chunks in the [p][n] layout, 8 consecutive n per thread.
+// Each chunk's 32 bytes of fp32 S_c are replaced in place by the state entering that
+// chunk as 8 hi bf16 followed by 8 lo bf16.  The final state goes to the cache in its
+// [n][p] layout through an LDS transpose (and the starting state comes in the same way).
+// grid (P/32 * N/64, H, nseq), 256 threads: 32 p x 8 groups of 8 n.
+__global__ __launch_bounds__(256) void state_pass_pn(const MParams p) {
+    __shared__ float sT[64][33];
+    const int h = blockIdx.y, seq = blockIdx.z;
+    const int N = p.N, P = p.P;
+    const int ntl = N / 64;
+    const int ptile = blockIdx.x / ntl, ntile = blockIdx.x % ntl;
+    const int tid = threadIdx.x;
+    const int pl = tid >> 3, ng = tid & 7;
+    const int pcol = ptile * 32 + pl, n0 = ntile * 64 + ng * 8;
+    if (blockIdx.x == 0 && h == 0 && seq == 0) {
+        for (int i = tid; i < p.batch; i += blockDim.x) {
+            const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
+            if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
+            if (mine || p.cont) p.pending[i] = 0;
+        }
+    }
+    float *cache = p.state + (size_t)(seq * p.H + h) * p.head_stride;
+    float hv[8];
+    if (p.cont) {
+        // coalesced rows n of the cache -> LDS -> this thread's 8 n of column pcol
+        for (int i = tid; i < 64 * 32; i += 256) {
+            const int n = i / 32, q = i % 32;
+            sT[n][q] = cache[(size_t)(ntile * 64 + n) * P + ptile * 32 + q];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = sT[ng * 8 + i][pl];
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = 0.f;
+    }
+    const size_t NP = (size_t)P * N;
+    for (int c = 0; c < p.nch; ++c) {
+        const size_t ch = ((size_t)seq * p.nch + c) * p.H + h;
+        float *slot = p.ws + ch * NP + (size_t)pcol * N + n0;
+        const float4 s0 = *reinterpret_cast<const float4 *>(slot);
+        const float4 s1 = *reinterpret_cast<const float4 *>(slot + 4);
+        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            bf16 a, b;
+            split(hv[i], a, b);
+            hi[i] = a;
+            lo[i] = b;
+        }
+        *reinterpret_cast<bf16x8 *>(slot) = hi;
+        *reinterpret_cast<bf16x8 *>(slot + 4) = lo;
+        const float e = __expf(p.ws_tot[ch]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = __builtin_fmaf(e, hv[i], sc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sT[ng * 8 + i][pl] = hv[i];
+    __syncthreads();
+    for (int i = tid; i < 64 * 32; i += 256) {
+        const int n = i / 32, q = i % 32;
+        cache[(size_t)(ntile * 64 + n) * P + ptile * 32 + q] = sT[n][q];
+    }
+}
+
+// ------------------------------------------------------------------------- phase 3
+// One workgroup per (seq, chunk, head); Q/64 waves, each owning the 32-row tiles
+// I = wave and nt-1-wave (equal work: the causal part of tile I has I+1 column tiles).
+template <int N, int P>
+__global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
+    extern __shared__ __align__(16) char lds[];
+    const int H = p.H, G = p.G, Q = p.Q;
+    const int nitems = p.nseq * p.nch * H;
+    const int item = xcd_item(nitems);
+    const int h = item % H, c = (item / H) % p.nch, seq = item / H / p.nch;
+    const int g = h / (H / G);
+    const int c0 = c * Q, len = min(Q, p.L - c0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+    const int NT = blockDim.x;
+    const int BS = N + 8, XS = Q + 4;  // padded LDS rows (elements)
+
+    bf16 *sB = reinterpret_cast<bf16 *>(lds);      // [Q][BS]   B rows of the chunk
+    bf16 *sXT = sB + Q * BS;                        // [P][XS]   X^T of the chunk
+    float *sDt = reinterpret_cast<float *>(sXT + P * XS);  // [Q]
+    float *sDtA = sDt + Q, *sR = sDtA + Q, *sSuf = sR + Q, *sColf = sSuf + Q, *sEin = sColf + Q;
+    float *sTot = sEin + Q;                         // [8]
+    float *sMid = sTot + 8;                         // [8][8]
+
+    const size_t tok0 = (size_t)seq * p.L + c0;
+    const float Ah = p.A[h], Dh = p.D[h];
+    for (int s = tid; s < Q; s += NT) {
+        const float d = s < len ? bf2f(p.dt[(tok0 + s) * H + h]) : 0.f;
+        sDt[s] = d;
+        sDtA[s] = d * Ah;
+    }
+    // B rows (zero past the chunk end)
+    for (int it = tid; it < Q * (N / 8); it += NT) {
+        const int s = it / (N / 8), ng = it % (N / 8);
+        const uint4 v = s < len ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + s) * G + g) * N + ng * 8)
+                                : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(sB + s * BS + ng * 8) = v;
+    }
+    // X^T (zero past the chunk end: those columns meet zero weights, but 0 * NaN is not 0)
+    for (int it = tid; it < (Q / 4) * (P / 8); it += NT) {
+        const int sq = it / (P / 8), pg = it % (P / 8);
+        uint4 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = sq * 4 + r;
+            v[r] = s < len ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + s) * H + h) * P + pg * 8)
+                           : make_uint4(0, 0, 0, 0);
+        }
+        const uint16_t *e0 = reinterpret_cast<const uint16_t *>(&v[0]);
+        const uint16_t *e1 = reinterpret_cast<const uint16_t *>(&v[1]);
+        const uint16_t *e2 = reinterpret_cast<const uint16_t *>(&v[2]);
+        const uint16_t *e3 = reinterpret_cast<const uint16_t *>(&v[3]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint2 w;
+            w.x = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
+            w.y = (uint32_t)e2[i] | ((uint32_t)e3[i] << 16);
+            *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * XS + sq * 4) = w;
+        }
+    }
+    __syncthreads();
+    chunk_factors(sDtA, len, sR, sSuf, sTot, tid, NT);
+    const int ntile = (len + kT - 1) / kT;
+    for (int s = tid; s < len; s += NT) {
+        sColf[s] = sDt[s] * __expf(sSuf[s]);  // dt_s * decay(s, end of s's tile)
+        float m = sR[s];
+        for (int q = 0; q < s / kT; ++q) m += sTot[q];
+        sEin[s] = __expf(m);                  // decay from the chunk start through s
+    }
+    if (tid < 64) {
+        const int I = tid / 8, J = tid % 8;
+        float m = 0.f;
+        for (int q = J + 1; q < I; ++q) m += sTot[q];
+        sMid[tid] = (J < I && I < ntile) ? __expf(m) : 0.f;  // whole tiles strictly between J and I
+    }
+    __syncthreads();
+
+    const bool has_hin = p.cont || c > 0;
+    const bf16 *hin = reinterpret_cast<const bf16 *>(p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N);
+    const int nt = Q / kT;
+    constexpr int PT = P / kT, NK = N / 16;
+    for (int which = 0; which < 2; ++which) {
+        const int I = which == 0 ? wave : nt - 1 - wave;
+        if (I * kT >= len) continue;
+        const int t = I * kT + l32;  // this lane's output row as an A/B operand index
+        // C rows of this tile: the B operand of Z and the A operand of C h_in
+        bf16x8 cf[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            cf[kk] = t < len ? *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + t) * G + g) * N + kk * 16 + hf * 8)
+                             : bf16x8{};
+        }
+        f32x16 acc[PT];
+#pragma unroll
+        for (int i = 0; i < PT; ++i) acc[i] = f32x16{};
+        if (has_hin) {
+            // acc = C_I h_in (hi + lo), then rows scaled by the decay since the chunk start
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                // row p of the [p][n] slots: fp32-sized, so 2N bf16 per row
+                const bf16 *row = hin + (size_t)(pt * kT + l32) * N * 2;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const bf16 *grp = row + (kk * 2 + hf) * 8 * 2;  // 8 hi then 8 lo
+                    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(grp);
+                    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(grp + 8);
+                    acc[pt] = mfma(cf[kk], bh, acc[pt]);
+                    acc[pt] = mfma(cf[kk], bl, acc[pt]);
+                }
+            }
+            float ein[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ein[r] = sEin[min(I * kT + 8 * (r / 4) + 4 * hf + (r % 4), Q - 1)];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[pt][r] *= ein[r];
+            }
+        }
+        const float et = t < len ? __expf(sR[t]) : 0.f;
+        for (int J = 0; J <= I; ++J) {
+            // Z[s][t] = B_s . C_t for s in tile J (registers: s = 32J + 8(r/4) + 4hf + r%4)
+            f32x16 z = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
+                z = mfma(bfr, cf[kk], z);
+            }
+            // M[t][s]: causal mask, decay, dt_s; D on the diagonal; split hi/lo
+            const float rowf = (I == J) ? 0.f : sMid[I * 8 + J] * et;
+            bf16x8 ah[2], al[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int s = J * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                float m = 0.f;
+                if (s <= t && t < len) {
+                    if (I == J) {
+                        m = z[r] * sDt[s] * __expf(sR[t] - sR[s]);
+                        if (s == t) m += Dh;
+                    } else {
+                        m = z[r] * sColf[s] * rowf;
+                    }
+                }
+                bf16 a, b;
+                split(m, a, b);
+                ah[r / 8][r % 8] = a;
+                al[r / 8][r % 8] = b;
+            }
+            // Y_I += M X_J: B operand slot (hf, v) is X[s][p] for the same s as M's slot
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const bf16 *xr = sXT + (pt * kT + l32) * XS + J * kT + 4 * hf;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(xr + ks * 16);
+                    const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(xr + ks * 16 + 8);
+                    const bf16x8 xv = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                    acc[pt] = mfma(ah[ks], xv, acc[pt]);
+                    acc[pt] = mfma(al[ks], xv, acc[pt]);
+                }
+            }
+        }
+        // y rows of this tile (lane: column p, rows t = 32I + 8(r/4) + 4hf + r%4)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tr = I * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                if (tr < len) p.y[((tok0 + tr) * H + h) * P + pt * kT + l32] = acc[pt][r];
+            }
+        }
+    }
+}
+
+size_t out_lds_bytes(int Q, int N, int P) {
+    return (size_t)Q * (N + 8) * 2 + (size_t)P * (Q + 4) * 2 + 6 * Q * 4 + 8 * 4 + 64 * 4;
+}
+size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 + (4 * 256 + 8) * 4; }
+
+constexpr size_t kLdsMax = 160 * 1024;
+
+}  // namespace
+
+// Shapes the matrix-core path covers: bf16 inputs, N and P multiples of 32 up to 256,
+// a chunk the LDS can hold.
+bool prefill_mfma_supported(int Q, int N, int P) {
+    if (N % 32 != 0 || P % 32 != 0 || N > 256 || P > 256) return false;
+    if (N % 64 != 0) return false;  // phase 2 works on 64-row tiles
+    if (out_lds_bytes(Q, N, P) > kLdsMax) return false;
+    const int PS = P < 32768 / N ? P : 32768 / N;
+    // phase 1 deals (PS/32)*(N/32) output tiles to 4 waves, at most 8 each
+    const int tiles = (PS / 32) * (N / 32);
+    return PS % 32 == 0 && tiles % 4 == 0 && tiles >= 4 && tiles <= 32 && state_lds_bytes(PS, N) <= kLdsMax;
+}
+
+hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, int chunk, const void *x,
+                               const void *B, const void *C, const void *dt, const float *A, const float *D,
+                               float *y, void *ws, bool cont, hipStream_t s) {
+    MParams p;
+    p.x = static_cast<const uint16_t *>(x);
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = static_cast<const uint16_t *>(C);
+    p.dt = static_cast<const uint16_t *>(dt);
+    p.A = A;
+    p.D = D;
+    p.y = y;
+    p.head_stride = c.lay.state_head_stride / 4;
+    p.state = cache_state(c) + (size_t)slot0 * c.dims.nheads * p.head_stride;
+    p.L = L;
+    p.Q = chunk;
+    p.nch = (L + chunk - 1) / chunk;
+    p.H = c.dims.nheads;
+    p.P = c.dims.headdim;
+    p.N = c.dims.dstate;
+    p.G = c.dims.ngroups;
+    p.pos = cache_pos(c);
+    p.pending = cache_pending(c);
+    p.slot0 = slot0;
+    p.nseq = nseq;
+    p.batch = c.dims.batch;
+    p.cont = cont ? 1 : 0;
+    const int64_t states = (int64_t)nseq * p.nch * p.H * p.N * p.P * 4;
+    p.ws = static_cast<float *>(ws);
+    p.ws_tot = reinterpret_cast<float *>(static_cast<char *>(ws) + (states + 255) / 256 * 256);
+    p.PS = p.P < 32768 / p.N ? p.P : 32768 / p.N;
+    p.nslab = p.P / p.PS;
+
+    const size_t l1 = state_lds_bytes(p.PS, p.N), l3 = out_lds_bytes(chunk, p.N, p.P);
+    const int tpw = (p.PS / kT) * (p.N / kT) / 4;
+    const void *k1 = tpw == 1 ? reinterpret_cast<const void *>(chunk_state_mfma<1>)
+                   : tpw == 2 ? reinterpret_cast<const void *>(chunk_state_mfma<2>)
+                   : tpw == 4 ? reinterpret_cast<const void *>(chunk_state_mfma<4>)
+                              : reinterpret_cast<const void *>(chunk_state_mfma<8>);
+    const void *k3 = nullptr;
+#define MIL_OUT_CASE(n, pp) \
+    if (p.N == n && p.P == pp) k3 = reinterpret_cast<const void *>(chunk_out_mfma<n, pp>);
+    MIL_OUT_CASE(64, 32) MIL_OUT_CASE(64, 64) MIL_OUT_CASE(64, 128) MIL_OUT_CASE(64, 256)
+    MIL_OUT_CASE(128, 32) MIL_OUT_CASE(128, 64) MIL_OUT_CASE(128, 128) MIL_OUT_CASE(128, 256)
+    MIL_OUT_CASE(256, 32) MIL_OUT_CASE(256, 64) MIL_OUT_CASE(256, 128) MIL_OUT_CASE(256, 256)
+#undef MIL_OUT_CASE
+    if (!k3) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+    if (e == hipSuccess) e = hipFuncSetAttribute(k3, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+    if (e != hipSuccess) return e;
+    void *args[] = {&p};
+    trace_begin(c, MIL_TRACE_PREFILL_STATE, s);
+    e = hipLaunchKernel(k1, dim3(nseq * p.nch * p.H * p.nslab), dim3(256), args, l1, s);
+    trace_end(c, MIL_TRACE_PREFILL_STATE, s);
+    if (e != hipSuccess) return e;
+    trace_begin(c, MIL_TRACE_PREFILL_PASS, s);
+    hipLaunchKernelGGL(state_pass_pn, dim3((p.P / 32) * (p.N / 64), p.H, nseq), dim3(256), 0, s, p);
+    trace_end(c, MIL_TRACE_PREFILL_PASS, s);
+    e = hipGetLastError();
+    if (e != hipSuccess || y == nullptr) return e;
+    trace_begin(c, MIL_TRACE_PREFILL_OUT, s);
+    e = hipLaunchKernel(k3, dim3(nseq * p.nch * p.H), dim3(chunk / 64 * 64), args, l3, s);
+    trace_end(c, MIL_TRACE_PREFILL_OUT, s);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+}  // namespace mil

@@ -65,14 +65,18 @@ hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, con
 // pending[b] = 0 for every slot (after a fold that has consumed them).
 hipError_t launch_clear_pending(const CacheImpl &c, hipStream_t s);
 
-// Set pos[slot] = L (or += L when cont) and pending[slot] = 0 for slots [slot0, slot0+nseq).
-hipError_t launch_prefill_counters(const CacheImpl &c, int slot0, int nseq, int L, bool cont,
-                                   hipStream_t s);
-
-// Chunked prefill (three phases: chunk states, inter-chunk pass, chunk outputs).
+// Chunked prefill (three phases: chunk states, inter-chunk pass, chunk outputs).  The
+// inter-chunk pass also sets pos[slot] = L (or += L when cont) for the prefilled slots
+// and pending = 0 (for every slot when cont: the fold before it consumed them all).
 int64_t prefill_workspace_bytes(const mil_ssm_dims &d, int nseq, int L, int chunk);
 hipError_t launch_prefill(const CacheImpl &c, int slot0, int nseq, int L, int chunk, const void *x,
                           const void *B, const void *C, const void *dt, const float *A,
                           const float *D, float *y, void *ws, bool cont, hipStream_t s);
+
+// Matrix-core form of the three prefill phases (bf16 inputs; see prefill_mfma_supported).
+bool prefill_mfma_supported(int Q, int N, int P);
+hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, int chunk, const void *x,
+                               const void *B, const void *C, const void *dt, const float *A,
+                               const float *D, float *y, void *ws, bool cont, hipStream_t s);
 
 }  // namespace mil

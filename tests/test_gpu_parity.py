@@ -52,20 +52,24 @@ def make_layer_and_tokens(rng, batch, T, H, P, N, G, dtype, a_mode="cfg"):
 
 # --------------------------------------------------------------------------- prefill
 
+# (B, H, P, N, G): N = 32 takes the vector-ALU kernels; N = 64 / 128 with bf16 inputs
+# takes the matrix-core kernels
+VALU_SHAPE = (2, 4, 32, 32, 2)
+MFMA_SHAPE = (2, 4, 64, 64, 2)
 PREFILL_CASES = []
-for dtype in (synth.F32, synth.BF16):
-    for L in (1, 63, 64, 65, 255, 256, 257, 1000):
+for dtype, shape in ((synth.F32, VALU_SHAPE), (synth.BF16, VALU_SHAPE), (synth.BF16, MFMA_SHAPE)):
+    for L in (1, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1000):
         for chunk in (64, 256):
-            PREFILL_CASES.append((dtype, L, chunk, "cfg"))
+            PREFILL_CASES.append((dtype, shape, L, chunk, "cfg"))
     for a_mode in ("zero", "tiny"):
         for (L, chunk) in ((300, 64), (1000, 128), (600, 256)):
-            PREFILL_CASES.append((dtype, L, chunk, a_mode))
+            PREFILL_CASES.append((dtype, shape, L, chunk, a_mode))
 
 
-@pytest.mark.parametrize("dtype,L,chunk,a_mode", PREFILL_CASES)
-def test_prefill_matches_oracle(dtype, L, chunk, a_mode):
+@pytest.mark.parametrize("dtype,shape,L,chunk,a_mode", PREFILL_CASES)
+def test_prefill_matches_oracle(dtype, shape, L, chunk, a_mode):
     rng = np.random.default_rng(7000 + L + chunk)
-    Bt, H, P, N, G = 2, 4, 32, 32, 2
+    Bt, H, P, N, G = shape
     layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, dtype, a_mode)
     cache = SSMCache(Bt, H, P, N, G, 4, dtype)
     A, D = dev_layer(layer)
@@ -78,25 +82,47 @@ def test_prefill_matches_oracle(dtype, L, chunk, a_mode):
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 16, 16, 1), (2, 4, 64, 16, 4), (1, 2, 128, 64, 1), (1, 4, 256, 32, 2),
-                                   (1, 2, 16, 256, 2)])
+                                   (1, 2, 16, 256, 2), (1, 2, 32, 128, 1), (1, 4, 128, 128, 4), (1, 2, 256, 64, 2),
+                                   (1, 2, 64, 256, 1), (1, 2, 128, 256, 2), (1, 1, 256, 256, 1)])
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
-def test_prefill_shapes(shape, dtype):
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_prefill_shapes(shape, dtype, chunk):
     Bt, H, P, N, G = shape
     rng = np.random.default_rng(sum(shape))
     layer, tok = make_layer_and_tokens(rng, Bt, 300, H, P, N, G, dtype)
     cache = SSMCache(Bt, H, P, N, G, 4, dtype)
-    y = sync_np(cache.prefill(*dev_tokens(tok), *dev_layer(layer), chunk=128))
+    y = sync_np(cache.prefill(*dev_tokens(tok), *dev_layer(layer), chunk=chunk))
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
     assert y_err(y, ry) <= TOL[dtype]
     assert state_err(logical_state(cache), rs) <= TOL[dtype]
 
 
+def test_prefill_misaligned_inputs_take_the_vector_path():
+    """Token tensors only 2-byte aligned cannot use the 16-byte loads of the matrix-core
+    kernels; the result must be the same to tolerance."""
+    rng = np.random.default_rng(37)
+    Bt, L, H, P, N, G = 1, 200, 4, 64, 64, 2
+    layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, synth.BF16)
+    cache = SSMCache(Bt, H, P, N, G, 4, synth.BF16)
+    x, B, C, dt = dev_tokens(tok)
+    xs = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+    xs[1:].copy_(x.reshape(-1))
+    xm = xs[1:].view(x.shape)
+    assert xm.data_ptr() % 16 != 0
+    y = sync_np(cache.prefill(xm, B, C, dt, *dev_layer(layer), chunk=64))
+    ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
+    assert y_err(y, ry) <= TOL[synth.BF16]
+    assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
+
+
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
-def test_integer_linear_attention_is_exact(dtype):
+@pytest.mark.parametrize("shape", [(2, 4, 32, 16, 2), (2, 4, 64, 64, 2)])
+def test_integer_linear_attention_is_exact(dtype, shape):
     """A = 0, dt = 1, inputs in {-1, 0, 1}: every value is an exact small integer, so
     prefill, verify and the folded state must match the oracle exactly."""
     rng = np.random.default_rng(31)
-    Bt, L, K, H, P, N, G = 2, 150, 4, 4, 32, 16, 2
+    Bt, H, P, N, G = shape
+    L, K = 150, 4
     tok = synth.integer_tokens(rng, Bt, L + K, H, P, N, G, dtype)
     layer = synth.Layer(synth.quantize(np.zeros(H), synth.F32),
                         synth.quantize(rng.integers(-2, 3, size=H).astype(np.float64), synth.F32))
@@ -118,11 +144,13 @@ def test_integer_linear_attention_is_exact(dtype):
                           oracle.commit(rs, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j))
 
 
-def test_prefill_continue_after_pending_rows():
+@pytest.mark.parametrize("shape", [VALU_SHAPE, MFMA_SHAPE])
+def test_prefill_continue_after_pending_rows(shape):
     """prefill L1, verify K, commit j (deferred), prefill L2 with CONTINUE == prefill of
     L1 + j accepted drafts + L2."""
     rng = np.random.default_rng(41)
-    Bt, L1, K, L2, H, P, N, G = 2, 100, 4, 157, 4, 32, 32, 2
+    Bt, H, P, N, G = shape
+    L1, K, L2 = 100, 4, 157
     dtype = synth.BF16
     layer, tok = make_layer_and_tokens(rng, Bt, L1 + K + L2, H, P, N, G, dtype)
     a = synth.slice_tokens(tok, 0, Bt, 0, L1)
