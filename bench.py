@@ -71,15 +71,16 @@ def prefill_work(w, L):
             "prefill_out": (inp_out + y, fl_out), "all": (inp_out + y + st, fl_state + fl_out)}
 
 
-def verify_work(w, batch, K, pending):
-    """Algorithmic bytes and flops of one verify launch: state read once, written once
-    where rows are folded, token rows of the folded and draft tokens, fp32 y."""
+def verify_work(w, batch, K, pend_mean, write_frac):
+    """Algorithmic bytes and flops of one verify launch: every slot's state read once,
+    written once where rows are folded (fraction write_frac of the slots), the token rows
+    of the folded (pend_mean per slot on average) and draft tokens, fp32 y."""
     e = elt(w.dtype)
     S = w.H * w.N * w.P * 4
-    byt = batch * S + sum(S for m in pending if m > 0)
-    byt += sum((m + K) * (w.H * w.P + w.G * w.N + w.H) * e for m in pending) + batch * K * w.G * w.N * e
+    byt = batch * S * (1.0 + write_frac)
+    byt += batch * (pend_mean + K) * (w.H * w.P + w.G * w.N + w.H) * e + batch * K * w.G * w.N * e
     byt += batch * K * w.H * w.P * 4
-    fl = sum(w.H * w.N * w.P * (3 * m + 5 * K) for m in pending)
+    fl = batch * w.H * w.N * w.P * (3 * pend_mean + 5 * K)
     return byt, fl
 
 
@@ -90,7 +91,28 @@ def commit_work(w, j):
 
 # --------------------------------------------------------------------------- GPU run
 
+def _to_dev_factory(torch, synth, dev):
+    def to_dev(t):
+        if t.dtype == synth.BF16:
+            return torch.from_numpy(np.ascontiguousarray(t.store).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(t.store)).to(dev)
+    return to_dev
+
+
+def step_kind(w):
+    if w.name == "llama8b_long_prefill":
+        return "prefill"
+    if w.name in ("llama8b_batched", "hybrid_decode"):
+        return "verify"
+    return "full"
+
+
 def run_gpu(args, w):
+    """Times `args.steps` steps.  Step kinds: "full" = prefill + verify + commit on a fresh
+    slot; "verify" = verify + commit on prefilled caches (every layer for the hybrid
+    workload); "prefill" = one long prefill."""
+    import ctypes
+
     import torch
 
     from speculative_decode_amd import _lib as L
@@ -99,67 +121,114 @@ def run_gpu(args, w):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    to_dev = _to_dev_factory(torch, synth, dev)
     rng = np.random.default_rng(w.seed)
-    layer = synth.draw_layer(rng, w.H)
-
-    def to_dev(t):
-        if t.dtype == synth.BF16:
-            return torch.from_numpy(np.ascontiguousarray(t.store).view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(t.store)).to(dev)
-
-    A, D = to_dev(layer.A), to_dev(layer.D)
-    Lp, K, Bt = w.L, w.K, w.batch
-    # enough independent (cache, prompt, drafts) sets to exceed the 256 MB Infinity Cache
-    nch = (Lp + w.chunk - 1) // w.chunk
-    per_set = Bt * (prefill_work(w, Lp)["all"][0] + nch * w.H * w.N * w.P * 4)  # inputs, y, state, workspace
-    R = args.rotate or max(2, min(64, int(np.ceil(320e6 / per_set))))
-    sets = []
-    for r in range(R):
-        pre = synth.draw_tokens(rng, Bt, Lp, w.H, w.P, w.N, w.G, w.dtype)
-        drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
-        j = synth.draw_accept_uniform(rng, Bt, K)
-        cache = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
-        ws = torch.empty(cache.workspace_bytes(Bt, Lp, w.chunk) + 256, dtype=torch.uint8, device=dev)
-        y = torch.empty((Bt, Lp, w.H, w.P), dtype=torch.float32, device=dev)
-        yv = torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev)
-        sets.append(dict(cache=cache, pre=[to_dev(t) for t in (pre.x, pre.B, pre.C, pre.dt)],
-                         drf=[to_dev(t) for t in (drf.x, drf.B, drf.C, drf.dt)],
-                         j=torch.from_numpy(j).to(dev), jn=j, ws=ws, y=y, yv=yv))
+    kind = step_kind(w)
+    Bt, K = w.batch, w.K
+    nlayers = w.layers
+    layers = [synth.draw_layer(rng, w.H) for _ in range(nlayers)]
+    AD = [(to_dev(l.A), to_dev(l.D)) for l in layers]
     lib = L.lib()
+    sets = []
+
+    if kind == "full":
+        Lp = w.L
+        nch = (Lp + w.chunk - 1) // w.chunk
+        per_set = Bt * (prefill_work(w, Lp)["all"][0] + nch * w.H * w.N * w.P * 4)
+        R = args.rotate or max(2, min(64, int(np.ceil(320e6 / per_set))))
+        for r in range(R):
+            pre = synth.draw_tokens(rng, Bt, Lp, w.H, w.P, w.N, w.G, w.dtype)
+            drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
+            j = synth.draw_accept_uniform(rng, Bt, K)
+            cache = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
+            sets.append(dict(caches=[cache], pre=[to_dev(t) for t in (pre.x, pre.B, pre.C, pre.dt)],
+                             drf=[[to_dev(t) for t in (drf.x, drf.B, drf.C, drf.dt)]],
+                             j=[torch.from_numpy(j).to(dev)], jn=[j],
+                             ws=torch.empty(cache.workspace_bytes(Bt, Lp, w.chunk) + 256, dtype=torch.uint8,
+                                            device=dev),
+                             y=torch.empty((Bt, Lp, w.H, w.P), dtype=torch.float32, device=dev),
+                             yv=[torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev)]))
+    elif kind == "prefill":
+        Lp = w.L
+        nch = (Lp + w.chunk - 1) // w.chunk
+        per_set = Bt * (prefill_work(w, Lp)["all"][0] + nch * w.H * w.N * w.P * 4)
+        R = args.rotate or max(1, min(16, int(np.ceil(320e6 / per_set))))
+        for r in range(R):
+            pre = synth.draw_tokens(rng, Bt, Lp, w.H, w.P, w.N, w.G, w.dtype)
+            cache = SSMCache(Bt, w.H, w.P, w.N, w.G, 4, w.dtype, device=dev)
+            sets.append(dict(caches=[cache], pre=[to_dev(t) for t in (pre.x, pre.B, pre.C, pre.dt)],
+                             ws=torch.empty(cache.workspace_bytes(Bt, Lp, w.chunk) + 256, dtype=torch.uint8,
+                                            device=dev),
+                             y=torch.empty((Bt, Lp, w.H, w.P), dtype=torch.float32, device=dev)))
+    else:
+        # prior contexts: per-slot lengths (batched) or a fixed 1024 (hybrid), prefilled once
+        # on the GPU; every other cache is a byte copy of that one (a snapshot)
+        if w.ctx_range:
+            ctx = rng.integers(w.ctx_range[0], w.ctx_range[1] + 1, size=Bt)
+        else:
+            ctx = np.full(Bt, w.L)
+        state_bytes = Bt * w.H * w.N * w.P * 4
+        R = args.rotate or (1 if nlayers > 1 else max(2, min(64, int(np.ceil(320e6 / state_bytes)))))
+        proto = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
+        for b in range(Bt):
+            pre = synth.draw_tokens(rng, 1, int(ctx[b]), w.H, w.P, w.N, w.G, w.dtype)
+            proto.prefill(*[to_dev(t) for t in (pre.x, pre.B, pre.C, pre.dt)], *AD[0], slot0=b,
+                          chunk=128 if w.N > 128 else w.chunk, want_y=False)
+        torch.cuda.synchronize()
+        for r in range(R):
+            caches, drfs, js, jns, yvs = [], [], [], [], []
+            for li in range(nlayers):
+                c = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
+                c.buffer.copy_(proto.buffer)
+                drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
+                j = (synth.draw_accept_geometric(rng, Bt, K) if w.accept == "geometric"
+                     else synth.draw_accept_uniform(rng, Bt, K))
+                caches.append(c)
+                drfs.append([to_dev(t) for t in (drf.x, drf.B, drf.C, drf.dt)])
+                js.append(torch.from_numpy(j).to(dev))
+                jns.append(j)
+                yvs.append(torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev))
+            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs))
+        del proto
+        torch.cuda.synchronize()
+    R = len(sets)
 
     def step(s):
         st = sets[s % R]
-        c = st["cache"]
-        x, B, C, dt = st["pre"]
-        c.prefill(x, B, C, dt, A, D, y=st["y"], chunk=w.chunk, ws=st["ws"])
+        if kind in ("full", "prefill"):
+            x, B, C, dt = st["pre"]
+            st["caches"][0].prefill(x, B, C, dt, *AD[0], y=st["y"], chunk=w.chunk, ws=st["ws"])
         evs["mid"][s].record()
-        dx, dB, dC, ddt = st["drf"]
-        c.verify(dx, dB, dC, ddt, A, D, y=st["yv"])
-        c.commit(st["j"], dx, dB, ddt)
-
-    import ctypes
+        if kind in ("full", "verify"):
+            for li, c in enumerate(st["caches"]):
+                dx, dB, dC, ddt = st["drf"][li]
+                c.verify(dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
+                c.commit(st["j"][li], dx, dB, ddt)
 
     def set_trace(s, name):
-        c = sets[s % R]["cache"]
-        if name is None:
-            lib.mil_ssm_cache_trace(ctypes.byref(c.desc), 0, None, None)
-        else:
+        st = sets[s % R]
+        for c in st["caches"]:
+            if name is None:
+                lib.mil_ssm_cache_trace(ctypes.byref(c.desc), 0, None, None)
+        if name is not None:
+            # trace one cache per step (the first layer's)
             a, b = evs["ta"][s], evs["tb"][s]
-            lib.mil_ssm_cache_trace(ctypes.byref(c.desc), L.TRACE[name], ctypes.c_void_p(a.cuda_event),
-                                    ctypes.c_void_p(b.cuda_event))
+            lib.mil_ssm_cache_trace(ctypes.byref(st["caches"][0].desc), L.TRACE[name],
+                                    ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event))
 
-    n_ev = max(args.steps, args.warmup, len(KERNELS) * 4)
+    kernels = {"full": KERNELS, "prefill": KERNELS[:3], "verify": KERNELS[3:]}[kind]
+    n_ev = max(args.steps, args.warmup, len(kernels) * 4)
     evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in ("beg", "mid", "end", "ta", "tb")}
     for e in evs["ta"] + evs["tb"]:
         e.record()  # creates the underlying hipEvent so that its handle can be passed down
     torch.cuda.synchronize()
 
-    # warmup, then one pass per kernel to find the one with the largest time per step
+    # warmup, then one pass per kernel to find the one with the largest time per launch
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
     ktime = {}
-    for i, name in enumerate(KERNELS):
+    for i, name in enumerate(kernels):
         for rep in range(4):
             s = i * 4 + rep
             set_trace(s, name)
@@ -186,31 +255,40 @@ def run_gpu(args, w):
     step_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
     dom_ms = float(np.mean([evs["ta"][s].elapsed_time(evs["tb"][s]) for s in range(args.steps)]))
 
-    # algorithmic work per launch of each kernel (pending rows: the previous commit of
-    # each slot was folded by the prefill that starts every step, so verify folds none)
-    pw = prefill_work(w, Lp)
-    work = {k: (pw[k][0] * Bt, pw[k][1] * Bt) for k in ("prefill_state", "prefill_pass", "prefill_out")}
-    work["verify"] = verify_work(w, Bt, K, [0] * Bt)
-    jmean = float(np.mean([st["jn"].mean() for st in sets]))
-    work["commit"] = commit_work(w, [jmean] * Bt)
-    return dict(R=R, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant, dom_ms=dom_ms,
-                ktime=ktime, work=work, verify_ms=ktime["verify"], device=torch.cuda.get_device_name(dev))
+    # algorithmic work per launch of each kernel
+    work = {}
+    if kind in ("full", "prefill"):
+        pw = prefill_work(w, w.L)
+        work.update({k: (pw[k][0] * Bt, pw[k][1] * Bt) for k in ("prefill_state", "prefill_pass", "prefill_out")})
+    if kind in ("full", "verify"):
+        # rows pending at a verify: none after a prefill ("full"); else the previous
+        # commit's accepted lengths, whose mean is that of the j distribution
+        jall = np.concatenate([jn for st in sets for jn in st["jn"]])
+        if kind == "full":
+            work["verify"] = verify_work(w, Bt, K, 0.0, 0.0)
+        else:
+            work["verify"] = verify_work(w, Bt, K, float(jall.mean()), float((jall > 0).mean()))
+        work["commit"] = commit_work(w, [float(jall.mean())] * Bt)
+    return dict(R=R, kind=kind, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant,
+                dom_ms=dom_ms, ktime=ktime, work=work, device=torch.cuda.get_device_name(dev))
 
 
 # --------------------------------------------------------------------------- CPU baseline
 
-def run_cpu_baseline(w, budget_s=12.0, max_steps=8):
+def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
+    """The oracle, as it stands, on the same step (prefill + verify + commit) of the same
+    shapes, repeated on one seeded sample until about budget_s seconds of CPU work."""
     import oracle
     from speculative_decode_amd import synth
     rng = np.random.default_rng(w.seed + 77)
     layer = synth.draw_layer(rng, w.H)
     threads = oracle.default_threads()
+    pre = synth.draw_tokens(rng, w.batch, w.L, w.H, w.P, w.N, w.G, w.dtype)
+    drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
+    j = synth.draw_accept_uniform(rng, w.batch, w.K)
     t_pre = t_vc = 0.0
     steps = 0
     while steps < max_steps and (t_pre + t_vc) < budget_s:
-        pre = synth.draw_tokens(rng, w.batch, w.L, w.H, w.P, w.N, w.G, w.dtype)
-        drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
-        j = synth.draw_accept_uniform(rng, w.batch, w.K)
         a = time.perf_counter()
         _, h = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64, nthreads=threads)
         b = time.perf_counter()
@@ -253,11 +331,9 @@ def main():
         sys.exit(2)
     from speculative_decode_amd import synth
     w = synth.WORKLOADS[args.workload]
-    if w.L <= 0 or w.K <= 0:
-        print(f"workload {args.workload} has no prefill+verify step; use llama8b_single or tiny_f32", file=sys.stderr)
-        sys.exit(2)
     args.steps = max(1, args.steps)
     g = run_gpu(args, w)
+    kind = g["kind"]
 
     if args.copy_mib:
         import torch
@@ -293,13 +369,20 @@ def main():
                 roof["traffic"] = ent["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             pass
-    vb, _ = g["work"]["verify"]
     kern = {k: dict(ms=g["ktime"][k], GBps=g["work"][k][0] / (g["ktime"][k] * 1e-3) / 1e9,
-                    TFLOPs=g["work"][k][1] / (g["ktime"][k] * 1e-3) / 1e12) for k in KERNELS}
+                    TFLOPs=g["work"][k][1] / (g["ktime"][k] * 1e-3) / 1e12) for k in g["ktime"]}
+    cfg = {"workload": w.name, "batch": Bt, "heads": w.H, "headdim": w.P, "dstate": w.N, "groups": w.G,
+           "layers": w.layers, "chunk": w.chunk, "rotating_sets": g["R"], "parallelism": "single GPU",
+           "step": {"full": f"prefill {L} + verify {K} + commit", "prefill": f"prefill {L}",
+                    "verify": f"{w.layers} x (verify {K} + commit)"}[kind]}
+    if kind != "prefill":
+        cfg.update({"drafts_K": K, "accept": "j ~ min(Geom(0.3)-1, K)" if w.accept == "geometric" else "j ~ U{0..K}"})
+    if kind != "verify":
+        cfg["prefill_len"] = L
+    if w.ctx_range:
+        cfg["context"] = f"U{{{w.ctx_range[0]}..{w.ctx_range[1]}}} per sequence"
     out = {
         "metric": "verified tokens/s + HBM GB/s (K-step SSM verify); prefill scan tokens/s",
-        "value": Bt * K / (g["vc_ms"] * 1e-3),
-        "unit": "verified tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -309,23 +392,24 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 in, f32 state/accumulate" if bf16 else "f32",
         "data": "synthetic (seeded numpy PCG64; random layer parameters, no trained weights)",
-        "config": {"workload": w.name, "batch": Bt, "heads": w.H, "headdim": w.P, "dstate": w.N, "groups": w.G,
-                   "prefill_len": L, "chunk": w.chunk, "drafts_K": K, "accept": "j ~ U{0..K}",
-                   "rotating_sets": g["R"], "parallelism": "single GPU"},
-        "prefill_tokens_per_s": Bt * L / (g["pre_ms"] * 1e-3),
-        "verify_commit_ms": g["vc_ms"],
-        "prefill_ms": g["pre_ms"],
-        "hbm_gbs": vb / (g["ktime"]["verify"] * 1e-3) / 1e9,
-        "roofline": roof,
-        "kernels": kern,
-        "wall_s_timed": g["wall"],
-        "device": g["device"],
-        "source_sha": source_hash(),
+        "config": cfg,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = run_cpu_baseline(w)
+    if kind == "prefill":
+        out["value"] = Bt * L / (g["pre_ms"] * 1e-3)
+        out["unit"] = "prefill tokens/s"
+        out["prefill_tokens_per_s"] = out["value"]
     else:
-        out["cpu_baseline"] = None
+        out["value"] = Bt * K / (g["vc_ms"] * 1e-3)
+        out["unit"] = "verified tokens/s"
+        vb, _ = g["work"]["verify"]
+        out["hbm_gbs"] = vb / (g["ktime"]["verify"] * 1e-3) / 1e9
+        out["verify_commit_ms"] = g["vc_ms"]
+        if kind == "full":
+            out["prefill_tokens_per_s"] = Bt * L / (g["pre_ms"] * 1e-3)
+            out["prefill_ms"] = g["pre_ms"]
+    out.update({"roofline": roof, "kernels": kern, "wall_s_timed": g["wall"], "device": g["device"],
+                "source_sha": source_hash()})
+    out["cpu_baseline"] = None if args.no_cpu_baseline or kind != "full" else run_cpu_baseline(w)
     print(json.dumps(out))
 
 

@@ -19,49 +19,49 @@ __global__ void fill_zero_kernel(uint32_t *p, int64_t words) {
 
 struct CommitParams {
     const int32_t *accepted;
-    const uint32_t *x, *B, *dt;        // drafts, viewed as 32-bit words
-    uint32_t *px, *pB, *pdt;           // pending rows, viewed as 32-bit words
+    const char *x, *B, *dt;           // drafts [batch][K][row]
+    char *px, *pB, *pdt;              // pending rows [batch][k_max][row]
     int32_t *pos, *pending, *err;
-    int x_row_words, B_row_words;  // 32-bit words per token row (H*P, G*N elements)
-    int dt_elems;                  // elements per token row of dt (H)
-    int K, k_max, dt_elt;
+    int x_row, B_row, dt_row;         // bytes per token row (H*P, G*N, H elements)
+    int K, k_max;
 };
 
-// One workgroup per slot.  A rejected value (j outside 0..K) is reported in err[b]
-// and leaves pos and the pending rows alone; pending becomes 0 because the verify
-// that preceded this commit has already folded the previous rows into the state.
+// Copy `bytes` (a multiple of sizeof(V)) with one vector per thread per pass.
+template <typename V>
+__device__ __forceinline__ void copy_row(char *dst, const char *src, int bytes) {
+    const V *s = reinterpret_cast<const V *>(src);
+    V *d = reinterpret_cast<V *>(dst);
+    const int n = bytes / (int)sizeof(V);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
+}
+
+// grid (K, batch): workgroup (k, b) copies accepted row k of slot b (if k < j); the
+// k = 0 workgroup also does the slot's bookkeeping.  A rejected value (j outside 0..K)
+// is reported in err[b] and leaves pos and the pending rows alone; pending becomes 0
+// because the verify that preceded this commit has already folded the previous rows.
+template <typename V>
 __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
-    const int b = blockIdx.x;
+    const int k = blockIdx.x, b = blockIdx.y;
     const int j = p.accepted[b];
-    if (j < 0 || j > p.K) {
-        if (threadIdx.x == 0) {
+    const bool ok = j >= 0 && j <= p.K;
+    if (k == 0 && threadIdx.x == 0) {
+        if (ok) {
+            p.pending[b] = j;
+            p.pos[b] += j;
+        } else {
             p.err[b] = MIL_DEVERR_ACCEPT;
             p.pending[b] = 0;
         }
-        return;
     }
-    // accepted rows k < j: [b][k][row] -> [b][k][row] of the pending area (32-bit words)
-    const int xw = p.x_row_words, bw = p.B_row_words, de = p.dt_elems;
-    for (int k = 0; k < j; ++k) {
-        const uint32_t *xs = p.x + ((int64_t)b * p.K + k) * xw;
-        uint32_t *xd = p.px + ((int64_t)b * p.k_max + k) * xw;
-        for (int i = threadIdx.x; i < xw; i += blockDim.x) xd[i] = xs[i];
-        const uint32_t *bs = p.B + ((int64_t)b * p.K + k) * bw;
-        uint32_t *bd = p.pB + ((int64_t)b * p.k_max + k) * bw;
-        for (int i = threadIdx.x; i < bw; i += blockDim.x) bd[i] = bs[i];
-        // dt rows can be an odd number of bf16 elements long: copied element by element
-        const int64_t src = ((int64_t)b * p.K + k) * de, dst = ((int64_t)b * p.k_max + k) * de;
-        for (int i = threadIdx.x; i < de; i += blockDim.x) {
-            if (p.dt_elt == 2)
-                reinterpret_cast<uint16_t *>(p.pdt)[dst + i] = reinterpret_cast<const uint16_t *>(p.dt)[src + i];
-            else
-                p.pdt[dst + i] = p.dt[src + i];
-        }
-    }
-    if (threadIdx.x == 0) {
-        p.pending[b] = j;
-        p.pos[b] += j;
-    }
+    if (!ok || k >= j) return;
+    const size_t src = (size_t)b * p.K + k, dst = (size_t)b * p.k_max + k;
+    copy_row<V>(p.px + dst * p.x_row, p.x + src * p.x_row, p.x_row);
+    copy_row<V>(p.pB + dst * p.B_row, p.B + src * p.B_row, p.B_row);
+    // dt rows (H elements) need not be a whole number of vectors
+    const char *ds = p.dt + src * p.dt_row;
+    char *dd = p.pdt + dst * p.dt_row;
+    for (int i = threadIdx.x; i < p.dt_row / 2; i += blockDim.x)
+        reinterpret_cast<uint16_t *>(dd)[i] = reinterpret_cast<const uint16_t *>(ds)[i];
 }
 
 __global__ void clear_pending_kernel(int32_t *pending, int batch) {
@@ -84,24 +84,27 @@ hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, con
     const int e = elt_bytes(c.dtype);
     CommitParams p;
     p.accepted = accepted;
-    p.x = static_cast<const uint32_t *>(x);
-    p.B = static_cast<const uint32_t *>(B);
-    p.dt = static_cast<const uint32_t *>(dt);
-    p.px = static_cast<uint32_t *>(cache_pend_x(c));
-    p.pB = static_cast<uint32_t *>(cache_pend_B(c));
-    p.pdt = static_cast<uint32_t *>(cache_pend_dt(c));
+    p.x = static_cast<const char *>(x);
+    p.B = static_cast<const char *>(B);
+    p.dt = static_cast<const char *>(dt);
+    p.px = static_cast<char *>(cache_pend_x(c));
+    p.pB = static_cast<char *>(cache_pend_B(c));
+    p.pdt = static_cast<char *>(cache_pend_dt(c));
     p.pos = cache_pos(c);
     p.pending = cache_pending(c);
     p.err = cache_err(c);
-    // H*P and G*N are multiples of 16 (P, N >= 16), so these rows are whole words
-    p.x_row_words = c.dims.nheads * c.dims.headdim * e / 4;
-    p.B_row_words = c.dims.ngroups * c.dims.dstate * e / 4;
-    p.dt_elems = c.dims.nheads;
+    p.x_row = c.dims.nheads * c.dims.headdim * e;   // multiples of 32 bytes (P, N >= 16)
+    p.B_row = c.dims.ngroups * c.dims.dstate * e;
+    p.dt_row = c.dims.nheads * e;                    // even number of bytes
     p.K = K;
     p.k_max = c.k_max;
-    p.dt_elt = e;
+    // pending rows are 256-B aligned; 16-byte copies when the draft rows are too
+    const bool v16 = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
     trace_begin(c, MIL_TRACE_COMMIT, s);
-    hipLaunchKernelGGL(ssm_commit_kernel, dim3(c.dims.batch), dim3(256), 0, s, p);
+    if (v16)
+        hipLaunchKernelGGL(ssm_commit_kernel<uint4>, dim3(K, c.dims.batch), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(ssm_commit_kernel<uint32_t>, dim3(K, c.dims.batch), dim3(256), 0, s, p);
     trace_end(c, MIL_TRACE_COMMIT, s);
     return hipGetLastError();
 }

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void chunk_state_mfma(const MParams p) {
         __syncthreads();
         // X^T block: thread item = (s quad, 8-column group); 4 rows of 8 bf16 -> 8 rows of 4
         for (int it = tid; it < (kSB / 4) * (PS / 8); it += 256) {
-            const int sq = it / (PS / 8), pg = it % (PS / 8);
+            const int pg = it / (kSB / 4), sq = it % (kSB / 4);  // token quads fastest
             uint4 v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void chunk_state_mfma(const MParams p) {
         }
         // (w B)^T block, split hi/lo
         for (int it = tid; it < (kSB / 4) * (N / 8); it += 256) {
-            const int sq = it / (N / 8), ng = it % (N / 8);
+            const int ng = it / (kSB / 4), sq = it % (kSB / 4);
             float wv[4];
             uint4 v[4];
 #pragma unroll
@@ -285,6 +285,26 @@ __global__ __launch_bounds__(256) void state_pass_pn(const MParams p) {
     }
 }
 
+// Y += M X for one 32-column tile J: the A operands (hi, lo) hold M[t][s] with k-slot
+// (hf, v) <-> s = 32J + 16ks + 8(v/4) + 4hf + v%4, so the B operand reads X^T row p at
+// the same s: two groups of four consecutive tokens.  xr points at X^T[l32][32J + 4hf].
+template <int PT>
+__device__ __forceinline__ void accumulate_mx(f32x16 *acc, const bf16x8 *ah, const bf16x8 *al, const bf16 *xr,
+                                              int XS) {
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+        const bf16 *row = xr + pt * kT * XS;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(row + ks * 16);
+            const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(row + ks * 16 + 8);
+            const bf16x8 xv = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            acc[pt] = mfma(ah[ks], xv, acc[pt]);
+            acc[pt] = mfma(al[ks], xv, acc[pt]);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------- phase 3
 // One workgroup per (seq, chunk, head); Q/64 waves, each owning the 32-row tiles
 // I = wave and nt-1-wave (equal work: the causal part of tile I has I+1 column tiles).
@@ -299,7 +319,7 @@ __global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
     const int c0 = c * Q, len = min(Q, p.L - c0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
     const int NT = blockDim.x;
-    const int BS = N + 8, XS = Q + 4;  // padded LDS rows (elements)
+    const int BS = N + 8, XS = Q + 8;  // padded LDS rows (elements)
 
     bf16 *sB = reinterpret_cast<bf16 *>(lds);      // [Q][BS]   B rows of the chunk
     bf16 *sXT = sB + Q * BS;                        // [P][XS]   X^T of the chunk
@@ -324,7 +344,8 @@ __global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
     }
     // X^T (zero past the chunk end: those columns meet zero weights, but 0 * NaN is not 0)
     for (int it = tid; it < (Q / 4) * (P / 8); it += NT) {
-        const int sq = it / (P / 8), pg = it % (P / 8);
+        // token quads fastest: neighbouring threads write neighbouring 8 bytes of a row
+        const int pg = it / (Q / 4), sq = it % (Q / 4);
         uint4 v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -403,63 +424,80 @@ __global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
                 for (int r = 0; r < 16; ++r) acc[pt][r] *= ein[r];
             }
         }
-        const float et = t < len ? __expf(sR[t]) : 0.f;
-        for (int J = 0; J <= I; ++J) {
-            // Z[s][t] = B_s . C_t for s in tile J (registers: s = 32J + 8(r/4) + 4hf + r%4)
+        // rows t >= len are computed but never stored (MFMA rows do not mix)
+        const float et = __expf(sR[min(t, Q - 1)]);
+        // off-diagonal tiles J < I: every s < t, so no mask; decay = colf(s) * mid(I,J) * e^{R_t}
+        for (int J = 0; J < I; ++J) {
             f32x16 z = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
                 const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
                 z = mfma(bfr, cf[kk], z);
             }
-            // M[t][s]: causal mask, decay, dt_s; D on the diagonal; split hi/lo
-            const float rowf = (I == J) ? 0.f : sMid[I * 8 + J] * et;
+            const float rowf = sMid[I * 8 + J] * et;
             bf16x8 ah[2], al[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int s = J * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                float m = 0.f;
-                if (s <= t && t < len) {
-                    if (I == J) {
-                        m = z[r] * sDt[s] * __expf(sR[t] - sR[s]);
-                        if (s == t) m += Dh;
-                    } else {
-                        m = z[r] * sColf[s] * rowf;
-                    }
-                }
-                bf16 a, b;
-                split(m, a, b);
-                ah[r / 8][r % 8] = a;
-                al[r / 8][r % 8] = b;
-            }
-            // Y_I += M X_J: B operand slot (hf, v) is X[s][p] for the same s as M's slot
+            for (int q = 0; q < 4; ++q) {
+                // registers 4q..4q+3 hold s = 32J + 8q + 4hf + (0..3)
+                const float4 cf4 = *reinterpret_cast<const float4 *>(sColf + J * kT + 8 * q + 4 * hf);
+                const float cv[4] = {cf4.x, cf4.y, cf4.z, cf4.w};
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const bf16 *xr = sXT + (pt * kT + l32) * XS + J * kT + 4 * hf;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(xr + ks * 16);
-                    const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(xr + ks * 16 + 8);
-                    const bf16x8 xv = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                    acc[pt] = mfma(ah[ks], xv, acc[pt]);
-                    acc[pt] = mfma(al[ks], xv, acc[pt]);
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * q + u;
+                    bf16 a, b;
+                    split(z[r] * cv[u] * rowf, a, b);
+                    ah[r / 8][r % 8] = a;
+                    al[r / 8][r % 8] = b;
                 }
             }
+            accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
+        }
+        // diagonal tile J = I: causal mask, decay exp(R_t - R_s), dt_s, and D on s = t
+        {
+            const int J = I;
+            f32x16 z = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
+                z = mfma(bfr, cf[kk], z);
+            }
+            const float Rt = sR[min(t, Q - 1)];
+            bf16x8 ah[2], al[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 r4 = *reinterpret_cast<const float4 *>(sR + J * kT + 8 * q + 4 * hf);
+                const float4 d4 = *reinterpret_cast<const float4 *>(sDt + J * kT + 8 * q + 4 * hf);
+                const float rv[4] = {r4.x, r4.y, r4.z, r4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * q + u;
+                    const int sl = 8 * q + 4 * hf + u;  // s - 32J
+                    float m = z[r] * dv[u] * __expf(Rt - rv[u]);
+                    m = sl < l32 ? m : (sl == l32 ? m + Dh : 0.f);
+                    bf16 a, b;
+                    split(m, a, b);
+                    ah[r / 8][r % 8] = a;
+                    al[r / 8][r % 8] = b;
+                }
+            }
+            accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
         // y rows of this tile (lane: column p, rows t = 32I + 8(r/4) + 4hf + r%4)
+        float *yb = p.y + ((tok0 + I * kT) * H + h) * P + l32;
+        const int ystride = H * P;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
+        for (int r = 0; r < 16; ++r) {
+            const int tl = 8 * (r / 4) + 4 * hf + (r % 4);
+            if (I * kT + tl < len) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tr = I * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                if (tr < len) p.y[((tok0 + tr) * H + h) * P + pt * kT + l32] = acc[pt][r];
+                for (int pt = 0; pt < PT; ++pt) yb[tl * ystride + pt * kT] = acc[pt][r];
             }
         }
     }
 }
 
 size_t out_lds_bytes(int Q, int N, int P) {
-    return (size_t)Q * (N + 8) * 2 + (size_t)P * (Q + 4) * 2 + 6 * Q * 4 + 8 * 4 + 64 * 4;
+    return (size_t)Q * (N + 8) * 2 + (size_t)P * (Q + 8) * 2 + 6 * Q * 4 + 8 * 4 + 64 * 4;
 }
 size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 + (4 * 256 + 8) * 4; }
 

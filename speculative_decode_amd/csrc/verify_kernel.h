@@ -178,17 +178,27 @@ __global__ __launch_bounds__(512) void ssm_verify_kernel(const VerifyParams p) {
         for (int i = 0; i <= tid; ++i) a *= sDA[i];
         sAlpha[tid] = a;
     }
-    for (int i = tid; i < K * K; i += NT) {
-        const int k = i / K, s = i - k * K;
-        float w = 0.f;
-        if (s <= k) {
-            float dot = 0.f;
-            for (int n = 0; n < N; ++n) dot = __builtin_fmaf(sDC[k * N + n], sDB[s * N + n], dot);
-            float beta = 1.f;
-            for (int j = s + 1; j <= k; ++j) beta *= sDA[j];
-            w = beta * sDdt[s] * dot;
+    // eight lanes per (k, s) pair, each over every eighth n, then a fixed butterfly
+    for (int base = 0; base < K * K * 8; base += NT) {
+        const int i = base + tid;
+        const int pair = i >> 3, part = i & 7;
+        const int k = pair / max(K, 1), s = pair - k * K;
+        const bool live = pair < K * K && s <= k;
+        float dot = 0.f;
+        if (live)
+            for (int n = part; n < N; n += 8) dot = __builtin_fmaf(sDC[k * N + n], sDB[s * N + n], dot);
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
+        dot += __shfl_xor(dot, 4);
+        if (part == 0 && pair < K * K) {
+            float w = 0.f;
+            if (live) {
+                float beta = 1.f;
+                for (int j = s + 1; j <= k; ++j) beta *= sDA[j];
+                w = beta * sDdt[s] * dot;
+            }
+            sW[k * KT + s] = w;
         }
-        sW[k * KT + s] = w;
     }
 
     // ---- fold the pending rows, write back once, accumulate C_k . h0 ----
