@@ -312,6 +312,66 @@ def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
                        f"fp64 oracle, {t_pre + t_vc:.1f} s")
 
 
+# --------------------------------------------------------------------------- rocprofv3 summaries
+
+KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
+    "prefill_state": "chunk_state_", "prefill_pass": "state_pass", "prefill_out": "chunk_out_",
+    "verify": "ssm_verify_kernel", "commit": "ssm_commit_kernel", "copy": "elementwise",
+}
+
+
+def _family(name):
+    for k, pat in KERNEL_PATTERNS.items():
+        if pat in name:
+            return k
+    return None
+
+
+def summarize(dbs):
+    """Per-kernel durations from rocprofv3 --kernel-trace databases, as a text table."""
+    import sqlite3
+    rows = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for name, dur in con.execute("select name, duration from kernels"):
+            rows.setdefault(name, []).append(dur)
+    tot = sum(sum(v) for v in rows.values())
+    lines = [f"{'calls':>6} {'mean_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for name, v in sorted(rows.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{len(v):6d} {np.mean(v) / 1e3:10.3f} {np.min(v) / 1e3:10.3f} {np.max(v) / 1e3:10.3f} "
+                     f"{100 * sum(v) / tot:6.2f}  {name[:110]}")
+    return "\n".join(lines)
+
+
+def traffic(fetch_db, write_db, workload, copy_mib):
+    """HBM bytes per launch of each kernel family from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain elementwise copy of
+    copy_mib MiB (which reads and writes exactly that many bytes) in the same process."""
+    import sqlite3
+
+    def per_family(db, counter):
+        con = sqlite3.connect(db)
+        acc = {}
+        for name, v in con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                                   (counter,)):
+            f = _family(name)
+            if f:
+                acc.setdefault(f, []).append(v * 1024.0)
+        return {k: float(np.mean(v)) for k, v in acc.items()}
+
+    fe = per_family(fetch_db, "FETCH_SIZE")
+    wr = per_family(write_db, "WRITE_SIZE")
+    known = copy_mib * 1024 * 1024
+    kf, kw = known / fe["copy"], known / wr["copy"]
+    out = {"_calibration": {"copy_bytes": known, "fetch_counter_bytes": fe["copy"],
+                            "write_counter_bytes": wr["copy"], "fetch_scale": kf, "write_scale": kw}}
+    for k in fe:
+        if k != "copy" and k in wr:
+            out[f"{k}/{workload}"] = {"fetch_bytes": fe[k] * kf, "write_bytes": wr[k] * kw,
+                                      "bytes_per_launch": fe[k] * kf + wr[k] * kw, "source_sha": source_hash()}
+    return out
+
+
 # --------------------------------------------------------------------------- main
 
 def main():
@@ -324,7 +384,25 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, time a plain elementwise copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", nargs="+", metavar="DB",
+                    help="print a per-kernel summary of rocprofv3 --kernel-trace databases and exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="turn FETCH_SIZE / WRITE_SIZE --pmc databases (run with --copy-mib) into "
+                         "profiles/traffic.json entries for --workload, then exit")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize(args.summarize))
+        return
+    if args.traffic:
+        if not args.copy_mib:
+            ap.error("--traffic needs the --copy-mib value the counter runs used")
+        t = traffic(args.traffic[0], args.traffic[1], args.workload, args.copy_mib)
+        old = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+        old.update(t)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(old, fh, indent=1, sort_keys=True)
+        print(json.dumps(t, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the SSM path has no cross-GPU step in this build)", file=sys.stderr)
