@@ -63,8 +63,8 @@ int mil_ssm_supported(const mil_ssm_dims *dims, int32_t dtype) {
     if (st != MIL_OK) return st;
     st = check_dtype(dtype);
     if (st != MIL_OK) return st;
-    for (int kt : {4, 8, 16})
-        if (!verify_supported(dims->headdim, dims->dstate, kt)) return MIL_E_UNSUPPORTED;
+    if (!verify_supported(dims->batch, dims->nheads, dims->headdim, dims->dstate, 1, 1))
+        return MIL_E_UNSUPPORTED;
     return MIL_OK;
 }
 
@@ -110,6 +110,8 @@ int describe(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t
     int st = mil_ssm_cache_layout(d, k_max, dtype, &L);
     if (st != MIL_OK) return st;
     if ((st = mil_ssm_supported(d, dtype)) != MIL_OK) return st;
+    // every K up to k_max needs a verify shape (its LDS grows with K and k_max)
+    if (!verify_supported(d->batch, d->nheads, d->headdim, d->dstate, k_max, k_max)) return MIL_E_UNSUPPORTED;
     if (!aligned(dev_buf, kAlign)) return MIL_E_ALIGN;
     if ((int64_t)bytes < L.bytes) return MIL_E_INVALID;
     memset(cache->opaque, 0, sizeof(cache->opaque));

@@ -55,7 +55,8 @@ hipError_t launch_fill_zero(void *p, int64_t words, hipStream_t s);
 // K drafts from that state.  K == 0 is the fold alone (x/B/C/dt/y unused).
 hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B, const void *C,
                          const void *dt, const float *A, const float *D, float *y, hipStream_t s);
-bool verify_supported(int P, int N, int kt);
+// A verify launch shape exists for these sizes (K drafts, up to kmax pending rows).
+bool verify_supported(int batch, int H, int P, int N, int K, int kmax);
 
 // Check accepted[b] in 0..K, copy the accepted draft rows into the pending area,
 // set pending[b] = accepted[b], pos[b] += accepted[b]; a bad value sets err[b] and pending[b] = 0.

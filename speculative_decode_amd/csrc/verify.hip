@@ -3,10 +3,8 @@
 
 namespace mil {
 
-bool verify_supported(int P, int N, int kt) {
-    (void)kt;
-    return (P == 16 || P == 32 || P == 64 || P == 128 || P == 256) &&
-           (N == 16 || N == 32 || N == 64 || N == 128 || N == 256) && shape_known(P, N);
+bool verify_supported(int batch, int H, int P, int N, int K, int kmax) {
+    return shape_for(batch, H, P, N, K, kmax).S > 0;
 }
 
 hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B, const void *C,
@@ -31,12 +29,11 @@ hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B
     vp.G = c.dims.ngroups;
     vp.K = K;
     vp.k_max = c.k_max;
-    const int kt = c.k_max <= 4 ? 4 : (c.k_max <= 8 ? 8 : 16);  // bounds both K and pending
     const int batch = c.dims.batch;
     const int id = K > 0 ? MIL_TRACE_VERIFY : MIL_TRACE_FOLD;
     trace_begin(c, id, s);
-    const hipError_t e = c.dtype == MIL_BF16 ? dispatch_verify_bf16(vp, kt, batch, s)
-                                             : dispatch_verify_f32(vp, kt, batch, s);
+    const hipError_t e = c.dtype == MIL_BF16 ? dispatch_verify_bf16(vp, batch, s)
+                                             : dispatch_verify_f32(vp, batch, s);
     trace_end(c, id, s);
     return e;
 }

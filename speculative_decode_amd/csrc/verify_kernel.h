@@ -17,11 +17,12 @@
 //   alpha_k = prod_{i<=k} abar_i,  beta_{k,s} = prod_{s<i<=k} abar_i,  abar_i = exp(dt_i A).
 // No draft token ever touches the stored state; a later commit decides which ones count.
 //
-// Work decomposition (gfx950, wave64): a workgroup owns PT state columns of one
-// (slot, head); each wave splits into 64/PT row groups of PT lanes, S waves per group,
-// so each lane owns ROWS consecutive rows of one column.  State traffic is one coalesced
-// fp32 read (and at most one write) per element; the per-row work is in registers and
-// the cross-row-group sum goes through LDS once at the end, in a fixed order.
+// Work decomposition (gfx950, wave64): one workgroup per (slot, head), S waves.  A lane
+// owns 4 adjacent columns (16-byte loads) of ROWS consecutive state rows; P/4 lanes
+// cover a row, so a wave reads 64 * 16 bytes of whole rows per load instruction.  State
+// traffic is one read and at most one write per element; per-row work is in registers,
+// partial C_k . h sums are combined across the row groups of a wave with shuffles and
+// across waves through LDS, always in the same order.
 #pragma once
 
 #include "ssm_internal.h"
@@ -52,75 +53,68 @@ struct VerifyParams {
     const float *A, *D;
     float *y;
     int H, P, N, G, K, k_max;
-    int pt_log2;
 };
 
-
-// Launch shape for (P, N): PT columns per workgroup, S waves, ROWS rows per lane.
+// Launch shape: S waves per workgroup, ROWS rows per lane.  More waves when there are
+// few (slot, head) pairs, at most 16 rows per lane where N allows, at least one.
 struct Shape {
-    int PT, S, ROWS;
+    int S, ROWS;
 };
 
-inline Shape shape_for(int P, int N) {
-    const int PT = P < 64 ? P : 64;
-    const int RGW = 64 / PT;
-    int rows = N / RGW;  // with one wave
-    int S = 1;
-    while (rows > 32 && S < 8) {  // at most 32 rows per lane
-        S *= 2;
-        rows /= 2;
+// Threads a workgroup may have for a given ROWS (more rows need more registers per lane).
+constexpr int max_threads(int rows) { return rows >= 16 ? 512 : 1024; }
+
+inline size_t verify_lds_floats(int N, int P, int K, int kmax, int S) {
+    return (size_t)kmax * N + 2 * K * N + (size_t)kmax * P + K * P + kmax + 4 * K + K * K + (size_t)S * K * P;
+}
+constexpr size_t kVerifyLdsMax = 160 * 1024;
+
+// Launch shape for K drafts with up to kmax pending rows; S = 0 when none fits.
+inline Shape shape_for(int batch, int H, int P, int N, int K, int kmax) {
+    Shape best{0, 0};
+    if (P < 16 || P > 256 || (P & (P - 1)) || N < 16 || N > 256 || (N & (N - 1))) return best;
+    const int RGW = 256 / P;  // row groups per wave (P/4 lanes per row)
+    for (int S = 1; S <= 16; S *= 2) {
+        const int rg = S * RGW;
+        if (rg > N) break;
+        const int rows = N / rg;
+        if (rows > 32 || S * 64 > max_threads(rows)) continue;
+        if (verify_lds_floats(N, P, K, kmax, S) * sizeof(float) > kVerifyLdsMax) continue;
+        best = {S, rows};
+        if ((int64_t)batch * H * S >= 2048 && rows <= 16) break;
     }
-    return {PT, S, rows};
+    return best;
 }
 
-inline int log2i(int v) {
-    int l = 0;
-    while ((1 << l) < v) ++l;
-    return l;
-}
-
-inline bool shape_known(int P, int N) {
-    const Shape sh = shape_for(P, N);
-    const int RG = sh.S * (64 / sh.PT);
-    return RG * sh.ROWS == N && P % sh.PT == 0 &&
-           (sh.ROWS == 4 || sh.ROWS == 8 || sh.ROWS == 16 || sh.ROWS == 32);
-}
-
-
-hipError_t dispatch_verify_bf16(const VerifyParams &vp, int kt, int batch, hipStream_t s);
-hipError_t dispatch_verify_f32(const VerifyParams &vp, int kt, int batch, hipStream_t s);
+hipError_t dispatch_verify_bf16(const VerifyParams &vp, int batch, hipStream_t s);
+hipError_t dispatch_verify_f32(const VerifyParams &vp, int batch, hipStream_t s);
 
 namespace {
 
-template <typename T, int ROWS, int KT>
-__global__ __launch_bounds__(512) void ssm_verify_kernel(const VerifyParams p) {
-    // runtime shape: PT = 1 << p.pt_log2 columns per workgroup, S = blockDim.x / 64 waves
-    extern __shared__ float lds[];
-    const int PT = 1 << p.pt_log2;
-    const int RGW = 64 >> p.pt_log2;     // row groups per wave
-    const int NT = blockDim.x;
-    const int RG = (NT >> 6) * RGW;      // row groups per workgroup
-    const int N = p.N;                   // == RG * ROWS (checked by the launcher)
-    float *sRB = lds;                    // [KT][N]  pending rows' B
-    float *sDB = sRB + KT * N;           // [KT][N]  drafts' B
-    float *sDC = sDB + KT * N;           // [KT][N]  drafts' C
-    float *sRA = sDC + KT * N;           // [KT]     pending rows' abar
-    float *sDA = sRA + KT;               // [KT]     drafts' abar
-    float *sDdt = sDA + KT;              // [KT]     drafts' dt
-    float *sAlpha = sDdt + KT;           // [KT]     alpha_k
-    float *sW = sAlpha + KT;             // [KT][KT] beta_{k,s} dt_s (C_k . B_s)
-    float *sXd = sW + KT * KT;           // [KT][PT] drafts' x on this column tile
-    float *sRed = sXd + KT * PT;         // [RG][KT][PT] partial C_k . h0 per row group
+template <typename T, int ROWS>
+__global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const VerifyParams p) {
+    extern __shared__ __align__(16) float lds[];
+    const int N = p.N, P = p.P, H = p.H, G = p.G, K = p.K, kmax = p.k_max;
+    const int LPR = P >> 2;        // lanes per state row
+    const int RGW = 64 / LPR;      // row groups per wave
+    const int NT = blockDim.x, S = NT >> 6;
+    float *sRB = lds;              // [kmax][N]  pending rows' B
+    float *sDB = sRB + kmax * N;   // [K][N]     drafts' B
+    float *sDC = sDB + K * N;      // [K][N]     drafts' C
+    float *sRU = sDC + K * N;      // [kmax][P]  pending rows' dt * x
+    float *sXd = sRU + kmax * P;   // [K][P]     drafts' x
+    float *sRA = sXd + K * P;      // [kmax]     pending rows' abar
+    float *sDA = sRA + kmax;       // [K]        drafts' abar
+    float *sDdt = sDA + K;         // [K]        drafts' dt
+    float *sAlpha = sDdt + K;      // [K]        alpha_k
+    float *sW = sAlpha + K;        // [K][K]     beta_{k,s} dt_s (C_k . B_s)
+    float *sRed = sW + K * K;      // [S][K][P]  per-wave partial C_k . h0
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int col = lane & (PT - 1);
-    const int rg = wave * RGW + (lane >> p.pt_log2);
-    const int b = blockIdx.z, h = blockIdx.y;
-    const int H = p.H, P = p.P, G = p.G, K = p.K, kmax = p.k_max;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c4 = lane % LPR, rsub = lane / LPR;
+    const int n0 = (wave * RGW + rsub) * ROWS;
+    const int h = blockIdx.x, b = blockIdx.y;
     const int g = h / (H / G);
-    const int c0 = blockIdx.x * PT;
-    const int pcol = c0 + col;
     const int m = p.pending[b];
     const float Ah = p.A[h];
 
@@ -132,7 +126,7 @@ __global__ __launch_bounds__(512) void ssm_verify_kernel(const VerifyParams p) {
     const T *dC = static_cast<const T *>(p.C);
     const T *dDt = static_cast<const T *>(p.dt);
 
-    // ---- small token loads first, so that waiting for them does not wait for the state ----
+    // ---- token rows first (small), so that waiting for them does not wait for the state ----
     for (int i = tid; i < m * N; i += NT) {
         const int s = i / N, n = i - s * N;
         sRB[i] = ld(pB, ((size_t)(b * kmax + s) * G + g) * N + n);
@@ -143,18 +137,14 @@ __global__ __launch_bounds__(512) void ssm_verify_kernel(const VerifyParams p) {
         sDB[i] = ld(dB, off);
         sDC[i] = ld(dC, off);
     }
-    for (int i = tid; i < K * PT; i += NT) {
-        const int k = i >> p.pt_log2, c = i & (PT - 1);
-        sXd[i] = ld(dX, ((size_t)(b * K + k) * H + h) * P + c0 + c);
+    for (int i = tid; i < m * P; i += NT) {
+        const int s = i / P, c = i - s * P;
+        const size_t row = (size_t)(b * kmax + s) * H + h;
+        sRU[i] = ld(pDt, row) * ld(pX, row * P + c);
     }
-    float u[KT];  // dt_s * x_s[pcol] of the pending rows
-#pragma unroll
-    for (int s = 0; s < KT; ++s) {
-        u[s] = 0.f;
-        if (s < m) {
-            const size_t row = (size_t)(b * kmax + s);
-            u[s] = ld(pDt, row * H + h) * ld(pX, (row * H + h) * P + pcol);
-        }
+    for (int i = tid; i < K * P; i += NT) {
+        const int k = i / P, c = i - k * P;
+        sXd[i] = ld(dX, ((size_t)(b * K + k) * H + h) * P + c);
     }
     if (tid < m) sRA[tid] = expf(ld(pDt, (size_t)(b * kmax + tid) * H + h) * Ah);
     if (tid < K) {
@@ -163,22 +153,20 @@ __global__ __launch_bounds__(512) void ssm_verify_kernel(const VerifyParams p) {
         sDA[tid] = expf(d * Ah);
     }
 
-    // ---- the state rows: one coalesced read per element ----
-    float *st = p.state + (size_t)(b * H + h) * p.head_stride + pcol;
-    const int n0 = rg * ROWS;
-    float hr[ROWS];
+    // ---- the state rows: 16-byte loads, one read per element ----
+    float *st = p.state + (size_t)(b * H + h) * p.head_stride + 4 * c4;
+    float4 hv[ROWS];
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) hr[i] = st[(size_t)(n0 + i) * P];
+    for (int i = 0; i < ROWS; ++i) hv[i] = *reinterpret_cast<const float4 *>(st + (size_t)(n0 + i) * P);
 
     __syncthreads();
 
-    // ---- per-draft scalars: alpha_k and w_{k,s} = beta_{k,s} dt_s (C_k . B_s) ----
+    // ---- per-draft scalars: alpha_k and w_{k,s}, eight lanes per (k, s) pair ----
     if (tid < K) {
         float a = 1.f;
         for (int i = 0; i <= tid; ++i) a *= sDA[i];
         sAlpha[tid] = a;
     }
-    // eight lanes per (k, s) pair, each over every eighth n, then a fixed butterfly
     for (int base = 0; base < K * K * 8; base += NT) {
         const int i = base + tid;
         const int pair = i >> 3, part = i & 7;
@@ -197,72 +185,106 @@ __global__ __launch_bounds__(512) void ssm_verify_kernel(const VerifyParams p) {
                 for (int j = s + 1; j <= k; ++j) beta *= sDA[j];
                 w = beta * sDdt[s] * dot;
             }
-            sW[k * KT + s] = w;
+            sW[k * K + s] = w;
         }
     }
 
-    // ---- fold the pending rows, write back once, accumulate C_k . h0 ----
-    float acc[KT];
+    // ---- fold the m pending rows, token by token, then write the rows back once ----
+    for (int s = 0; s < m; ++s) {
+        const float a = sRA[s];
+        const float4 u = *reinterpret_cast<const float4 *>(sRU + s * P + 4 * c4);
+        const float *bs = sRB + s * N + n0;
 #pragma unroll
-    for (int k = 0; k < KT; ++k) acc[k] = 0.f;
+        for (int i = 0; i < ROWS; ++i) {
+            const float bn = bs[i];
+            hv[i].x = state_step(a, hv[i].x, bn, u.x);
+            hv[i].y = state_step(a, hv[i].y, bn, u.y);
+            hv[i].z = state_step(a, hv[i].z, bn, u.z);
+            hv[i].w = state_step(a, hv[i].w, bn, u.w);
+        }
+    }
+    if (m > 0) {
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-        const int n = n0 + i;
-        float hv = hr[i];
-#pragma unroll
-        for (int s = 0; s < KT; ++s)
-            if (s < m) hv = state_step(sRA[s], hv, sRB[s * N + n], u[s]);
-        if (m > 0) st[(size_t)n * P] = hv;
-#pragma unroll
-        for (int k = 0; k < KT; ++k)
-            if (k < K) acc[k] = __builtin_fmaf(sDC[k * N + n], hv, acc[k]);
+        for (int i = 0; i < ROWS; ++i) *reinterpret_cast<float4 *>(st + (size_t)(n0 + i) * P) = hv[i];
     }
     if (K == 0) return;  // fold only
+
+    // ---- C_k . h0 over this lane's rows, then over the wave's row groups ----
+    for (int k = 0; k < K; ++k) {
+        const float *ck = sDC + k * N + n0;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < KT; ++k)
-        if (k < K) sRed[(rg * KT + k) * PT + col] = acc[k];
+        for (int i = 0; i < ROWS; ++i) {
+            const float c = ck[i];
+            acc.x = __builtin_fmaf(c, hv[i].x, acc.x);
+            acc.y = __builtin_fmaf(c, hv[i].y, acc.y);
+            acc.z = __builtin_fmaf(c, hv[i].z, acc.z);
+            acc.w = __builtin_fmaf(c, hv[i].w, acc.w);
+        }
+        for (int d = LPR; d < 64; d <<= 1) {
+            acc.x += __shfl_xor(acc.x, d);
+            acc.y += __shfl_xor(acc.y, d);
+            acc.z += __shfl_xor(acc.z, d);
+            acc.w += __shfl_xor(acc.w, d);
+        }
+        if (rsub == 0) *reinterpret_cast<float4 *>(sRed + (wave * K + k) * P + 4 * c4) = acc;
+    }
     __syncthreads();
 
-    // ---- outputs: sum row groups in order, then the closed-form draft terms ----
+    // ---- outputs: waves summed in order, then the closed-form draft terms ----
     const float Dh = p.D[h];
-    for (int i = tid; i < K * PT; i += NT) {
-        const int k = i >> p.pt_log2, c = i & (PT - 1);
-        float ch = 0.f;
-        for (int r = 0; r < RG; ++r) ch += sRed[(r * KT + k) * PT + c];
-        float yv = sAlpha[k] * ch;
-        for (int s = 0; s <= k; ++s) yv = __builtin_fmaf(sW[k * KT + s], sXd[s * PT + c], yv);
-        yv = __builtin_fmaf(Dh, sXd[k * PT + c], yv);
-        p.y[((size_t)(b * K + k) * H + h) * P + c0 + c] = yv;
+    for (int i = tid; i < K * LPR; i += NT) {
+        const int k = i / LPR, q = i - k * LPR;
+        float4 ch = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int w = 0; w < S; ++w) {
+            const float4 v = *reinterpret_cast<const float4 *>(sRed + (w * K + k) * P + 4 * q);
+            ch.x += v.x;
+            ch.y += v.y;
+            ch.z += v.z;
+            ch.w += v.w;
+        }
+        const float al = sAlpha[k];
+        float4 yv = make_float4(al * ch.x, al * ch.y, al * ch.z, al * ch.w);
+        for (int s2 = 0; s2 <= k; ++s2) {
+            const float wv = sW[k * K + s2];
+            const float4 xs = *reinterpret_cast<const float4 *>(sXd + s2 * P + 4 * q);
+            yv.x = __builtin_fmaf(wv, xs.x, yv.x);
+            yv.y = __builtin_fmaf(wv, xs.y, yv.y);
+            yv.z = __builtin_fmaf(wv, xs.z, yv.z);
+            yv.w = __builtin_fmaf(wv, xs.w, yv.w);
+        }
+        const float4 xk = *reinterpret_cast<const float4 *>(sXd + k * P + 4 * q);
+        yv.x = __builtin_fmaf(Dh, xk.x, yv.x);
+        yv.y = __builtin_fmaf(Dh, xk.y, yv.y);
+        yv.z = __builtin_fmaf(Dh, xk.z, yv.z);
+        yv.w = __builtin_fmaf(Dh, xk.w, yv.w);
+        *reinterpret_cast<float4 *>(p.y + ((size_t)(b * K + k) * H + h) * P + 4 * q) = yv;
     }
 }
 
-size_t lds_bytes(int N, int KT, int PT, int S) {
-    return sizeof(float) * (size_t)(3 * KT * N + 4 * KT + KT * KT + KT * PT + S * 64 * KT);
-}
-
-template <typename T, int ROWS, int KT>
-hipError_t launch_one(VerifyParams vp, const Shape &sh, int batch, hipStream_t s) {
-    vp.pt_log2 = log2i(sh.PT);
-    const size_t lds = lds_bytes(vp.N, KT, sh.PT, sh.S);
-    auto kern = ssm_verify_kernel<T, ROWS, KT>;
+template <typename T, int ROWS>
+hipError_t launch_one(const VerifyParams &vp, const Shape &sh, int batch, hipStream_t s) {
+    const size_t lds = sizeof(float) * verify_lds_floats(vp.N, vp.P, vp.K, vp.k_max, sh.S);
+    auto kern = ssm_verify_kernel<T, ROWS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    dim3 grid(vp.P / sh.PT, vp.H, batch);
-    hipLaunchKernelGGL(kern, grid, dim3(sh.S * 64), lds, s, vp);
+    hipLaunchKernelGGL(kern, dim3(vp.H, batch), dim3(sh.S * 64), lds, s, vp);
     return hipGetLastError();
 }
 
-template <typename T, int KT>
+template <typename T>
 hipError_t dispatch_rows(const VerifyParams &vp, int batch, hipStream_t s) {
-    const Shape sh = shape_for(vp.P, vp.N);
+    const Shape sh = shape_for(batch, vp.H, vp.P, vp.N, vp.K, vp.k_max);
     switch (sh.ROWS) {
-        case 4: return launch_one<T, 4, KT>(vp, sh, batch, s);
-        case 8: return launch_one<T, 8, KT>(vp, sh, batch, s);
-        case 16: return launch_one<T, 16, KT>(vp, sh, batch, s);
-        case 32: return launch_one<T, 32, KT>(vp, sh, batch, s);
+        case 1: return launch_one<T, 1>(vp, sh, batch, s);
+        case 2: return launch_one<T, 2>(vp, sh, batch, s);
+        case 4: return launch_one<T, 4>(vp, sh, batch, s);
+        case 8: return launch_one<T, 8>(vp, sh, batch, s);
+        case 16: return launch_one<T, 16>(vp, sh, batch, s);
+        case 32: return launch_one<T, 32>(vp, sh, batch, s);
         default: return hipErrorInvalidValue;
     }
 }
