@@ -36,6 +36,23 @@ __device__ __forceinline__ float ld(const uint16_t *p, size_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at `base` (gfx9-family descriptor word 3); loads and
+// stores through it take one per-lane offset plus a scalar offset, and accesses past
+// `bytes` are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const f32x4v t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void buf_store4(float4 v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const f32x4v t = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, 0);
+}
+
 // The single state step that folds one accepted token into a stored state element:
 //   h <- abar * h + B[n] * (dt * x[p]).
 // Every path that writes a state through accepted tokens (verify's fold, commit's
@@ -81,7 +98,7 @@ inline Shape shape_for(int batch, int H, int P, int N, int K, int kmax) {
         if (rows > 32 || S * 64 > max_threads(rows)) continue;
         if (verify_lds_floats(N, P, K, kmax, S) * sizeof(float) > kVerifyLdsMax) continue;
         best = {S, rows};
-        if ((int64_t)batch * H * S >= 2048 && rows <= 16) break;
+        if ((int64_t)batch * H * S >= 2048 && rows <= 8) break;
     }
     return best;
 }
@@ -153,11 +170,12 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
         sDA[tid] = expf(d * Ah);
     }
 
-    // ---- the state rows: 16-byte loads, one read per element ----
-    float *st = p.state + (size_t)(b * H + h) * p.head_stride + 4 * c4;
+    // ---- the state rows: 16-byte buffer loads, one read per element ----
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.state + (size_t)(b * H + h) * p.head_stride, N * P * 4);
+    const int voff = (n0 * P + 4 * c4) * 4;  // this lane's first row and columns
     float4 hv[ROWS];
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) hv[i] = *reinterpret_cast<const float4 *>(st + (size_t)(n0 + i) * P);
+    for (int i = 0; i < ROWS; ++i) hv[i] = buf_load4(srs, voff, i * P * 4);
 
     __syncthreads();
 
@@ -205,7 +223,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     }
     if (m > 0) {
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) *reinterpret_cast<float4 *>(st + (size_t)(n0 + i) * P) = hv[i];
+        for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
     }
     if (K == 0) return;  // fold only
 
