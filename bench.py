@@ -381,6 +381,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_single")
     ap.add_argument("--rotate", type=int, default=0, help="independent cache/input sets (0: enough for >320 MB)")
+    ap.add_argument("--chunk", type=int, default=0, help="prefill chunk length (0: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, time a plain elementwise copy of this many MiB (counter calibration)")
@@ -409,6 +410,9 @@ def main():
         sys.exit(2)
     from speculative_decode_amd import synth
     w = synth.WORKLOADS[args.workload]
+    if args.chunk:
+        import dataclasses
+        w = dataclasses.replace(w, chunk=args.chunk)
     args.steps = max(1, args.steps)
     g = run_gpu(args, w)
     kind = g["kind"]

@@ -18,6 +18,8 @@
 // Phase 3 computes Z with B_J as A and C_I as B, so each lane's D registers hold one
 // output row t (= its column) and 16 source tokens s: exactly an A operand for M X
 // once the k-slot (hf, v) <-> s correspondence is applied to how X is read from LDS.
+#include <algorithm>
+
 #include "ssm_internal.h"
 
 namespace mil {
@@ -36,6 +38,19 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 __device__ __forceinline__ float bf2f(bf16 v) { return static_cast<float>(v); }
+// Column i (0..7) of four rows of 8 bf16 each, as 4 consecutive bf16 (one row of the
+// transpose): byte selects on register words, so nothing goes through memory.
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int k) {
+    return k == 0 ? v.x : (k == 1 ? v.y : (k == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ uint2 column4(const uint4 &v0, const uint4 &v1, const uint4 &v2, const uint4 &v3, int i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of each word
+    uint2 w;
+    w.x = __builtin_amdgcn_perm(word_of(v1, i >> 1), word_of(v0, i >> 1), sel);
+    w.y = __builtin_amdgcn_perm(word_of(v3, i >> 1), word_of(v2, i >> 1), sel);
+    return w;
+}
+
 // hi = nearest bf16 of v, lo = nearest bf16 of the remainder
 __device__ __forceinline__ void split(float v, bf16 &hi, bf16 &lo) {
     hi = static_cast<bf16>(v);
@@ -69,19 +84,30 @@ __device__ __forceinline__ int xcd_item(int n) {
 //   R[t]    = sum_{tile start..t} dtA          (inclusive, within t's tile)
 //   suf[s]  = sum_{s+1..tile end} dtA          (exclusive, within s's tile)
 //   tot[i]  = sum over tile i
+// One 32-lane half-wave per tile: a shuffle scan up for R, and a shuffle scan down over
+// the shifted values for suf (a sum of later terms, not a difference).  dtA must be zero
+// from len to the next multiple of 32.
 __device__ void chunk_factors(const float *dtA, int len, float *R, float *suf, float *tot, int tid, int nt) {
-    for (int t = tid; t < len; t += nt) {
-        const int ts = t / kT * kT, te = min(ts + kT, len) - 1;
-        float r = 0.f;
-        for (int q = ts; q <= t; ++q) r += dtA[q];
-        float l = 0.f;
-        for (int q = te; q > t; --q) l += dtA[q];
-        R[t] = r;
-        suf[t] = l;
-    }
-    __syncthreads();
     const int ntile = (len + kT - 1) / kT;
-    if (tid < ntile) tot[tid] = R[min(tid * kT + kT, len) - 1];
+    for (int base = 0; base < ntile * kT; base += nt) {
+        const int t = base + tid;
+        const int l32 = tid & 31;
+        const bool in = t < ntile * kT;
+        float r = in ? dtA[t] : 0.f;
+        float u = (in && l32 < 31) ? dtA[t + 1] : 0.f;
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) {
+            const float ru = __shfl_up(r, d, 32);
+            const float ud = __shfl_down(u, d, 32);
+            if (l32 >= d) r += ru;
+            if (l32 + d < 32) u += ud;
+        }
+        if (in) {
+            R[t] = r;
+            suf[t] = u;
+            if (l32 == 31) tot[t / kT] = r;
+        }
+    }
     __syncthreads();
 }
 
@@ -114,7 +140,7 @@ __global__ __launch_bounds__(256) void chunk_state_mfma(const MParams p) {
 
     const size_t tok0 = (size_t)seq * p.L + c0;
     const float Ah = p.A[h];
-    for (int s = tid; s < len; s += 256) sDtA[s] = bf2f(p.dt[(tok0 + s) * H + h]) * Ah;
+    for (int s = tid; s < 256; s += 256) sDtA[s] = s < len ? bf2f(p.dt[(tok0 + s) * H + h]) * Ah : 0.f;
     __syncthreads();
     chunk_factors(sDtA, len, sR, sSuf, sTot, tid, 256);
     const int ntile = (len + kT - 1) / kT;
@@ -136,58 +162,73 @@ __global__ __launch_bounds__(256) void chunk_state_mfma(const MParams p) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
 
-    for (int sb = 0; sb < len; sb += kSB) {
-        __syncthreads();
-        // X^T block: thread item = (s quad, 8-column group); 4 rows of 8 bf16 -> 8 rows of 4
-        for (int it = tid; it < (kSB / 4) * (PS / 8); it += 256) {
-            const int pg = it / (kSB / 4), sq = it % (kSB / 4);  // token quads fastest
-            uint4 v[4];
+    // token blocks of 64 go through LDS; the global loads of block b+1 are issued before
+    // the matrix products of block b.  Items (4 tokens x 8 columns) per block: 2*PS of X and
+    // 2*N of B, at most 512 each, so two per thread.
+    const int xitems = (kSB / 4) * (PS / 8), witems = (kSB / 4) * (N / 8);
+    uint4 vx[2][4], vw[2][4];
+    float wv[2][4];
+    auto fetch = [&](int sb) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int it = tid + j * 256;
+            const int pg = it / (kSB / 4), sq = it % (kSB / 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = sb + sq * 4 + r;
-                v[r] = s < len ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + s) * H + h) * P + p0 + pg * 8)
+                vx[j][r] = (it < xitems && s < len)
+                               ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + s) * H + h) * P + p0 + pg * 8)
                                : make_uint4(0, 0, 0, 0);
             }
-            const uint16_t *e0 = reinterpret_cast<const uint16_t *>(&v[0]);
-            const uint16_t *e1 = reinterpret_cast<const uint16_t *>(&v[1]);
-            const uint16_t *e2 = reinterpret_cast<const uint16_t *>(&v[2]);
-            const uint16_t *e3 = reinterpret_cast<const uint16_t *>(&v[3]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint2 w;
-                w.x = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
-                w.y = (uint32_t)e2[i] | ((uint32_t)e3[i] << 16);
-                *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * kSBS + sq * 4) = w;
-            }
         }
-        // (w B)^T block, split hi/lo
-        for (int it = tid; it < (kSB / 4) * (N / 8); it += 256) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int it = tid + j * 256;
             const int ng = it / (kSB / 4), sq = it % (kSB / 4);
-            float wv[4];
-            uint4 v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = sb + sq * 4 + r;
-                const bool ok = s < len;
-                wv[r] = ok ? sW[s] : 0.f;
-                v[r] = ok ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + s) * G + g) * N + ng * 8)
-                          : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                bf16x4 hi, lo;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float b = bf2f(reinterpret_cast<const uint16_t *>(&v[r])[i]);
-                    bf16 a, z;
-                    split(wv[r] * b, a, z);
-                    hi[r] = a;
-                    lo[r] = z;
-                }
-                *reinterpret_cast<bf16x4 *>(sWh + (ng * 8 + i) * kSBS + sq * 4) = hi;
-                *reinterpret_cast<bf16x4 *>(sWl + (ng * 8 + i) * kSBS + sq * 4) = lo;
+                const bool ok = it < witems && s < len;
+                wv[j][r] = ok ? sW[s] : 0.f;
+                vw[j][r] = ok ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + s) * G + g) * N + ng * 8)
+                              : make_uint4(0, 0, 0, 0);
             }
         }
+    };
+    __syncthreads();  // sW visible
+    fetch(0);
+    for (int sb = 0; sb < len; sb += kSB) {
+        __syncthreads();  // the previous block's products are done with LDS
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int it = tid + j * 256;
+            if (it < xitems) {
+                const int pg = it / (kSB / 4), sq = it % (kSB / 4);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * kSBS + sq * 4) =
+                        column4(vx[j][0], vx[j][1], vx[j][2], vx[j][3], i);
+            }
+            if (it < witems) {
+                const int ng = it / (kSB / 4), sq = it % (kSB / 4);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    bf16x4 hi, lo;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t wd = word_of(vw[j][r], i >> 1);
+                        const float bb = __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
+                        bf16 x1, x2;
+                        split(wv[j][r] * bb, x1, x2);
+                        hi[r] = x1;
+                        lo[r] = x2;
+                    }
+                    *reinterpret_cast<bf16x4 *>(sWh + (ng * 8 + i) * kSBS + sq * 4) = hi;
+                    *reinterpret_cast<bf16x4 *>(sWl + (ng * 8 + i) * kSBS + sq * 4) = lo;
+                }
+            }
+        }
+        if (sb + kSB < len) fetch(sb + kSB);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -256,25 +297,41 @@ __global__ __launch_bounds__(256) void state_pass_pn(const MParams p) {
         for (int i = 0; i < 8; ++i) hv[i] = 0.f;
     }
     const size_t NP = (size_t)P * N;
-    for (int c = 0; c < p.nch; ++c) {
-        const size_t ch = ((size_t)seq * p.nch + c) * p.H + h;
-        float *slot = p.ws + ch * NP + (size_t)pcol * N + n0;
-        const float4 s0 = *reinterpret_cast<const float4 *>(slot);
-        const float4 s1 = *reinterpret_cast<const float4 *>(slot + 4);
-        const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        bf16x8 hi, lo;
+    constexpr int U = 4;  // chunks whose states are loaded before any is rewritten
+    for (int cb = 0; cb < p.nch; cb += U) {
+        float4 s0[U], s1[U];
+        float tt[U];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            bf16 a, b;
-            split(hv[i], a, b);
-            hi[i] = a;
-            lo[i] = b;
+        for (int u = 0; u < U; ++u) {
+            if (cb + u < p.nch) {
+                const size_t ch = ((size_t)seq * p.nch + cb + u) * p.H + h;
+                const float *slot = p.ws + ch * NP + (size_t)pcol * N + n0;
+                s0[u] = *reinterpret_cast<const float4 *>(slot);
+                s1[u] = *reinterpret_cast<const float4 *>(slot + 4);
+                tt[u] = p.ws_tot[ch];
+            }
         }
-        *reinterpret_cast<bf16x8 *>(slot) = hi;
-        *reinterpret_cast<bf16x8 *>(slot + 4) = lo;
-        const float e = __expf(p.ws_tot[ch]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) hv[i] = __builtin_fmaf(e, hv[i], sc[i]);
+        for (int u = 0; u < U; ++u) {
+            if (cb + u < p.nch) {
+                const size_t ch = ((size_t)seq * p.nch + cb + u) * p.H + h;
+                float *slot = p.ws + ch * NP + (size_t)pcol * N + n0;
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    bf16 a, b;
+                    split(hv[i], a, b);
+                    hi[i] = a;
+                    lo[i] = b;
+                }
+                *reinterpret_cast<bf16x8 *>(slot) = hi;
+                *reinterpret_cast<bf16x8 *>(slot + 4) = lo;
+                const float e = __expf(tt[u]);
+                const float sc[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) hv[i] = __builtin_fmaf(e, hv[i], sc[i]);
+            }
+        }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) sT[ng * 8 + i][pl] = hv[i];
@@ -306,10 +363,12 @@ __device__ __forceinline__ void accumulate_mx(f32x16 *acc, const bf16x8 *ah, con
 }
 
 // ------------------------------------------------------------------------- phase 3
-// One workgroup per (seq, chunk, head); Q/64 waves, each owning the 32-row tiles
-// I = wave and nt-1-wave (equal work: the causal part of tile I has I+1 column tiles).
+// One workgroup per (seq, chunk, head); Q/32 waves, each owning one 32-row tile.  Waves
+// w and w + 4 share a SIMD, so tiles are dealt as I = w (w < nw/2) and I = nw-1-(w-nw/2):
+// a SIMD then holds tiles I and nw-1-I, whose causal parts (I+1 and nw-I column tiles)
+// add up to the same work on every SIMD, and its two waves hide each other's latency.
 template <int N, int P>
-__global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
+__global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
     extern __shared__ __align__(16) char lds[];
     const int H = p.H, G = p.G, Q = p.Q;
     const int nitems = p.nseq * p.nch * H;
@@ -320,50 +379,82 @@ __global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
     const int NT = blockDim.x;
     const int BS = N + 8, XS = Q + 8;  // padded LDS rows (elements)
+    constexpr int PT = P / kT, NK = N / 16;
+    constexpr int HS = N * 2 + 8;      // padded LDS row of the carried state (bf16 elements)
 
+    // LDS: [B rows | X^T] during the intra-chunk products; the carried state (hi/lo)
+    // reuses the same bytes afterwards; then the per-token factors.
     bf16 *sB = reinterpret_cast<bf16 *>(lds);      // [Q][BS]   B rows of the chunk
     bf16 *sXT = sB + Q * BS;                        // [P][XS]   X^T of the chunk
-    float *sDt = reinterpret_cast<float *>(sXT + P * XS);  // [Q]
+    bf16 *sH = reinterpret_cast<bf16 *>(lds);       // [P][HS]   carried state, later
+    const size_t big = max((size_t)Q * BS + (size_t)P * XS, (size_t)P * HS) * 2;
+    float *sDt = reinterpret_cast<float *>(lds + big);  // [Q]
     float *sDtA = sDt + Q, *sR = sDtA + Q, *sSuf = sR + Q, *sColf = sSuf + Q, *sEin = sColf + Q;
     float *sTot = sEin + Q;                         // [8]
     float *sMid = sTot + 8;                         // [8][8]
 
     const size_t tok0 = (size_t)seq * p.L + c0;
     const float Ah = p.A[h], Dh = p.D[h];
-    for (int s = tid; s < Q; s += NT) {
-        const float d = s < len ? bf2f(p.dt[(tok0 + s) * H + h]) : 0.f;
-        sDt[s] = d;
-        sDtA[s] = d * Ah;
+    const int nt = Q / kT;
+    const int I = wave < nt / 2 ? wave : nt - 1 - (wave - nt / 2);  // this wave's 32-row tile
+    const bool active = I * kT < len;
+    const int t = I * kT + l32;  // this lane's output row as an A/B operand index
+
+    // C rows of this wave's tile (the B operand of Z and the A operand of C h_in), first,
+    // so that their latency overlaps the staging below
+    bf16x8 cf[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+        cf[kk] = (active && t < len)
+                     ? *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + t) * G + g) * N + kk * 16 + hf * 8)
+                     : bf16x8{};
+
+    // every global load of the staging is issued before the first LDS write
+    const float dv = tid < Q && tid < len ? bf2f(p.dt[(tok0 + tid) * H + h]) : 0.f;  // NT = 2Q >= Q
+    constexpr int BI = N / 16;  // B pieces per thread: Q*N/8 pieces over NT = 2Q threads
+    uint4 vb[BI];
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int it = tid + j * NT;
+        const int sr = it / (N / 8), ng = it % (N / 8);
+        vb[j] = sr < len ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + sr) * G + g) * N + ng * 8)
+                         : make_uint4(0, 0, 0, 0);
     }
-    // B rows (zero past the chunk end)
-    for (int it = tid; it < Q * (N / 8); it += NT) {
-        const int s = it / (N / 8), ng = it % (N / 8);
-        const uint4 v = s < len ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + s) * G + g) * N + ng * 8)
-                                : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(sB + s * BS + ng * 8) = v;
-    }
-    // X^T (zero past the chunk end: those columns meet zero weights, but 0 * NaN is not 0)
-    for (int it = tid; it < (Q / 4) * (P / 8); it += NT) {
-        // token quads fastest: neighbouring threads write neighbouring 8 bytes of a row
+    constexpr int XI = (P + 63) / 64;  // X items (4 tokens x 8 columns) per thread
+    uint4 vx[XI][4];
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+        const int it = tid + j * NT;
         const int pg = it / (Q / 4), sq = it % (Q / 4);
-        uint4 v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int s = sq * 4 + r;
-            v[r] = s < len ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + s) * H + h) * P + pg * 8)
+            const int sr = sq * 4 + r;
+            vx[j][r] = (it < (Q / 4) * (P / 8) && sr < len)
+                           ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + sr) * H + h) * P + pg * 8)
                            : make_uint4(0, 0, 0, 0);
         }
-        const uint16_t *e0 = reinterpret_cast<const uint16_t *>(&v[0]);
-        const uint16_t *e1 = reinterpret_cast<const uint16_t *>(&v[1]);
-        const uint16_t *e2 = reinterpret_cast<const uint16_t *>(&v[2]);
-        const uint16_t *e3 = reinterpret_cast<const uint16_t *>(&v[3]);
+    }
+    if (tid < Q) {
+        sDt[tid] = dv;
+        sDtA[tid] = dv * Ah;  // zero past the chunk end
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint2 w;
-            w.x = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
-            w.y = (uint32_t)e2[i] | ((uint32_t)e3[i] << 16);
-            *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * XS + sq * 4) = w;
-        }
+    for (int j = 0; j < BI; ++j) {
+        const int it = tid + j * NT;
+        const int sr = it / (N / 8), ng = it % (N / 8);
+        *reinterpret_cast<uint4 *>(sB + sr * BS + ng * 8) = vb[j];
+    }
+    // X^T (zero past the chunk end: those columns meet zero weights, but 0 * NaN is not 0);
+    // token quads fastest, so neighbouring threads write neighbouring 8 bytes of a row
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+        const int it = tid + j * NT;
+        if (it >= (Q / 4) * (P / 8)) break;
+        const int pg = it / (Q / 4), sq = it % (Q / 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * XS + sq * 4) =
+                column4(vx[j][0], vx[j][1], vx[j][2], vx[j][3], i);
     }
     __syncthreads();
     chunk_factors(sDtA, len, sR, sSuf, sTot, tid, NT);
@@ -375,55 +466,35 @@ __global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
         sEin[s] = __expf(m);                  // decay from the chunk start through s
     }
     if (tid < 64) {
-        const int I = tid / 8, J = tid % 8;
+        const int Ii = tid / 8, J = tid % 8;
         float m = 0.f;
-        for (int q = J + 1; q < I; ++q) m += sTot[q];
-        sMid[tid] = (J < I && I < ntile) ? __expf(m) : 0.f;  // whole tiles strictly between J and I
+        for (int q = J + 1; q < Ii; ++q) m += sTot[q];
+        sMid[tid] = (J < Ii && Ii < ntile) ? __expf(m) : 0.f;  // whole tiles strictly between J and Ii
     }
     __syncthreads();
 
+    // the carried state of this chunk ([p][n] groups of 8 hi + 8 lo bf16), fetched into
+    // registers now and parked in LDS once the intra-chunk products are done
     const bool has_hin = p.cont || c > 0;
-    const bf16 *hin = reinterpret_cast<const bf16 *>(p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N);
-    const int nt = Q / kT;
-    constexpr int PT = P / kT, NK = N / 16;
-    for (int which = 0; which < 2; ++which) {
-        const int I = which == 0 ? wave : nt - 1 - wave;
-        if (I * kT >= len) continue;
-        const int t = I * kT + l32;  // this lane's output row as an A/B operand index
-        // C rows of this tile: the B operand of Z and the A operand of C h_in
-        bf16x8 cf[NK];
+    const uint4 *hin = reinterpret_cast<const uint4 *>(p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N);
+    constexpr int HV = P * N * 4 / 16;  // 16-byte pieces
+    constexpr int HPT = (HV + 511) / 512;
+    constexpr bool kPrefetch = HPT <= 8;  // larger states are read at the LDS write instead
+    // the prefetch covers the whole state only when NT * HPT pieces do (512 threads)
+    const bool pre = kPrefetch && NT * HPT >= HV;
+    uint4 hpre[kPrefetch ? HPT : 1];
+    if (pre && has_hin) {
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            cf[kk] = t < len ? *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + t) * G + g) * N + kk * 16 + hf * 8)
-                             : bf16x8{};
+        for (int i = 0; i < HPT; ++i) {
+            const int v = tid + i * NT;
+            hpre[i] = v < HV ? hin[v] : make_uint4(0, 0, 0, 0);
         }
-        f32x16 acc[PT];
+    }
+
+    f32x16 acc[PT];
 #pragma unroll
-        for (int i = 0; i < PT; ++i) acc[i] = f32x16{};
-        if (has_hin) {
-            // acc = C_I h_in (hi + lo), then rows scaled by the decay since the chunk start
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                // row p of the [p][n] slots: fp32-sized, so 2N bf16 per row
-                const bf16 *row = hin + (size_t)(pt * kT + l32) * N * 2;
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    const bf16 *grp = row + (kk * 2 + hf) * 8 * 2;  // 8 hi then 8 lo
-                    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(grp);
-                    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(grp + 8);
-                    acc[pt] = mfma(cf[kk], bh, acc[pt]);
-                    acc[pt] = mfma(cf[kk], bl, acc[pt]);
-                }
-            }
-            float ein[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ein[r] = sEin[min(I * kT + 8 * (r / 4) + 4 * hf + (r % 4), Q - 1)];
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[pt][r] *= ein[r];
-            }
-        }
+    for (int i = 0; i < PT; ++i) acc[i] = f32x16{};
+    if (active) {
         // rows t >= len are computed but never stored (MFMA rows do not mix)
         const float et = __expf(sR[min(t, Q - 1)]);
         // off-diagonal tiles J < I: every s < t, so no mask; decay = colf(s) * mid(I,J) * e^{R_t}
@@ -482,22 +553,65 @@ __global__ __launch_bounds__(256) void chunk_out_mfma(const MParams p) {
             }
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
-        // y rows of this tile (lane: column p, rows t = 32I + 8(r/4) + 4hf + r%4)
-        float *yb = p.y + ((tok0 + I * kT) * H + h) * P + l32;
-        const int ystride = H * P;
+    }
+    if (has_hin) {
+        __syncthreads();  // every wave is done with B and X^T
+        // N/4 pieces of 16 B per row p of the state
+        if (pre) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int tl = 8 * (r / 4) + 4 * hf + (r % 4);
-            if (I * kT + tl < len) {
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) yb[tl * ystride + pt * kT] = acc[pt][r];
+            for (int i = 0; i < (kPrefetch ? HPT : 1); ++i) {
+                const int v = tid + i * NT;
+                if (v < HV) *reinterpret_cast<uint4 *>(sH + (v / (N / 4)) * HS + (v % (N / 4)) * 8) = hpre[i];
             }
+        } else {
+            for (int v = tid; v < HV; v += NT)
+                *reinterpret_cast<uint4 *>(sH + (v / (N / 4)) * HS + (v % (N / 4)) * 8) = hin[v];
+        }
+        __syncthreads();
+        if (active) {
+            // acc += diag(exp(a_t)) C_I h_in, h_in as hi + lo
+            f32x16 acc2[PT];
+#pragma unroll
+            for (int i = 0; i < PT; ++i) acc2[i] = f32x16{};
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const bf16 *row = sH + (pt * kT + l32) * HS;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const bf16 *grp = row + (kk * 2 + hf) * 16;  // 8 hi then 8 lo
+                    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(grp);
+                    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(grp + 8);
+                    acc2[pt] = mfma(cf[kk], bh, acc2[pt]);
+                    acc2[pt] = mfma(cf[kk], bl, acc2[pt]);
+                }
+            }
+            float ein[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ein[r] = sEin[min(I * kT + 8 * (r / 4) + 4 * hf + (r % 4), Q - 1)];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[pt][r] = __builtin_fmaf(ein[r], acc2[pt][r], acc[pt][r]);
+            }
+        }
+    }
+    if (!active) return;
+    // y rows of this tile (lane: column p, rows t = 32I + 8(r/4) + 4hf + r%4)
+    float *yb = p.y + ((tok0 + I * kT) * H + h) * P + l32;
+    const int ystride = H * P;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int tl = 8 * (r / 4) + 4 * hf + (r % 4);
+        if (I * kT + tl < len) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) yb[tl * ystride + pt * kT] = acc[pt][r];
         }
     }
 }
 
 size_t out_lds_bytes(int Q, int N, int P) {
-    return (size_t)Q * (N + 8) * 2 + (size_t)P * (Q + 8) * 2 + 6 * Q * 4 + 8 * 4 + 64 * 4;
+    const size_t big = std::max((size_t)Q * (N + 8) + (size_t)P * (Q + 8), (size_t)P * (N * 2 + 8)) * 2;
+    return big + 6 * Q * 4 + 8 * 4 + 64 * 4;
 }
 size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 + (4 * 256 + 8) * 4; }
 
@@ -577,7 +691,7 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     e = hipGetLastError();
     if (e != hipSuccess || y == nullptr) return e;
     trace_begin(c, MIL_TRACE_PREFILL_OUT, s);
-    e = hipLaunchKernel(k3, dim3(nseq * p.nch * p.H), dim3(chunk / 64 * 64), args, l3, s);
+    e = hipLaunchKernel(k3, dim3(nseq * p.nch * p.H), dim3(chunk / 32 * 64), args, l3, s);
     trace_end(c, MIL_TRACE_PREFILL_OUT, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
