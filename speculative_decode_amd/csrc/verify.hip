@@ -29,6 +29,8 @@ hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B
     vp.G = c.dims.ngroups;
     vp.K = K;
     vp.k_max = c.k_max;
+    vp.cs = 1;  // set by the launcher from the chosen shape
+    vp.vec = (((uintptr_t)x | (uintptr_t)B | (uintptr_t)C) & 15) == 0;
     const int batch = c.dims.batch;
     const int id = K > 0 ? MIL_TRACE_VERIFY : MIL_TRACE_FOLD;
     trace_begin(c, id, s);

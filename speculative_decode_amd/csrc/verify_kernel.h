@@ -17,9 +17,13 @@
 //   alpha_k = prod_{i<=k} abar_i,  beta_{k,s} = prod_{s<i<=k} abar_i,  abar_i = exp(dt_i A).
 // No draft token ever touches the stored state; a later commit decides which ones count.
 //
-// Work decomposition (gfx950, wave64): one workgroup per (slot, head), S waves.  A lane
-// owns 4 adjacent columns (16-byte loads) of ROWS consecutive state rows; P/4 lanes
-// cover a row, so a wave reads 64 * 16 bytes of whole rows per load instruction.  State
+// Work decomposition (gfx950, wave64): one workgroup per (slot, head, column tile of
+// P/CS columns), S waves.  A lane owns 4 adjacent columns (16-byte loads) of ROWS
+// consecutive state rows; P/(4 CS) lanes cover a row tile, so a wave reads 64 * 16
+// bytes per load instruction.  Splitting the columns keeps ROWS (and the registers a
+// lane needs) small enough for two workgroups to share a CU, one streaming while the
+// other computes; the readout needs no exchange between tiles, since every output
+// column sums over all N rows of its own column only.  State
 // traffic is one read and at most one write per element; per-row work is in registers,
 // partial C_k . h sums are combined across the row groups of a wave with shuffles and
 // across waves through LDS, always in the same order.
@@ -44,13 +48,16 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
+// The state is streamed: read once and written once per round, so its accesses carry
+// the non-temporal cache policy (bit 1 of the cache-policy operand on gfx94x/gfx950).
+constexpr int kStreamPolicy = 2;
 __device__ __forceinline__ float4 buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    const f32x4v t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const f32x4v t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamPolicy);
     return make_float4(t[0], t[1], t[2], t[3]);
 }
 __device__ __forceinline__ void buf_store4(float4 v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
     const f32x4v t = {v.x, v.y, v.z, v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, kStreamPolicy);
 }
 
 // The single state step that folds one accepted token into a stored state element:
@@ -70,35 +77,50 @@ struct VerifyParams {
     const float *A, *D;
     float *y;
     int H, P, N, G, K, k_max;
+    int cs;   // column tiles per head
+    int vec;  // draft x, B, C 16-byte aligned: token rows staged in 16-byte chunks
 };
 
-// Launch shape: S waves per workgroup, ROWS rows per lane.  More waves when there are
-// few (slot, head) pairs, at most 16 rows per lane where N allows, at least one.
+// Launch shape: CS column tiles per head, S waves per workgroup, ROWS rows per lane.
 struct Shape {
-    int S, ROWS;
+    int S, ROWS, CS;
 };
 
 // Threads a workgroup may have for a given ROWS (more rows need more registers per lane).
 constexpr int max_threads(int rows) { return rows >= 16 ? 512 : 1024; }
 
-inline size_t verify_lds_floats(int N, int P, int K, int kmax, int S) {
-    return (size_t)kmax * N + 2 * K * N + (size_t)kmax * P + K * P + kmax + 4 * K + K * K + (size_t)S * K * P;
+// LDS floats of one workgroup covering Pc columns.
+inline size_t verify_lds_floats(int N, int Pc, int K, int kmax, int S) {
+    return (size_t)kmax * N + 2 * K * N + (size_t)kmax * Pc + K * Pc + 2 * kmax + 4 * K + K * K + (size_t)S * K * Pc;
 }
 constexpr size_t kVerifyLdsMax = 160 * 1024;
 
+// Shape policy.  Whole rows per workgroup (CS = 1) whenever LDS allows: each workgroup
+// then streams one contiguous N x P block, which HBM serves better than the strided
+// halves or quarters of rows that column tiles read.  Within that, the fewest waves with
+// at most kRowsTarget rows per lane and at least kWavesTarget waves in the grid, else the
+// most waves (fewest rows per lane).  Column tiles only where a whole-row workgroup's LDS
+// (which grows with K, kmax and S) does not fit.
+constexpr int kRowsTarget = 8;
+constexpr int64_t kWavesTarget = 2048;
+
 // Launch shape for K drafts with up to kmax pending rows; S = 0 when none fits.
 inline Shape shape_for(int batch, int H, int P, int N, int K, int kmax) {
-    Shape best{0, 0};
+    Shape best{0, 0, 0};
     if (P < 16 || P > 256 || (P & (P - 1)) || N < 16 || N > 256 || (N & (N - 1))) return best;
-    const int RGW = 256 / P;  // row groups per wave (P/4 lanes per row)
-    for (int S = 1; S <= 16; S *= 2) {
-        const int rg = S * RGW;
-        if (rg > N) break;
-        const int rows = N / rg;
-        if (rows > 32 || S * 64 > max_threads(rows)) continue;
-        if (verify_lds_floats(N, P, K, kmax, S) * sizeof(float) > kVerifyLdsMax) continue;
-        best = {S, rows};
-        if ((int64_t)batch * H * S >= 2048 && rows <= 8) break;
+    for (int cs = 1; cs <= 4 && P / cs >= 16; cs *= 2) {
+        const int Pc = P / cs;
+        const int RGW = 256 / Pc;  // row groups per wave (Pc/4 lanes per row)
+        for (int S = 1; S <= 16; S *= 2) {
+            const int rg = S * RGW;
+            if (rg > N) break;
+            const int rows = N / rg;
+            if (rows > 32 || S * 64 > max_threads(rows)) continue;
+            if (verify_lds_floats(N, Pc, K, kmax, S) * sizeof(float) > kVerifyLdsMax) continue;
+            best = {S, rows, cs};
+            if (rows <= kRowsTarget && (int64_t)batch * H * cs * S >= kWavesTarget) return best;
+        }
+        if (best.S) return best;
     }
     return best;
 }
@@ -108,29 +130,43 @@ hipError_t dispatch_verify_f32(const VerifyParams &vp, int batch, hipStream_t s)
 
 namespace {
 
+// 16 stored bytes -> fp32 values in LDS (bf16 widens exactly by a 16-bit shift).
+__device__ __forceinline__ void put16(float *dst, const uint4 v, const uint16_t *) {
+    reinterpret_cast<float4 *>(dst)[0] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                                                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    reinterpret_cast<float4 *>(dst)[1] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                                                     __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+}
+__device__ __forceinline__ void put16(float *dst, const uint4 v, const float *) {
+    *reinterpret_cast<uint4 *>(dst) = v;
+}
+
 template <typename T, int ROWS>
 __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const VerifyParams p) {
     extern __shared__ __align__(16) float lds[];
     const int N = p.N, P = p.P, H = p.H, G = p.G, K = p.K, kmax = p.k_max;
-    const int LPR = P >> 2;        // lanes per state row
+    const int Pc = P / p.cs;       // columns of this workgroup's tile
+    const int LPR = Pc >> 2;       // lanes per state row
     const int RGW = 64 / LPR;      // row groups per wave
     const int NT = blockDim.x, S = NT >> 6;
     float *sRB = lds;              // [kmax][N]  pending rows' B
     float *sDB = sRB + kmax * N;   // [K][N]     drafts' B
     float *sDC = sDB + K * N;      // [K][N]     drafts' C
-    float *sRU = sDC + K * N;      // [kmax][P]  pending rows' dt * x
-    float *sXd = sRU + kmax * P;   // [K][P]     drafts' x
-    float *sRA = sXd + K * P;      // [kmax]     pending rows' abar
-    float *sDA = sRA + kmax;       // [K]        drafts' abar
+    float *sRX = sDC + K * N;      // [kmax][Pc] pending rows' x (own columns)
+    float *sXd = sRX + kmax * Pc;  // [K][Pc]    drafts' x (own columns)
+    float *sRA = sXd + K * Pc;     // [kmax]     pending rows' abar
+    float *sRdt = sRA + kmax;      // [kmax]     pending rows' dt
+    float *sDA = sRdt + kmax;      // [K]        drafts' abar
     float *sDdt = sDA + K;         // [K]        drafts' dt
     float *sAlpha = sDdt + K;      // [K]        alpha_k
     float *sW = sAlpha + K;        // [K][K]     beta_{k,s} dt_s (C_k . B_s)
-    float *sRed = sW + K * K;      // [S][K][P]  per-wave partial C_k . h0
+    float *sRed = sW + K * K;      // [S][K][Pc] per-wave partial C_k . h0
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c4 = lane % LPR, rsub = lane / LPR;
     const int n0 = (wave * RGW + rsub) * ROWS;
-    const int h = blockIdx.x, b = blockIdx.y;
+    const int h = blockIdx.x / p.cs, b = blockIdx.y;
+    const int col0 = (blockIdx.x - h * p.cs) * Pc;
     const int g = h / (H / G);
     const int m = p.pending[b];
     const float Ah = p.A[h];
@@ -143,39 +179,94 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     const T *dC = static_cast<const T *>(p.C);
     const T *dDt = static_cast<const T *>(p.dt);
 
-    // ---- token rows first (small), so that waiting for them does not wait for the state ----
-    for (int i = tid; i < m * N; i += NT) {
-        const int s = i / N, n = i - s * N;
-        sRB[i] = ld(pB, ((size_t)(b * kmax + s) * G + g) * N + n);
-    }
-    for (int i = tid; i < K * N; i += NT) {
-        const int k = i / N, n = i - k * N;
-        const size_t off = ((size_t)(b * K + k) * G + g) * N + n;
-        sDB[i] = ld(dB, off);
-        sDC[i] = ld(dC, off);
-    }
-    for (int i = tid; i < m * P; i += NT) {
-        const int s = i / P, c = i - s * P;
-        const size_t row = (size_t)(b * kmax + s) * H + h;
-        sRU[i] = ld(pDt, row) * ld(pX, row * P + c);
-    }
-    for (int i = tid; i < K * P; i += NT) {
-        const int k = i / P, c = i - k * P;
-        sXd[i] = ld(dX, ((size_t)(b * K + k) * H + h) * P + c);
-    }
-    if (tid < m) sRA[tid] = expf(ld(pDt, (size_t)(b * kmax + tid) * H + h) * Ah);
-    if (tid < K) {
-        const float d = ld(dDt, (size_t)(b * K + tid) * H + h);
-        sDdt[tid] = d;
-        sDA[tid] = expf(d * Ah);
-    }
+    if (K == 0 && m == 0) return;  // nothing to fold and nothing to read out
 
-    // ---- the state rows: 16-byte buffer loads, one read per element ----
+    // ---- staging.  The global loads go out in one batch and are waited on once: first
+    // the token rows this workgroup needs as 16-byte chunks (pending B, draft B, draft C:
+    // N wide; pending x, draft x: this tile's Pc columns), then the dt values, then the
+    // state rows.  Loads return in issue order, so writing the token rows to LDS waits
+    // for them alone while the state loads are still in flight. ----
+    constexpr int E = 16 / sizeof(T);       // elements per chunk
+    constexpr int CH = ROWS >= 32 ? 1 : 4;  // chunks per thread in the batch
+    const int lgN = __builtin_ctz(N / E), lgP = __builtin_ctz(Pc / E);
+    const int e0 = m << lgN, e1 = e0 + (K << lgN), e2 = e1 + (K << lgN);
+    const int e3 = e2 + (m << lgP), e4 = e3 + (K << lgP);
+    const bool batched = p.vec && e4 <= CH * NT;  // else: element loops after the state loads
+    const int xoff = (int)(sRX - lds);
+    uint4 v[CH];
+    int dst[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) dst[j] = -1;
+    if (batched) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = j * NT + tid;
+            if (c < e4) {
+                const T *src;
+                if (c < e2) {
+                    const int seg = c < e0 ? 0 : (c < e1 ? 1 : 2);
+                    const int cc = c - (seg == 0 ? 0 : (seg == 1 ? e0 : e1));
+                    const int r = cc >> lgN, q = (cc & ((1 << lgN) - 1)) * E;
+                    const size_t row = seg == 0 ? (size_t)(b * kmax + r) : (size_t)(b * K + r);
+                    src = (seg == 0 ? pB : (seg == 1 ? dB : dC)) + (row * G + g) * N + q;
+                    dst[j] = (seg == 0 ? 0 : (seg == 1 ? kmax * N : (kmax + K) * N)) + r * N + q;
+                } else {
+                    const bool pend = c < e3;
+                    const int cc = c - (pend ? e2 : e3);
+                    const int r = cc >> lgP, q = (cc & ((1 << lgP) - 1)) * E;
+                    const size_t row = pend ? (size_t)(b * kmax + r) : (size_t)(b * K + r);
+                    src = (pend ? pX : dX) + (row * H + h) * P + col0 + q;
+                    dst[j] = xoff + (pend ? 0 : kmax * Pc) + r * Pc + q;
+                }
+                v[j] = *reinterpret_cast<const uint4 *>(src);
+            }
+        }
+    }
+    // dt of pending row / draft `tid`, from rows that exist whatever m and K are
+    const size_t prow = (size_t)(b * kmax + min(tid, kmax - 1)) * H + h;
+    const T *dsrc = K > 0 ? dDt + (size_t)(b * K + max(min(tid, K - 1), 0)) * H + h : pDt + prow;
+    const float pdt = ld(pDt, prow);
+    const float ddt = ld(dsrc, 0);
+
+    // the state rows: 16-byte buffer loads, one read per element
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.state + (size_t)(b * H + h) * p.head_stride, N * P * 4);
-    const int voff = (n0 * P + 4 * c4) * 4;  // this lane's first row and columns
+    const int voff = (n0 * P + col0 + 4 * c4) * 4;  // this lane's first row and columns
     float4 hv[ROWS];
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) hv[i] = buf_load4(srs, voff, i * P * 4);
+
+    if (batched) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            if (dst[j] >= 0) put16(lds + dst[j], v[j], static_cast<const T *>(nullptr));
+    } else {
+        for (int i = tid; i < m * N; i += NT) {
+            const int s = i / N, n = i - s * N;
+            sRB[i] = ld(pB, ((size_t)(b * kmax + s) * G + g) * N + n);
+        }
+        for (int i = tid; i < K * N; i += NT) {
+            const int k = i / N, n = i - k * N;
+            const size_t off = ((size_t)(b * K + k) * G + g) * N + n;
+            sDB[i] = ld(dB, off);
+            sDC[i] = ld(dC, off);
+        }
+        for (int i = tid; i < m * Pc; i += NT) {
+            const int s = i / Pc, c = i - s * Pc;
+            sRX[i] = ld(pX, ((size_t)(b * kmax + s) * H + h) * P + col0 + c);
+        }
+        for (int i = tid; i < K * Pc; i += NT) {
+            const int k = i / Pc, c = i - k * Pc;
+            sXd[i] = ld(dX, ((size_t)(b * K + k) * H + h) * P + col0 + c);
+        }
+    }
+    if (tid < m) {
+        sRdt[tid] = pdt;
+        sRA[tid] = expf(pdt * Ah);
+    }
+    if (tid < K) {
+        sDdt[tid] = ddt;
+        sDA[tid] = expf(ddt * Ah);
+    }
 
     __syncthreads();
 
@@ -209,8 +300,9 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
 
     // ---- fold the m pending rows, token by token, then write the rows back once ----
     for (int s = 0; s < m; ++s) {
-        const float a = sRA[s];
-        const float4 u = *reinterpret_cast<const float4 *>(sRU + s * P + 4 * c4);
+        const float a = sRA[s], d = sRdt[s];
+        const float4 xr = *reinterpret_cast<const float4 *>(sRX + s * Pc + 4 * c4);
+        const float4 u = make_float4(d * xr.x, d * xr.y, d * xr.z, d * xr.w);  // dt * x
         const float *bs = sRB + s * N + n0;
 #pragma unroll
         for (int i = 0; i < ROWS; ++i) {
@@ -225,7 +317,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
 #pragma unroll
         for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
     }
-    if (K == 0) return;  // fold only
+    if (K == 0) return;  // fold only: no outputs
 
     // ---- C_k . h0 over this lane's rows, then over the wave's row groups ----
     for (int k = 0; k < K; ++k) {
@@ -245,7 +337,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
             acc.z += __shfl_xor(acc.z, d);
             acc.w += __shfl_xor(acc.w, d);
         }
-        if (rsub == 0) *reinterpret_cast<float4 *>(sRed + (wave * K + k) * P + 4 * c4) = acc;
+        if (rsub == 0) *reinterpret_cast<float4 *>(sRed + (wave * K + k) * Pc + 4 * c4) = acc;
     }
     __syncthreads();
 
@@ -255,7 +347,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
         const int k = i / LPR, q = i - k * LPR;
         float4 ch = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int w = 0; w < S; ++w) {
-            const float4 v = *reinterpret_cast<const float4 *>(sRed + (w * K + k) * P + 4 * q);
+            const float4 v = *reinterpret_cast<const float4 *>(sRed + (w * K + k) * Pc + 4 * q);
             ch.x += v.x;
             ch.y += v.y;
             ch.z += v.z;
@@ -265,31 +357,33 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
         float4 yv = make_float4(al * ch.x, al * ch.y, al * ch.z, al * ch.w);
         for (int s2 = 0; s2 <= k; ++s2) {
             const float wv = sW[k * K + s2];
-            const float4 xs = *reinterpret_cast<const float4 *>(sXd + s2 * P + 4 * q);
+            const float4 xs = *reinterpret_cast<const float4 *>(sXd + s2 * Pc + 4 * q);
             yv.x = __builtin_fmaf(wv, xs.x, yv.x);
             yv.y = __builtin_fmaf(wv, xs.y, yv.y);
             yv.z = __builtin_fmaf(wv, xs.z, yv.z);
             yv.w = __builtin_fmaf(wv, xs.w, yv.w);
         }
-        const float4 xk = *reinterpret_cast<const float4 *>(sXd + k * P + 4 * q);
+        const float4 xk = *reinterpret_cast<const float4 *>(sXd + k * Pc + 4 * q);
         yv.x = __builtin_fmaf(Dh, xk.x, yv.x);
         yv.y = __builtin_fmaf(Dh, xk.y, yv.y);
         yv.z = __builtin_fmaf(Dh, xk.z, yv.z);
         yv.w = __builtin_fmaf(Dh, xk.w, yv.w);
-        *reinterpret_cast<float4 *>(p.y + ((size_t)(b * K + k) * H + h) * P + 4 * q) = yv;
+        *reinterpret_cast<float4 *>(p.y + ((size_t)(b * K + k) * H + h) * P + col0 + 4 * q) = yv;
     }
 }
 
 template <typename T, int ROWS>
 hipError_t launch_one(const VerifyParams &vp, const Shape &sh, int batch, hipStream_t s) {
-    const size_t lds = sizeof(float) * verify_lds_floats(vp.N, vp.P, vp.K, vp.k_max, sh.S);
+    const size_t lds = sizeof(float) * verify_lds_floats(vp.N, vp.P / sh.CS, vp.K, vp.k_max, sh.S);
     auto kern = ssm_verify_kernel<T, ROWS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(vp.H, batch), dim3(sh.S * 64), lds, s, vp);
+    VerifyParams q = vp;
+    q.cs = sh.CS;
+    hipLaunchKernelGGL(kern, dim3(vp.H * sh.CS, batch), dim3(sh.S * 64), lds, s, q);
     return hipGetLastError();
 }
 

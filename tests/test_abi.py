@@ -190,3 +190,14 @@ def test_cache_status_checks(lib):
     assert lib.mil_ssm_cache_status(None, ctypes.byref(bad), 0, None) == L.MIL_E_INVALID
     c = attached(lib)
     assert lib.mil_ssm_cache_status(ctypes.byref(c), None, 0, None) == L.MIL_E_INVALID
+
+
+def test_largest_state_with_most_drafts_is_accepted(lib):
+    """N = P = 256 with k_max = 16 needs more LDS than one whole-row workgroup has; the
+    verify launch then splits the columns, so init and attach accept the shape."""
+    d = L.Dims(1, 1, 256, 256, 1)
+    for dtype in (L.MIL_F32, L.MIL_BF16):
+        c = L.CacheDesc()
+        n = lib.mil_ssm_cache_bytes(ctypes.byref(d), L.MIL_KMAX_LIMIT, dtype)
+        assert lib.mil_ssm_cache_attach(ctypes.byref(c), ctypes.byref(d), L.MIL_KMAX_LIMIT, dtype,
+                                        ctypes.c_void_p(FAKE), n) == L.MIL_OK

@@ -204,7 +204,7 @@ def test_tiny_f32_protocol_against_oracle():
 
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
 @pytest.mark.parametrize("shape", [(3, 4, 16, 16, 2), (2, 4, 32, 64, 1), (2, 2, 128, 128, 1), (2, 4, 64, 256, 2),
-                                   (1, 2, 256, 32, 2)])
+                                   (1, 2, 256, 32, 2), (1, 1, 256, 256, 1)])
 @pytest.mark.parametrize("K,k_max", [(1, 1), (4, 4), (5, 8), (8, 8), (16, 16)])
 def test_verify_rounds_against_oracle(dtype, shape, K, k_max):
     """Several rounds with ragged accepted lengths per sequence: y of every round and
