@@ -363,31 +363,36 @@ __device__ __forceinline__ void accumulate_mx(f32x16 *acc, const bf16x8 *ah, con
 }
 
 // ------------------------------------------------------------------------- phase 3
-// One workgroup per (seq, chunk, head); Q/32 waves, each owning one 32-row tile.  Waves
-// w and w + 4 share a SIMD, so tiles are dealt as I = w (w < nw/2) and I = nw-1-(w-nw/2):
-// a SIMD then holds tiles I and nw-1-I, whose causal parts (I+1 and nw-I column tiles)
-// add up to the same work on every SIMD, and its two waves hide each other's latency.
-template <int N, int P>
+// One workgroup per (seq, chunk, head, column slab of PC of the P columns); Q/32 waves,
+// each owning one 32-row tile.  Waves w and w + 4 share a SIMD, so tiles are dealt as
+// I = w (w < nw/2) and I = nw-1-(w-nw/2): a SIMD then holds tiles I and nw-1-I, whose
+// causal parts (I+1 and nw-I column tiles) add up to the same work on every SIMD, and
+// its two waves hide each other's latency.  Splitting the columns over P/PC workgroups
+// (which recompute the same C B^T tiles) spreads short prompts over more compute units;
+// the slabs of one (chunk, head) are consecutive items, so they share B and C in one L2.
+template <int N, int PC>
 __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
     extern __shared__ __align__(16) char lds[];
-    const int H = p.H, G = p.G, Q = p.Q;
-    const int nitems = p.nseq * p.nch * H;
+    const int H = p.H, G = p.G, Q = p.Q, P = p.P;
+    const int nps = P / PC;
+    const int nitems = p.nseq * p.nch * H * nps;
     const int item = xcd_item(nitems);
-    const int h = item % H, c = (item / H) % p.nch, seq = item / H / p.nch;
+    const int pc0 = (item % nps) * PC, hc = item / nps;
+    const int h = hc % H, c = (hc / H) % p.nch, seq = hc / H / p.nch;
     const int g = h / (H / G);
     const int c0 = c * Q, len = min(Q, p.L - c0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
     const int NT = blockDim.x;
     const int BS = N + 8, XS = Q + 8;  // padded LDS rows (elements)
-    constexpr int PT = P / kT, NK = N / 16;
+    constexpr int PT = PC / kT, NK = N / 16;
     constexpr int HS = N * 2 + 8;      // padded LDS row of the carried state (bf16 elements)
 
     // LDS: [B rows | X^T] during the intra-chunk products; the carried state (hi/lo)
     // reuses the same bytes afterwards; then the per-token factors.
     bf16 *sB = reinterpret_cast<bf16 *>(lds);      // [Q][BS]   B rows of the chunk
-    bf16 *sXT = sB + Q * BS;                        // [P][XS]   X^T of the chunk
-    bf16 *sH = reinterpret_cast<bf16 *>(lds);       // [P][HS]   carried state, later
-    const size_t big = max((size_t)Q * BS + (size_t)P * XS, (size_t)P * HS) * 2;
+    bf16 *sXT = sB + Q * BS;                        // [PC][XS]  X^T of the chunk, this slab
+    bf16 *sH = reinterpret_cast<bf16 *>(lds);       // [PC][HS]  carried state, later
+    const size_t big = max((size_t)Q * BS + (size_t)PC * XS, (size_t)PC * HS) * 2;
     float *sDt = reinterpret_cast<float *>(lds + big);  // [Q]
     float *sDtA = sDt + Q, *sR = sDtA + Q, *sSuf = sR + Q, *sColf = sSuf + Q, *sEin = sColf + Q;
     float *sTot = sEin + Q;                         // [8]
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
         vb[j] = sr < len ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + sr) * G + g) * N + ng * 8)
                          : make_uint4(0, 0, 0, 0);
     }
-    constexpr int XI = (P + 63) / 64;  // X items (4 tokens x 8 columns) per thread
+    constexpr int XI = (PC + 63) / 64;  // X items (4 tokens x 8 columns) per thread
     uint4 vx[XI][4];
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
@@ -429,8 +434,8 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int sr = sq * 4 + r;
-            vx[j][r] = (it < (Q / 4) * (P / 8) && sr < len)
-                           ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + sr) * H + h) * P + pg * 8)
+            vx[j][r] = (it < (Q / 4) * (PC / 8) && sr < len)
+                           ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + sr) * H + h) * P + pc0 + pg * 8)
                            : make_uint4(0, 0, 0, 0);
         }
     }
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
         const int it = tid + j * NT;
-        if (it >= (Q / 4) * (P / 8)) break;
+        if (it >= (Q / 4) * (PC / 8)) break;
         const int pg = it / (Q / 4), sq = it % (Q / 4);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -476,8 +481,9 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
     // the carried state of this chunk ([p][n] groups of 8 hi + 8 lo bf16), fetched into
     // registers now and parked in LDS once the intra-chunk products are done
     const bool has_hin = p.cont || c > 0;
-    const uint4 *hin = reinterpret_cast<const uint4 *>(p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N);
-    constexpr int HV = P * N * 4 / 16;  // 16-byte pieces
+    const uint4 *hin = reinterpret_cast<const uint4 *>(p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N +
+                                                       (size_t)pc0 * N);
+    constexpr int HV = PC * N * 4 / 16;  // 16-byte pieces of this slab's rows
     constexpr int HPT = (HV + 511) / 512;
     constexpr bool kPrefetch = HPT <= 8;  // larger states are read at the LDS write instead
     // the prefetch covers the whole state only when NT * HPT pieces do (512 threads)
@@ -597,7 +603,7 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
     }
     if (!active) return;
     // y rows of this tile (lane: column p, rows t = 32I + 8(r/4) + 4hf + r%4)
-    float *yb = p.y + ((tok0 + I * kT) * H + h) * P + l32;
+    float *yb = p.y + ((tok0 + I * kT) * H + h) * P + pc0 + l32;
     const int ystride = H * P;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -616,6 +622,7 @@ size_t out_lds_bytes(int Q, int N, int P) {
 size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 + (4 * 256 + 8) * 4; }
 
 constexpr size_t kLdsMax = 160 * 1024;
+constexpr int64_t kOutItemsTarget = 256;  // phase-3 workgroups wanted (one per compute unit)
 
 }  // namespace
 
@@ -663,7 +670,10 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     p.PS = p.P < 32768 / p.N ? p.P : 32768 / p.N;
     p.nslab = p.P / p.PS;
 
-    const size_t l1 = state_lds_bytes(p.PS, p.N), l3 = out_lds_bytes(chunk, p.N, p.P);
+    // phase-3 column slabs: split P until the grid has a workgroup per compute unit
+    int pc = p.P;
+    while (pc > kT && (int64_t)nseq * p.nch * p.H * (p.P / pc) < kOutItemsTarget) pc /= 2;
+    const size_t l1 = state_lds_bytes(p.PS, p.N), l3 = out_lds_bytes(chunk, p.N, pc);
     const int tpw = (p.PS / kT) * (p.N / kT) / 4;
     const void *k1 = tpw == 1 ? reinterpret_cast<const void *>(chunk_state_mfma<1>)
                    : tpw == 2 ? reinterpret_cast<const void *>(chunk_state_mfma<2>)
@@ -671,7 +681,7 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
                               : reinterpret_cast<const void *>(chunk_state_mfma<8>);
     const void *k3 = nullptr;
 #define MIL_OUT_CASE(n, pp) \
-    if (p.N == n && p.P == pp) k3 = reinterpret_cast<const void *>(chunk_out_mfma<n, pp>);
+    if (p.N == n && pc == pp) k3 = reinterpret_cast<const void *>(chunk_out_mfma<n, pp>);
     MIL_OUT_CASE(64, 32) MIL_OUT_CASE(64, 64) MIL_OUT_CASE(64, 128) MIL_OUT_CASE(64, 256)
     MIL_OUT_CASE(128, 32) MIL_OUT_CASE(128, 64) MIL_OUT_CASE(128, 128) MIL_OUT_CASE(128, 256)
     MIL_OUT_CASE(256, 32) MIL_OUT_CASE(256, 64) MIL_OUT_CASE(256, 128) MIL_OUT_CASE(256, 256)
@@ -691,7 +701,7 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     e = hipGetLastError();
     if (e != hipSuccess || y == nullptr) return e;
     trace_begin(c, MIL_TRACE_PREFILL_OUT, s);
-    e = hipLaunchKernel(k3, dim3(nseq * p.nch * p.H), dim3(chunk / 32 * 64), args, l3, s);
+    e = hipLaunchKernel(k3, dim3(nseq * p.nch * p.H * (p.P / pc)), dim3(chunk / 32 * 64), args, l3, s);
     trace_end(c, MIL_TRACE_PREFILL_OUT, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
