@@ -168,8 +168,8 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     const int h = blockIdx.x / p.cs, b = blockIdx.y;
     const int col0 = (blockIdx.x - h * p.cs) * Pc;
     const int g = h / (H / G);
-    const int m = p.pending[b];
-    const float Ah = p.A[h];
+    const int m = __builtin_amdgcn_readfirstlane(p.pending[b]);  // uniform: branches on m stay scalar
+    const float Ah = p.A[h], Dh = p.D[h];
 
     const T *pX = static_cast<const T *>(p.pend_x);
     const T *pB = static_cast<const T *>(p.pend_B);
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
         }
     }
 
-    // ---- fold the m pending rows, token by token, then write the rows back once ----
+    // ---- fold the m pending rows, token by token ----
     for (int s = 0; s < m; ++s) {
         const float a = sRA[s], d = sRdt[s];
         const float4 xr = *reinterpret_cast<const float4 *>(sRX + s * Pc + 4 * c4);
@@ -313,11 +313,16 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
             hv[i].w = state_step(a, hv[i].w, bn, u.w);
         }
     }
-    if (m > 0) {
+    // The rows are written back (once, when m > 0) only after the readout below has
+    // used them: memory operations complete in issue order, and a readout placed after
+    // the stores would wait for them to drain.
+    if (K == 0) {  // fold only: no outputs
+        if (m > 0) {
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
+            for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
+        }
+        return;
     }
-    if (K == 0) return;  // fold only: no outputs
 
     // ---- C_k . h0 over this lane's rows, then over the wave's row groups ----
     for (int k = 0; k < K; ++k) {
@@ -339,10 +344,13 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
         }
         if (rsub == 0) *reinterpret_cast<float4 *>(sRed + (wave * K + k) * Pc + 4 * c4) = acc;
     }
+    if (m > 0) {
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
+    }
     __syncthreads();
 
     // ---- outputs: waves summed in order, then the closed-form draft terms ----
-    const float Dh = p.D[h];
     for (int i = tid; i < K * LPR; i += NT) {
         const int k = i / LPR, q = i - k * LPR;
         float4 ch = make_float4(0.f, 0.f, 0.f, 0.f);
