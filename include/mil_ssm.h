@@ -178,6 +178,35 @@ int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted,
                    const void *x, const void *B, const void *dt,
                    const float *A, const float *D, uint32_t flags, mil_stream_t stream);
 
+/*
+ * Greedy acceptance on the device, fused into the commit.
+ * QbitAI article "Llama 3+Mamba 强强联手", speculative-decoding walkthrough: the verifier
+ * checks the K drafted tokens in order, the accepted ones are kept and the sequence is
+ * cut at the first rejected one.  The pages do not say what makes a draft "correct"; the
+ * reading taken here is greedy verification: draft k of slot b is correct when it equals
+ * the verifier's most likely token at that position, the argmax over the vocabulary of
+ * logits[b][k][:] (ties go to the lowest token id; a NaN with the sign bit clear counts as
+ * the largest value).  accepted[b] = the number of leading correct drafts (0..K).
+ *
+ * draft_tokens  device int32 [batch][K], token ids the drafts stand for;
+ * logits        device [batch][K][vocab], MIL_F32 or MIL_BF16 (logits_dtype, independent
+ *               of the cache dtype), the verifier's scores at the K draft positions;
+ * accepted      device int32 [batch], written with accepted[b];
+ * verifier_tokens  device int32 [batch][K] written with the argmax per position, or NULL;
+ * ws            caller-owned device workspace of at least mil_ssm_greedy_workspace_bytes
+ *               bytes, 256-byte aligned (partial maxima; no state is kept in it).
+ * Everything else (x, B, dt, A, D, flags, order, K) is as for mil_ssm_commit, with
+ * accepted[b] computed here instead of given; the cache ends up exactly as after
+ * mil_ssm_commit with those accepted lengths.
+ */
+size_t mil_ssm_greedy_workspace_bytes(const mil_ssm_dims *dims, int32_t K, int32_t vocab);
+int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens,
+                          const void *logits, int32_t vocab, int32_t logits_dtype,
+                          int32_t *accepted, int32_t *verifier_tokens,
+                          const void *x, const void *B, const void *dt,
+                          const float *A, const float *D, void *ws, size_t ws_bytes,
+                          uint32_t flags, mil_stream_t stream);
+
 /* Synchronise `stream`, then report device-side errors: *bad_slot = first slot with
  * err != 0, or -1.  Returns MIL_OK, or MIL_E_INVALID when a slot has an error.
  * With clear != 0 the err words are zeroed afterwards. */
@@ -194,7 +223,8 @@ enum mil_trace_kernel {
     MIL_TRACE_COMMIT = 3,        /* accepted-length bookkeeping */
     MIL_TRACE_PREFILL_STATE = 4, /* prefill phase 1: per-chunk states */
     MIL_TRACE_PREFILL_PASS = 5,  /* prefill phase 2: sequential pass across chunks */
-    MIL_TRACE_PREFILL_OUT = 6    /* prefill phase 3: per-chunk outputs */
+    MIL_TRACE_PREFILL_OUT = 6,   /* prefill phase 3: per-chunk outputs */
+    MIL_TRACE_ACCEPT = 7         /* greedy acceptance: vocabulary argmax per draft position */
 };
 
 /* Profiling hook: until changed, every launch of `kernel` made through this descriptor

@@ -116,3 +116,25 @@ def commit(state, x, B, dt, A, D, accepted, nthreads=None, lib=None):
     out = np.array(state, dtype=np.float64, copy=True)
     scan(x, B, None, dt, A, D, out, ntok=acc, want_y=False, nthreads=nthreads, lib=lib)
     return out
+
+
+def greedy_accept(draft_tokens, logits):
+    """Greedy acceptance (the QbitAI walkthrough's keep-until-the-first-rejection, with a
+    draft taken as correct when it is the verifier's most likely token at its position).
+
+    draft_tokens [batch][K] int, logits [batch][K][vocab] (the exact values the GPU gets,
+    widened to float64).  Returns (accepted [batch] int32, verifier_tokens [batch][K]
+    int32): the argmax token of every position (the first index among equal maxima, as
+    numpy's argmax takes it) and the number of leading positions whose draft equals it.
+    """
+    drafts = np.asarray(draft_tokens)
+    lg = np.asarray(logits, dtype=np.float64)
+    tokens = np.argmax(lg, axis=2).astype(np.int32)
+    batch, K = drafts.shape
+    accepted = np.zeros(batch, dtype=np.int32)
+    for b in range(batch):
+        j = 0
+        while j < K and drafts[b, j] == tokens[b, j]:
+            j += 1
+        accepted[b] = j
+    return accepted, tokens

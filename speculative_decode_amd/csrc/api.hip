@@ -234,6 +234,44 @@ int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, con
     return MIL_OK;
 }
 
+size_t mil_ssm_greedy_workspace_bytes(const mil_ssm_dims *d, int32_t K, int32_t vocab) {
+    if (check_dims(d) != MIL_OK || K < 1 || K > MIL_KMAX_LIMIT || vocab < 1) return 0;
+    return (size_t)greedy_workspace_bytes(d->batch, K);
+}
+
+int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
+                          int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
+                          const void *x, const void *B, const void *dt, const float *A, const float *D, void *ws,
+                          size_t ws_bytes, uint32_t flags, mil_stream_t stream) {
+    CacheImpl *c = impl(cache);
+    if (!c) return MIL_E_INVALID;
+    if (c->phase != kVerified) return MIL_E_ORDER;
+    if (flags & ~MIL_COMMIT_MATERIALIZE) return MIL_E_INVALID;
+    if (K != c->verified_k) return MIL_E_INVALID;
+    if (!draft_tokens || !logits || !accepted || !x || !B || !dt || vocab < 1) return MIL_E_INVALID;
+    if (check_dtype(logits_dtype) != MIL_OK) return MIL_E_INVALID;
+    const bool mat = (flags & MIL_COMMIT_MATERIALIZE) != 0;
+    if (mat && (!A || !D)) return MIL_E_INVALID;
+    const int64_t need = greedy_workspace_bytes(c->dims.batch, K);
+    if (!ws || (int64_t)ws_bytes < need) return MIL_E_WORKSPACE;
+    const int eb = elt_bytes(c->dtype);
+    if (!aligned(draft_tokens, 4) || !aligned(accepted, 4) || (verifier_tokens && !aligned(verifier_tokens, 4)) ||
+        !aligned(logits, elt_bytes(logits_dtype)) || !aligned(ws, kAlign) || !aligned(x, 4) || !aligned(B, 4) ||
+        !aligned(dt, eb))
+        return MIL_E_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch_commit_greedy(*c, K, draft_tokens, logits, vocab, logits_dtype, accepted, verifier_tokens,
+                                        x, B, dt, ws, s);
+    if (e == hipSuccess && mat) {
+        e = launch_verify(*c, 0, nullptr, nullptr, nullptr, nullptr, A, D, nullptr, s);
+        if (e == hipSuccess) e = launch_clear_pending(*c, s);
+    }
+    if (e != hipSuccess) return MIL_E_HIP;
+    c->phase = kReady;
+    c->verified_k = 0;
+    return MIL_OK;
+}
+
 int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t clear, mil_stream_t stream) {
     const CacheImpl *c = impl(cache);
     if (!c || !bad_slot) return MIL_E_INVALID;
@@ -269,7 +307,7 @@ int mil_ssm_cache_phase(const mil_ssm_cache *cache) {
 
 int mil_ssm_cache_trace(mil_ssm_cache *cache, int32_t kernel, void *ev_start, void *ev_stop) {
     CacheImpl *c = impl(cache);
-    if (!c || kernel < MIL_TRACE_OFF || kernel > MIL_TRACE_PREFILL_OUT) return MIL_E_INVALID;
+    if (!c || kernel < MIL_TRACE_OFF || kernel > MIL_TRACE_ACCEPT) return MIL_E_INVALID;
     if (kernel == MIL_TRACE_OFF || !ev_start || !ev_stop) {
         c->trace_kernel = MIL_TRACE_OFF;
         c->trace_start = c->trace_stop = nullptr;

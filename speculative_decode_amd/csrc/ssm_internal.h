@@ -65,6 +65,11 @@ hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, con
 
 // pending[b] = 0 for every slot (after a fold that has consumed them).
 hipError_t launch_clear_pending(const CacheImpl &c, hipStream_t s);
+// Greedy acceptance fused into the commit (argmax over the vocabulary per draft position).
+int64_t greedy_workspace_bytes(int batch, int K);
+hipError_t launch_commit_greedy(const CacheImpl &c, int K, const int32_t *draft, const void *logits, int vocab,
+                                int logits_dtype, int32_t *accepted, int32_t *tokens, const void *x, const void *B,
+                                const void *dt, void *ws, hipStream_t s);
 
 // Chunked prefill (three phases: chunk states, inter-chunk pass, chunk outputs).  The
 // inter-chunk pass also sets pos[slot] = L (or += L when cont) for the prefilled slots

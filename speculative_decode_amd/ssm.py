@@ -177,3 +177,40 @@ class SSMCache:
                                     _ptr(A), _ptr(D), L.MIL_COMMIT_MATERIALIZE if materialize else 0,
                                     _stream(self.device))
         L.check(st, "mil_ssm_commit")
+
+    def greedy_workspace_bytes(self, K: int, vocab: int) -> int:
+        return int(L.lib().mil_ssm_greedy_workspace_bytes(ctypes.byref(self.dims), K, vocab))
+
+    def commit_greedy(self, draft_tokens, logits, x, B, dt, A=None, D=None, materialize=False,
+                      want_tokens=False, accepted=None, ws=None):
+        """Greedy acceptance on the device, then the commit: draft_tokens [batch][K] int32,
+        logits [batch][K][vocab] (float32 or bfloat16).  Returns (accepted [batch] int32,
+        verifier_tokens [batch][K] int32 or None)."""
+        K = x.shape[1]
+        self._check_tokens("commit_greedy", x, B, dt)
+        self._check_shapes("commit_greedy", self.batch, K, x, B, None, dt, A, D, None)
+        if draft_tokens.dtype != torch.int32 or draft_tokens.device != self.device:
+            raise TypeError("draft_tokens must be an int32 tensor on the cache's device")
+        if tuple(draft_tokens.shape) != (self.batch, K) or not draft_tokens.is_contiguous():
+            raise ValueError(f"commit_greedy: draft_tokens must have shape ({self.batch}, {K})")
+        if logits.device != self.device or logits.dim() != 3 or not logits.is_contiguous():
+            raise ValueError("commit_greedy: logits must be a contiguous [batch][K][vocab] tensor on the device")
+        if tuple(logits.shape[:2]) != (self.batch, K):
+            raise ValueError(f"commit_greedy: logits must start with ({self.batch}, {K})")
+        ldt = {torch.float32: L.MIL_F32, torch.bfloat16: L.MIL_BF16}.get(logits.dtype)
+        if ldt is None:
+            raise TypeError("logits must be float32 or bfloat16")
+        vocab = int(logits.shape[2])
+        if accepted is None:
+            accepted = torch.empty(self.batch, dtype=torch.int32, device=self.device)
+        tokens = torch.empty((self.batch, K), dtype=torch.int32, device=self.device) if want_tokens else None
+        need = self.greedy_workspace_bytes(K, vocab)
+        if ws is None:
+            ws = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
+        wp = (ws.data_ptr() + 255) // 256 * 256
+        st = L.lib().mil_ssm_commit_greedy(ctypes.byref(self.desc), K, _ptr(draft_tokens), _ptr(logits), vocab, ldt,
+                                           _ptr(accepted), _ptr(tokens), _ptr(x), _ptr(B), _ptr(dt), _ptr(A),
+                                           _ptr(D), ctypes.c_void_p(wp), ws.numel() - (wp - ws.data_ptr()),
+                                           L.MIL_COMMIT_MATERIALIZE if materialize else 0, _stream(self.device))
+        L.check(st, "mil_ssm_commit_greedy")
+        return accepted, tokens

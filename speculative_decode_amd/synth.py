@@ -110,6 +110,29 @@ def draw_accept_geometric(rng: np.random.Generator, batch: int, K: int, p: float
     return np.minimum(rng.geometric(p, size=batch) - 1, K).astype(np.int32)
 
 
+def draw_greedy(rng: np.random.Generator, batch: int, K: int, vocab: int, dtype: str,
+                planted: np.ndarray, ties: bool = False):
+    """Verifier logits [batch][K][vocab] ~ N(0,1) and draft tokens [batch][K] ~ U{0..vocab-1},
+    with a structure planted so that greedy verification accepts planted[b] drafts: at
+    positions k < planted[b] the draft's logit is set to 16 (far above every N(0,1) draw),
+    at k = planted[b] to -16.  With ties=True, some planted maxima get a second 16 at
+    another id (lower or higher than the draft), which makes the tie rule decide.
+    Returns (draft_tokens int32, logits Tensor)."""
+    draft = rng.integers(0, vocab, size=(batch, K)).astype(np.int32)
+    lg = rng.standard_normal((batch, K, vocab))
+    for b in range(batch):
+        for k in range(K):
+            if k < planted[b]:
+                lg[b, k, draft[b, k]] = 16.0
+                if ties and rng.random() < 0.5:
+                    other = int(rng.integers(0, vocab))
+                    if other != draft[b, k]:
+                        lg[b, k, other] = 16.0
+            elif k == planted[b]:
+                lg[b, k, draft[b, k]] = -16.0
+    return draft, quantize(lg, dtype)
+
+
 def integer_tokens(rng: np.random.Generator, batch: int, T: int, H: int, P: int, N: int,
                    G: int, dtype: str, lo: int = -1, hi: int = 1) -> Tokens:
     """Small-integer x, B, C with dt = 1: every product and partial sum of the

@@ -201,3 +201,27 @@ def test_largest_state_with_most_drafts_is_accepted(lib):
         n = lib.mil_ssm_cache_bytes(ctypes.byref(d), L.MIL_KMAX_LIMIT, dtype)
         assert lib.mil_ssm_cache_attach(ctypes.byref(c), ctypes.byref(d), L.MIL_KMAX_LIMIT, dtype,
                                         ctypes.c_void_p(FAKE), n) == L.MIL_OK
+
+
+def test_greedy_workspace_bytes(lib):
+    d = dims(batch=16)
+    w = lib.mil_ssm_greedy_workspace_bytes(ctypes.byref(d), 8, 128256)
+    assert w >= 16 * 8 * 8 and w % 256 == 0
+    assert lib.mil_ssm_greedy_workspace_bytes(ctypes.byref(d), 0, 128256) == 0
+    assert lib.mil_ssm_greedy_workspace_bytes(ctypes.byref(d), L.MIL_KMAX_LIMIT + 1, 128256) == 0
+    assert lib.mil_ssm_greedy_workspace_bytes(ctypes.byref(d), 8, 0) == 0
+
+
+def test_commit_greedy_checks(lib):
+    c = attached(lib, k_max=8)
+    f = lib.mil_ssm_commit_greedy
+    need = lib.mil_ssm_greedy_workspace_bytes(ctypes.byref(dims()), 4, 1000)
+
+    def call(cache=c, K=4, draft=P(), logits=P(), vocab=1000, ldt=L.MIL_BF16, acc=P(), tok=None, ws=P(),
+             ws_bytes=need, flags=0):
+        return f(ctypes.byref(cache), K, draft, logits, vocab, ldt, acc, tok, P(), P(), P(), None, None, ws,
+                 ws_bytes, flags, None)
+
+    assert call() == L.MIL_E_ORDER  # no verify before it (the checks after a verify are GPU tests)
+    assert call(cache=L.CacheDesc()) == L.MIL_E_INVALID  # never initialised
+    assert lib.mil_ssm_cache_phase(ctypes.byref(c)) == L.PHASE_READY

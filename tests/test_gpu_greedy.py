@@ -1,0 +1,153 @@
+"""GPU parity of the greedy acceptance fused into the commit (mil_ssm_commit_greedy)
+against the oracle's greedy_accept, and of the cache it leaves against a plain commit of
+the same accepted lengths.  Accepted lengths and argmax tokens are integers: compared bit
+for bit.  The argmax is taken on the exact values both sides receive (fp32, or bf16
+widened), so ties are decided the same way (lowest token id)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, dev, dev_layer, dev_tokens, state_err
+from speculative_decode_amd import _lib as L
+from speculative_decode_amd import synth
+from speculative_decode_amd.ssm import SSMCache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    L.lib()  # a missing library is a failure, not a skip
+
+
+def logits_dev(lg: synth.Tensor) -> torch.Tensor:
+    if lg.dtype == synth.BF16:
+        return torch.from_numpy(np.ascontiguousarray(lg.store).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(lg.store)).cuda()
+
+
+def two_caches(rng, shape, dtype, K, k_max):
+    """Two caches with the same prefilled context and the same verified drafts."""
+    Bt, H, P, N, G = shape
+    layer = synth.draw_layer(rng, H)
+    pre = synth.draw_tokens(rng, Bt, 24, H, P, N, G, dtype)
+    drafts = synth.draw_tokens(rng, Bt, K, H, P, N, G, dtype)
+    A, D = dev_layer(layer)
+    caches = []
+    for _ in range(2):
+        c = SSMCache(Bt, H, P, N, G, k_max, dtype)
+        c.prefill(*dev_tokens(pre), A, D)
+        dx, dB, dC, ddt = dev_tokens(drafts)
+        c.verify(dx, dB, dC, ddt, A, D)
+        caches.append(c)
+    return layer, pre, drafts, (A, D), caches
+
+
+CASES = [  # (batch, K, vocab, logits dtype, ties)
+    (1, 4, 1, synth.F32, False),
+    (3, 5, 7, synth.BF16, True),
+    (2, 4, 1000, synth.F32, True),
+    (4, 8, 4099, synth.BF16, False),   # odd vocab: bf16 rows not 16-byte aligned
+    (5, 16, 32000, synth.BF16, True),
+    (2, 3, 50000, synth.F32, False),
+]
+
+
+@pytest.mark.parametrize("batch,K,vocab,ldt,ties", CASES)
+def test_greedy_commit_matches_oracle(batch, K, vocab, ldt, ties):
+    rng = np.random.default_rng(1000 + batch * K + vocab)
+    shape = (batch, 4, 32, 32, 2)
+    layer, pre, drafts, (A, D), (cg, cp) = two_caches(rng, shape, synth.BF16, K, 16)
+    planted = rng.integers(0, K + 1, size=batch).astype(np.int32)
+    draft_tok, lg = synth.draw_greedy(rng, batch, K, vocab, ldt, planted, ties=ties)
+    j_ref, tok_ref = oracle.greedy_accept(draft_tok, lg.f64)
+    dx, dB, dC, ddt = dev_tokens(drafts)
+    acc, tok = cg.commit_greedy(torch.from_numpy(draft_tok).cuda(), logits_dev(lg), dx, dB, ddt, A, D,
+                                want_tokens=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), tok_ref)
+    assert np.array_equal(acc.cpu().numpy(), j_ref)
+    # the same cache as a plain commit of those lengths: counters, and the next round's y bit for bit
+    cp.commit(torch.from_numpy(j_ref).cuda(), dx, dB, ddt, A, D)
+    assert torch.equal(cg.pos(), cp.pos()) and torch.equal(cg.pending(), cp.pending())
+    nxt = synth.draw_tokens(rng, batch, K, 4, 32, 32, 2, synth.BF16)
+    ys = [c.verify(*dev_tokens(nxt), A, D) for c in (cg, cp)]
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    assert torch.equal(cg.state(), cp.state())
+
+
+def test_greedy_commit_full_vocabulary_batched():
+    """16 sequences, K = 8, the 128256-token vocabulary, bf16 logits."""
+    rng = np.random.default_rng(77)
+    batch, K, vocab = 16, 8, 128256
+    shape = (batch, 4, 32, 32, 2)
+    _, _, drafts, (A, D), (cg, _) = two_caches(rng, shape, synth.BF16, K, 8)
+    planted = synth.draw_accept_uniform(rng, batch, K)
+    draft_tok, lg = synth.draw_greedy(rng, batch, K, vocab, synth.BF16, planted, ties=True)
+    j_ref, tok_ref = oracle.greedy_accept(draft_tok, lg.f64)
+    dx, dB, dC, ddt = dev_tokens(drafts)
+    acc, tok = cg.commit_greedy(torch.from_numpy(draft_tok).cuda(), logits_dev(lg), dx, dB, ddt, A, D,
+                                want_tokens=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), tok_ref)
+    assert np.array_equal(acc.cpu().numpy(), j_ref)
+
+
+def test_greedy_commit_materialize_against_oracle():
+    """With MIL_COMMIT_MATERIALIZE the state is the oracle's state after the accepted drafts."""
+    rng = np.random.default_rng(91)
+    batch, K, vocab = 3, 4, 3000
+    shape = (batch, 4, 32, 32, 2)
+    layer, pre, drafts, (A, D), (cg, _) = two_caches(rng, shape, synth.F32, K, 4)
+    planted = np.array([0, 2, 4], dtype=np.int32)
+    draft_tok, lg = synth.draw_greedy(rng, batch, K, vocab, synth.F32, planted)
+    j_ref, _ = oracle.greedy_accept(draft_tok, lg.f64)
+    dx, dB, dC, ddt = dev_tokens(drafts)
+    cg.commit_greedy(torch.from_numpy(draft_tok).cuda(), logits_dev(lg), dx, dB, ddt, A, D, materialize=True)
+    _, h = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64)
+    ref = oracle.commit(h, drafts.x.f64, drafts.B.f64, drafts.dt.f64, layer.A.f64, layer.D.f64, j_ref)
+    torch.cuda.synchronize()
+    assert state_err(cg.state().cpu().numpy().astype(np.float64), ref) <= TOL[synth.F32]
+    assert cg.pos().cpu().tolist() == (24 + j_ref).tolist()
+
+
+def test_greedy_commit_argument_checks():
+    """Checks that need a verified cache (so a GPU): each error leaves the phase VERIFIED."""
+    rng = np.random.default_rng(5)
+    batch, K, vocab = 2, 4, 100
+    _, _, drafts, (A, D), (c, _) = two_caches(rng, (batch, 4, 32, 32, 2), synth.BF16, K, 8)
+    lib = L.lib()
+    dx, dB, dC, ddt = dev_tokens(drafts)
+    draft_tok = torch.zeros((batch, K), dtype=torch.int32, device="cuda")
+    logits = torch.zeros((batch, K, vocab), dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty(batch, dtype=torch.int32, device="cuda")
+    need = lib.mil_ssm_greedy_workspace_bytes(__import__("ctypes").byref(c.dims), K, vocab)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    wp = (ws.data_ptr() + 255) // 256 * 256
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call(K=K, draft=P(draft_tok), lgp=P(logits), vocab=vocab, ldt=L.MIL_BF16, accp=P(acc), wsp=wp,
+             wsb=need):
+        return lib.mil_ssm_commit_greedy(ctypes.byref(c.desc), K, draft, lgp, vocab, ldt, accp, None, P(dx), P(dB),
+                                         P(ddt), None, None, ctypes.c_void_p(wsp), wsb, 0, None)
+
+    assert call(K=K - 1) == L.MIL_E_INVALID
+    assert call(draft=None) == L.MIL_E_INVALID
+    assert call(lgp=None) == L.MIL_E_INVALID
+    assert call(accp=None) == L.MIL_E_INVALID
+    assert call(vocab=0) == L.MIL_E_INVALID
+    assert call(ldt=7) == L.MIL_E_INVALID
+    assert call(wsb=need - 1) == L.MIL_E_WORKSPACE
+    assert call(wsp=wp + 8) == L.MIL_E_ALIGN
+    assert call(lgp=ctypes.c_void_p(logits.data_ptr() + 1)) == L.MIL_E_ALIGN
+    assert c.phase() == L.PHASE_VERIFIED
+    assert call() == L.MIL_OK
+    assert c.phase() == L.PHASE_READY
+    torch.cuda.synchronize()

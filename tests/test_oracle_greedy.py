@@ -1,0 +1,98 @@
+"""Pins of the oracle's greedy acceptance (oracle.greedy_accept) against things other than
+itself: an explicit scan on small inputs full of ties, and planted structures whose
+answer is known by construction.  Planted mistakes in a copy of the function must be
+caught by these checks."""
+from __future__ import annotations
+
+import inspect
+import textwrap
+
+import numpy as np
+import pytest
+
+import oracle
+from speculative_decode_amd import synth
+
+
+def scan_argmax(row):
+    """Brute force: walk the row, keep the first index of the largest value."""
+    best, bi = row[0], 0
+    for i in range(1, len(row)):
+        if row[i] > best:
+            best, bi = row[i], i
+    return bi
+
+
+def check_brute_force(fn):
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        batch, K, V = rng.integers(1, 4), rng.integers(1, 6), rng.integers(1, 9)
+        logits = rng.integers(-2, 3, size=(batch, K, V)).astype(np.float64)  # many ties
+        tokens = np.array([[scan_argmax(logits[b, k]) for k in range(K)] for b in range(batch)])
+        drafts = np.where(rng.random((batch, K)) < 0.7, tokens, rng.integers(0, V, size=(batch, K)))
+        j, t = fn(drafts, logits)
+        assert np.array_equal(t, tokens), trial
+        for b in range(batch):
+            lead = 0
+            while lead < K and drafts[b, lead] == tokens[b, lead]:
+                lead += 1
+            assert j[b] == lead, (trial, b)
+
+
+def check_planted(fn):
+    rng = np.random.default_rng(12)
+    for dtype in (synth.F32, synth.BF16):
+        for K in (1, 4, 8):
+            planted = rng.integers(0, K + 1, size=7).astype(np.int32)
+            planted[0], planted[1] = 0, K  # first draft rejected; every draft accepted
+            drafts, lg = synth.draw_greedy(rng, 7, K, 300, dtype, planted)
+            j, t = fn(drafts, lg.f64)
+            assert np.array_equal(j, planted), (dtype, K)
+            for b in range(7):
+                assert np.array_equal(t[b, :planted[b]], drafts[b, :planted[b]])
+
+
+def check_ties_lowest_index(fn):
+    # two equal maxima: the lower id wins, whichever side the draft is on
+    logits = np.zeros((2, 1, 10))
+    logits[:, 0, [3, 7]] = 5.0
+    j, t = fn(np.array([[3], [7]]), logits)
+    assert t.tolist() == [[3], [3]] and j.tolist() == [1, 0]
+
+
+CHECKS = [check_brute_force, check_planted, check_ties_lowest_index]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
+def test_greedy_oracle_pin(check):
+    check(oracle.greedy_accept)
+
+
+MUTANTS = [
+    ("ties go to the highest id", "tokens = np.argmax(lg, axis=2).astype(np.int32)",
+     "tokens = (lg.shape[2] - 1 - np.argmax(lg[:, :, ::-1], axis=2)).astype(np.int32)"),
+    ("every match counted, not the leading run",
+     "        while j < K and drafts[b, j] == tokens[b, j]:\n            j += 1",
+     "        j = int(np.sum(drafts[b] == tokens[b]))"),
+    ("last draft never accepted", "while j < K and drafts", "while j < K - 1 and drafts"),
+    ("draft compared with the next position", "drafts[b, j] == tokens[b, j]",
+     "drafts[b, j] == tokens[b, min(j + 1, K - 1)]"),
+    ("argmin instead of argmax", "np.argmax(lg, axis=2)", "np.argmin(lg, axis=2)"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MUTANTS)), ids=[m[0] for m in MUTANTS])
+def test_greedy_planted_mistakes_are_caught(i):
+    desc, old, new = MUTANTS[i]
+    src = textwrap.dedent(inspect.getsource(oracle.greedy_accept))
+    assert src.count(old) == 1, desc
+    ns = {"np": np}
+    exec(src.replace(old, new), ns)
+    mutant = ns["greedy_accept"]
+    caught = 0
+    for check in CHECKS:
+        try:
+            check(mutant)
+        except AssertionError:
+            caught += 1
+    assert caught > 0, desc
