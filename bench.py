@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
-KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit"]
+KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -102,9 +102,15 @@ def _to_dev_factory(torch, synth, dev):
 def step_kind(w):
     if w.name == "llama8b_long_prefill":
         return "prefill"
-    if w.name in ("llama8b_batched", "hybrid_decode"):
+    if w.name in ("llama8b_batched", "hybrid_decode", "llama8b_batched_greedy"):
         return "verify"
     return "full"
+
+
+def accept_work(w, batch, K):
+    """Greedy acceptance: every logit read once, drafts in, accepted lengths and tokens out."""
+    le = 2  # bf16 logits
+    return batch * K * w.vocab * le + batch * K * 4 * 2 + batch * 4, 0
 
 
 def run_gpu(args, w):
@@ -168,6 +174,8 @@ def run_gpu(args, w):
         else:
             ctx = np.full(Bt, w.L)
         state_bytes = Bt * w.H * w.N * w.P * 4
+        if w.accept == "greedy":
+            state_bytes += Bt * K * w.vocab * 2  # the logits are rotated with the caches
         R = args.rotate or (1 if nlayers > 1 else max(2, min(64, int(np.ceil(320e6 / state_bytes)))))
         proto = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
         for b in range(Bt):
@@ -176,19 +184,27 @@ def run_gpu(args, w):
                           chunk=128 if w.N > 128 else w.chunk, want_y=False)
         torch.cuda.synchronize()
         for r in range(R):
-            caches, drfs, js, jns, yvs = [], [], [], [], []
+            caches, drfs, js, jns, yvs, greedy = [], [], [], [], [], []
             for li in range(nlayers):
                 c = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
                 c.buffer.copy_(proto.buffer)
                 drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
                 j = (synth.draw_accept_geometric(rng, Bt, K) if w.accept == "geometric"
                      else synth.draw_accept_uniform(rng, Bt, K))
+                if w.accept == "greedy":
+                    # logits planted so that greedy verification accepts j[b] drafts
+                    dtok, lg = synth.draw_greedy(rng, Bt, K, w.vocab, synth.BF16, j)
+                    greedy.append(dict(dtok=torch.from_numpy(dtok).to(dev), logits=to_dev(lg),
+                                       acc=torch.empty(Bt, dtype=torch.int32, device=dev),
+                                       ws=torch.empty(c.greedy_workspace_bytes(K, w.vocab) + 256,
+                                                      dtype=torch.uint8, device=dev)))
+                    del lg
                 caches.append(c)
                 drfs.append([to_dev(t) for t in (drf.x, drf.B, drf.C, drf.dt)])
                 js.append(torch.from_numpy(j).to(dev))
                 jns.append(j)
                 yvs.append(torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev))
-            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs))
+            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy))
         del proto
         torch.cuda.synchronize()
     R = len(sets)
@@ -203,7 +219,11 @@ def run_gpu(args, w):
             for li, c in enumerate(st["caches"]):
                 dx, dB, dC, ddt = st["drf"][li]
                 c.verify(dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
-                c.commit(st["j"][li], dx, dB, ddt)
+                if st.get("greedy"):
+                    gr = st["greedy"][li]
+                    c.commit_greedy(gr["dtok"], gr["logits"], dx, dB, ddt, accepted=gr["acc"], ws=gr["ws"])
+                else:
+                    c.commit(st["j"][li], dx, dB, ddt)
 
     def set_trace(s, name):
         st = sets[s % R]
@@ -216,7 +236,9 @@ def run_gpu(args, w):
             lib.mil_ssm_cache_trace(ctypes.byref(st["caches"][0].desc), L.TRACE[name],
                                     ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event))
 
-    kernels = {"full": KERNELS, "prefill": KERNELS[:3], "verify": KERNELS[3:]}[kind]
+    kernels = {"full": KERNELS[:5], "prefill": KERNELS[:3], "verify": KERNELS[3:5]}[kind]
+    if w.accept == "greedy":
+        kernels = kernels + ["accept"]
     n_ev = max(args.steps, args.warmup, len(kernels) * 4)
     evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in ("beg", "mid", "end", "ta", "tb")}
     for e in evs["ta"] + evs["tb"]:
@@ -269,6 +291,8 @@ def run_gpu(args, w):
         else:
             work["verify"] = verify_work(w, Bt, K, float(jall.mean()), float((jall > 0).mean()))
         work["commit"] = commit_work(w, [float(jall.mean())] * Bt)
+        if w.accept == "greedy":
+            work["accept"] = accept_work(w, Bt, K)
     return dict(R=R, kind=kind, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant,
                 dom_ms=dom_ms, ktime=ktime, work=work, device=torch.cuda.get_device_name(dev))
 
@@ -316,7 +340,7 @@ def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
 
 KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
     "prefill_state": "chunk_state_", "prefill_pass": "state_pass", "prefill_out": "chunk_out_",
-    "verify": "ssm_verify_kernel", "commit": "ssm_commit_kernel", "copy": "elementwise",
+    "verify": "ssm_verify_kernel", "commit": "_commit_kernel", "accept": "greedy_argmax", "copy": "elementwise",
 }
 
 
@@ -456,9 +480,12 @@ def main():
     cfg = {"workload": w.name, "batch": Bt, "heads": w.H, "headdim": w.P, "dstate": w.N, "groups": w.G,
            "layers": w.layers, "chunk": w.chunk, "rotating_sets": g["R"], "parallelism": "single GPU",
            "step": {"full": f"prefill {L} + verify {K} + commit", "prefill": f"prefill {L}",
-                    "verify": f"{w.layers} x (verify {K} + commit)"}[kind]}
+                    "verify": f"{w.layers} x (verify {K} + " + ("greedy commit)" if w.accept == "greedy"
+                                                                       else "commit)")}[kind]}
     if kind != "prefill":
-        cfg.update({"drafts_K": K, "accept": "j ~ min(Geom(0.3)-1, K)" if w.accept == "geometric" else "j ~ U{0..K}"})
+        cfg.update({"drafts_K": K, "accept": {"geometric": "j ~ min(Geom(0.3)-1, K)", "uniform": "j ~ U{0..K}",
+                                              "greedy": f"greedy on the device, bf16 logits over {w.vocab} tokens "
+                                                        "planted for j ~ U{0..K}"}[w.accept]})
     if kind != "verify":
         cfg["prefill_len"] = L
     if w.ctx_range:

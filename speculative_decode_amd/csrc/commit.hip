@@ -82,9 +82,11 @@ __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
 // compare-only work: exact.
 constexpr int kGreedySplitsMax = 64;
 
-__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {
+__device__ __forceinline__ uint32_t ordered(float v) {  // monotonic in v
     const uint32_t u = __float_as_uint(v);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // monotonic in v
+    return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t argmax_key(uint32_t o, uint32_t idx) {
     return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - idx);
 }
 __device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) { return a > b ? a : b; }
@@ -127,21 +129,45 @@ __global__ __launch_bounds__(256) void greedy_argmax_kernel(const ArgmaxParams p
     const int s = blockIdx.x, k = blockIdx.y, b = blockIdx.z;
     const T *row = static_cast<const T *>(p.logits) + ((int64_t)b * p.K + k) * p.vocab;
     const int64_t lo = (int64_t)s * p.chunk, hi = min(lo + p.chunk, p.vocab);
-    uint64_t best = 0;
+    // this thread's largest value (order-preserving bits) and its index; each thread walks
+    // its indices upwards and keeps a value only when strictly larger, so the lowest index
+    // of equal values stays
+    uint32_t bo = 0, bi = 0xFFFFFFFFu;
     int64_t tail = lo;
     if (p.vec) {
         constexpr int E = 16 / sizeof(T);  // lo is a multiple of 8, so of E
+        constexpr int U = 4;               // 16-byte loads in flight per thread
+        const uint4 *row4 = reinterpret_cast<const uint4 *>(row);
         const int64_t v0 = lo / E, v1 = hi / E;
-        for (int64_t i = v0 + threadIdx.x; i < v1; i += 256) {
-            const uint4 w = reinterpret_cast<const uint4 *>(row)[i];
+        for (int64_t base = v0 + threadIdx.x; base < v1; base += 256 * U) {
+            uint4 w[U];
 #pragma unroll
-            for (int q = 0; q < E; ++q)
-                best = kmax(best, argmax_key(element(w, q, static_cast<const T *>(nullptr)), (uint32_t)(i * E + q)));
+            for (int u = 0; u < U; ++u) w[u] = row4[min(base + u * 256, v1 - 1)];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = base + u * 256;
+                if (i < v1) {
+#pragma unroll
+                    for (int q = 0; q < E; ++q) {
+                        const uint32_t o = ordered(element(w[u], q, static_cast<const T *>(nullptr)));
+                        if (o > bo) {
+                            bo = o;
+                            bi = (uint32_t)(i * E + q);
+                        }
+                    }
+                }
+            }
         }
         tail = v1 * E;
     }
-    for (int64_t i = tail + threadIdx.x; i < hi; i += 256) best = kmax(best, argmax_key(logit(row[i]), (uint32_t)i));
-    best = block_max_key(best, sred);
+    for (int64_t i = tail + threadIdx.x; i < hi; i += 256) {
+        const uint32_t o = ordered(logit(row[i]));
+        if (o > bo) {
+            bo = o;
+            bi = (uint32_t)i;
+        }
+    }
+    const uint64_t best = block_max_key(argmax_key(bo, bi), sred);
     if (threadIdx.x == 0) p.part[((int64_t)b * p.K + k) * p.S + s] = best;
 }
 

@@ -176,7 +176,8 @@ class Workload:
     ctx_range: tuple = () # (lo, hi) inclusive per-sequence prefill lengths
     chunk: int = 256
     layers: int = 1
-    accept: str = "uniform"  # or "geometric"
+    accept: str = "uniform"  # or "geometric", or "greedy" (decided on the device from verifier logits)
+    vocab: int = 0           # vocabulary size of the verifier logits ("greedy")
     seed: int = 1000
 
 
@@ -190,6 +191,11 @@ WORKLOADS = {
     # batched verify: 16 sequences with prior contexts U{256..4096}
     "llama8b_batched": Workload("llama8b_batched", batch=16, H=32, P=128, N=128, G=8,
                                 dtype=BF16, K=8, ctx_range=(256, 4096), seed=1003),
+    # the batched round with its acceptance decided on the device: greedy verification
+    # against bf16 verifier logits over the Llama-3 vocabulary (128256 tokens)
+    "llama8b_batched_greedy": Workload("llama8b_batched_greedy", batch=16, H=32, P=128, N=128, G=8,
+                                       dtype=BF16, K=8, ctx_range=(256, 4096), accept="greedy",
+                                       vocab=128256, seed=1006),
     # one long prefill scan
     "llama8b_long_prefill": Workload("llama8b_long_prefill", batch=1, H=32, P=128, N=128, G=8,
                                      dtype=BF16, L=8192, chunk=256, seed=1004),
