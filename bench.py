@@ -209,12 +209,13 @@ def run_gpu(args, w):
         torch.cuda.synchronize()
     R = len(sets)
 
-    def step(s):
+    def step(s, mark=True):
         st = sets[s % R]
         if kind in ("full", "prefill"):
             x, B, C, dt = st["pre"]
             st["caches"][0].prefill(x, B, C, dt, *AD[0], y=st["y"], chunk=w.chunk, ws=st["ws"])
-        evs["mid"][s].record()
+        if mark:
+            evs["mid"][s].record()
         if kind in ("full", "verify"):
             for li, c in enumerate(st["caches"]):
                 dx, dB, dC, ddt = st["drf"][li]
@@ -260,22 +261,57 @@ def run_gpu(args, w):
         ktime[name] = float(np.mean([evs["ta"][i * 4 + r].elapsed_time(evs["tb"][i * 4 + r]) for r in range(4)]))
     dominant = max(ktime, key=ktime.get)
 
-    # timed region: K steps, the dominant kernel traced on every step
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        set_trace(s, dominant)
-        evs["beg"][s].record()
-        step(s)
-        evs["end"][s].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for s in range(args.steps):
-        set_trace(s, None)
-    pre_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["mid"][s]) for s in range(args.steps)]))
-    vc_ms = float(np.mean([evs["mid"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
-    step_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
-    dom_ms = float(np.mean([evs["ta"][s].elapsed_time(evs["tb"][s]) for s in range(args.steps)]))
+    eager_ms = None
+    if args.graph:
+        # verify rounds as HIP graphs: eager steps timed first for comparison, then each
+        # rotating set's whole step (every layer's verify + commit) captured once and
+        # replayed; the dominant kernel's time per launch is the traced one found above
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            evs["beg"][s].record()
+            step(s, mark=False)
+            evs["end"][s].record()
+        torch.cuda.synchronize()
+        eager_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(r, mark=False)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for s in range(args.warmup):
+            graphs[s % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            evs["beg"][s].record()
+            graphs[s % R].replay()
+            evs["end"][s].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = vc_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+        pre_ms = 0.0
+        dom_ms = ktime[dominant]
+    else:
+        # timed region: K steps, the dominant kernel traced on every step
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            set_trace(s, dominant)
+            evs["beg"][s].record()
+            step(s)
+            evs["end"][s].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for s in range(args.steps):
+            set_trace(s, None)
+        pre_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["mid"][s]) for s in range(args.steps)]))
+        vc_ms = float(np.mean([evs["mid"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+        step_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+        dom_ms = float(np.mean([evs["ta"][s].elapsed_time(evs["tb"][s]) for s in range(args.steps)]))
 
     # algorithmic work per launch of each kernel
     work = {}
@@ -294,7 +330,7 @@ def run_gpu(args, w):
         if w.accept == "greedy":
             work["accept"] = accept_work(w, Bt, K)
     return dict(R=R, kind=kind, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant,
-                dom_ms=dom_ms, ktime=ktime, work=work, device=torch.cuda.get_device_name(dev))
+                dom_ms=dom_ms, ktime=ktime, work=work, device=torch.cuda.get_device_name(dev), eager_ms=eager_ms)
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -407,6 +443,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="independent cache/input sets (0: enough for >320 MB)")
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk length (0: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="verify workloads: replay each round as a HIP graph (launches included in the time)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, time a plain elementwise copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="DB",
@@ -438,6 +476,8 @@ def main():
         import dataclasses
         w = dataclasses.replace(w, chunk=args.chunk)
     args.steps = max(1, args.steps)
+    if args.graph and step_kind(w) != "verify":
+        ap.error("--graph applies to the verify workloads (llama8b_batched, llama8b_batched_greedy, hybrid_decode)")
     g = run_gpu(args, w)
     kind = g["kind"]
 
@@ -490,6 +530,7 @@ def main():
         cfg["prefill_len"] = L
     if w.ctx_range:
         cfg["context"] = f"U{{{w.ctx_range[0]}..{w.ctx_range[1]}}} per sequence"
+    cfg["launch"] = "HIP graph per round (capture once, replay)" if g["eager_ms"] is not None else "eager"
     out = {
         "metric": "verified tokens/s + HBM GB/s (K-step SSM verify); prefill scan tokens/s",
         "n_gpus": 1,
@@ -513,6 +554,9 @@ def main():
         vb, _ = g["work"]["verify"]
         out["hbm_gbs"] = vb / (g["ktime"]["verify"] * 1e-3) / 1e9
         out["verify_commit_ms"] = g["vc_ms"]
+        if g["eager_ms"] is not None:
+            out["eager_step_ms"] = g["eager_ms"]
+            out["eager_tokens_per_s"] = Bt * K / (g["eager_ms"] * 1e-3)
         if kind == "full":
             out["prefill_tokens_per_s"] = Bt * L / (g["pre_ms"] * 1e-3)
             out["prefill_ms"] = g["pre_ms"]
