@@ -6,6 +6,10 @@ roll-back protocol of the QbitAI article's speculative-decoding walkthrough.
 Only `tests/`, `__graft_entry__.smoke()` and the bench's `cpu_baseline` leg
 may import this package.  It shares no code with the GPU library.
 
+Besides the recurrence (`scan`, `prefill`, `verify`, `commit`) it holds the two steps
+on either side of it: the input projections (`project`) and greedy acceptance
+(`greedy_accept`).
+
 All arrays are float64 numpy arrays in the token-row layouts
   x [batch][T][H][P], B and C [batch][T][G][N], dt [batch][T][H], A and D [H],
   state [batch][H][N][P], y [batch][T][H][P].
@@ -138,3 +142,33 @@ def greedy_accept(draft_tokens, logits):
             j += 1
         accepted[b] = j
     return accepted, tokens
+
+
+def softplus(z):
+    """log(1 + e^z) in float64 (numpy's logaddexp, which neither overflows for large z
+    nor loses the tail for very negative z)."""
+    return np.logaddexp(0.0, np.asarray(z, dtype=np.float64))
+
+
+def project(u, w_x, w_B, w_C, w_dt, dt_bias=None):
+    """The layer's per-token inputs from its input rows (the step before the recurrence).
+
+    "The Mamba in the Llama" builds the layer from an attention layer's own linear
+    projection weights (arXiv abstract, as on the chatpaper.ai and pith.science pages;
+    skycaiji.com summary, method paragraph: the modified Mamba is initialised from the
+    attention module).  Reading used here: x comes from the value projection, B from the
+    key projection, C from the query projection, and the step size from one more
+    projection per head through softplus (plus an optional per-head bias), so that dt > 0.
+
+    u [T][d]; w_x [H*P][d]; w_B, w_C [G*N][d]; w_dt [H][d]; dt_bias [H] or None; every
+    weight row is one output feature.  Returns float64 (x [T][H*P], B [T][G*N],
+    C [T][G*N], dt [T][H]) before any rounding to a storage type.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    x = u @ np.asarray(w_x, dtype=np.float64).T
+    B = u @ np.asarray(w_B, dtype=np.float64).T
+    C = u @ np.asarray(w_C, dtype=np.float64).T
+    z = u @ np.asarray(w_dt, dtype=np.float64).T
+    if dt_bias is not None:
+        z = z + np.asarray(dt_bias, dtype=np.float64)[None, :]
+    return x, B, C, softplus(z)
