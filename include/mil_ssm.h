@@ -207,6 +207,43 @@ int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_
                           const float *A, const float *D, void *ws, size_t ws_bytes,
                           uint32_t flags, mil_stream_t stream);
 
+/* ---- Input projections (the step before the layer) ----
+ *
+ * "The Mamba in the Llama" builds the layer out of an attention layer's own linear
+ * projection weights (arXiv abstract; skycaiji.com summary, method paragraph: the
+ * modified Mamba is initialised from the attention module).  Reading used here: the
+ * value projection gives x, the key projection B, the query projection C, and one more
+ * projection per head gives the step size through softplus, so that dt > 0:
+ *   x[t][h*P+p]  = sum_k u[t][k] w_x[h*P+p][k]
+ *   B[t][g*N+n]  = sum_k u[t][k] w_B[g*N+n][k]      C likewise with w_C
+ *   dt[t][h]     = softplus(sum_k u[t][k] w_dt[h][k] + dt_bias[h])
+ * for T input rows u of width d_model.  The outputs are laid out exactly as
+ * mil_ssm_verify / mil_ssm_prefill take them (x [T][H][P], B and C [T][G][N], dt [T][H],
+ * with T = batch*K or nseq*L rows), so they feed those calls directly.
+ *
+ * dims          H, P, N, G as for the cache (dims->batch is not used).
+ * T, d_model    rows and row width; d_model a multiple of 64, T >= 1.
+ * u             bf16 [T][d_model]; w_x bf16 [H*P][d_model]; w_B, w_C bf16 [G*N][d_model];
+ *               w_dt bf16 [H][d_model]: device pointers, 16-byte aligned, row-major (a
+ *               weight row is one output feature).  Each weight block must be under 2 GiB.
+ * dt_bias       fp32 [H] or NULL (no bias).
+ * out_dtype     MIL_BF16 or MIL_F32 for x, B, C, dt (products are summed in fp32; bf16
+ *               outputs are rounded to nearest even once, at the end).
+ * ws            caller-owned device workspace, 256-byte aligned, of at least
+ *               mil_ssm_project_workspace_bytes() bytes; may be NULL when that is 0.  It holds
+ *               fp32 partial sums when the d_model inputs are split over several
+ *               workgroups (few rows); they are added in a fixed order, so results are
+ *               reproducible.
+ * Returns MIL_E_INVALID (null pointer, bad size or dtype), MIL_E_UNSUPPORTED (d_model not
+ * a multiple of 64, a weight block over 2 GiB), MIL_E_WORKSPACE, MIL_E_ALIGN or MIL_E_HIP;
+ * nothing is enqueued on an error.  No cache is involved: it may run on any stream.
+ */
+size_t mil_ssm_project_workspace_bytes(const mil_ssm_dims *dims, int32_t T, int32_t d_model);
+int mil_ssm_project(const mil_ssm_dims *dims, int32_t T, int32_t d_model, const void *u,
+                    const void *w_x, const void *w_B, const void *w_C, const void *w_dt,
+                    const float *dt_bias, int32_t out_dtype, void *x, void *B, void *C, void *dt,
+                    void *ws, size_t ws_bytes, mil_stream_t stream);
+
 /* Synchronise `stream`, then report device-side errors: *bad_slot = first slot with
  * err != 0, or -1.  Returns MIL_OK, or MIL_E_INVALID when a slot has an error.
  * With clear != 0 the err words are zeroed afterwards. */

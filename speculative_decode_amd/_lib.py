@@ -25,7 +25,7 @@ EXPORTS = [
     "mil_status_string", "mil_ssm_supported", "mil_ssm_cache_layout", "mil_ssm_cache_bytes",
     "mil_ssm_cache_init", "mil_ssm_cache_attach", "mil_ssm_prefill_workspace_bytes", "mil_ssm_prefill", "mil_ssm_verify",
     "mil_ssm_commit", "mil_ssm_cache_status", "mil_ssm_cache_phase", "mil_ssm_cache_trace",
-    "mil_ssm_greedy_workspace_bytes", "mil_ssm_commit_greedy",
+    "mil_ssm_greedy_workspace_bytes", "mil_ssm_commit_greedy", "mil_ssm_project_workspace_bytes", "mil_ssm_project",
 ]
 TRACE = {"off": 0, "verify": 1, "fold": 2, "commit": 3, "prefill_state": 4, "prefill_pass": 5, "prefill_out": 6,
          "accept": 7}
@@ -84,6 +84,9 @@ def lib():
         "mil_ssm_greedy_workspace_bytes": ([dims_p, i32, i32], sz),
         "mil_ssm_commit_greedy": ([cache_p, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
                                   ctypes.c_int),
+        "mil_ssm_project_workspace_bytes": ([dims_p, i32, i32], sz),
+        "mil_ssm_project": ([dims_p, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
+                            ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         f = getattr(L, name)

@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libmil_ssm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "verify.hip", "verify_bf16.hip", "verify_f32.hip", "commit.hip", "prefill.hip", "prefill_mfma.hip"]
+SOURCES = ["api.hip", "verify.hip", "verify_bf16.hip", "verify_f32.hip", "commit.hip", "prefill.hip", "prefill_mfma.hip", "project.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -272,6 +272,33 @@ int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_
     return MIL_OK;
 }
 
+size_t mil_ssm_project_workspace_bytes(const mil_ssm_dims *d, int32_t T, int32_t d_model) {
+    if (check_dims(d) != MIL_OK || !project_supported(*d, T, d_model)) return 0;
+    return (size_t)project_workspace_bytes(*d, T, d_model);
+}
+
+int mil_ssm_project(const mil_ssm_dims *d, int32_t T, int32_t d_model, const void *u, const void *w_x,
+                    const void *w_B, const void *w_C, const void *w_dt, const float *dt_bias, int32_t out_dtype,
+                    void *x, void *B, void *C, void *dt, void *ws, size_t ws_bytes, mil_stream_t stream) {
+    int st = check_dims(d);
+    if (st != MIL_OK) return st;
+    if (check_dtype(out_dtype) != MIL_OK) return MIL_E_INVALID;
+    if (T < 1 || d_model < 1) return MIL_E_INVALID;
+    if (!u || !w_x || !w_B || !w_C || !w_dt || !x || !B || !C || !dt) return MIL_E_INVALID;
+    if (!project_supported(*d, T, d_model)) return MIL_E_UNSUPPORTED;
+    const int64_t need = project_workspace_bytes(*d, T, d_model);
+    if (need > 0 && (!ws || (int64_t)ws_bytes < need)) return MIL_E_WORKSPACE;
+    const int eb = elt_bytes(out_dtype);
+    if (!aligned(u, 16) || !aligned(w_x, 16) || !aligned(w_B, 16) || !aligned(w_C, 16) || !aligned(w_dt, 16) ||
+        (dt_bias && !aligned(dt_bias, 4)) || !aligned(x, eb) || !aligned(B, eb) || !aligned(C, eb) ||
+        !aligned(dt, eb) || (need > 0 && !aligned(ws, kAlign)))
+        return MIL_E_ALIGN;
+    const void *w[4] = {w_x, w_B, w_C, w_dt};
+    void *out[4] = {x, B, C, dt};
+    return hip_status(launch_project(*d, T, d_model, u, w, dt_bias, out_dtype == MIL_BF16, out, ws,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
 int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t clear, mil_stream_t stream) {
     const CacheImpl *c = impl(cache);
     if (!c || !bad_slot) return MIL_E_INVALID;

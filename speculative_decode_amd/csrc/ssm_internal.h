@@ -85,4 +85,11 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
                                const void *B, const void *C, const void *dt, const float *A,
                                const float *D, float *y, void *ws, bool cont, hipStream_t s);
 
+// Input projections x, B, C, dt = softplus(.) of T rows of width d (one bf16 GEMM over four
+// weight blocks; fp32 partial sums in `ws` when the inputs are split over workgroups).
+bool project_supported(const mil_ssm_dims &d, int T, int dmodel);
+int64_t project_workspace_bytes(const mil_ssm_dims &d, int T, int dmodel);
+hipError_t launch_project(const mil_ssm_dims &d, int T, int dmodel, const void *u, const void *const w[4],
+                          const float *bias, bool out_bf16, void *const out[4], void *ws, hipStream_t s);
+
 }  // namespace mil

@@ -214,3 +214,53 @@ class SSMCache:
                                            L.MIL_COMMIT_MATERIALIZE if materialize else 0, _stream(self.device))
         L.check(st, "mil_ssm_commit_greedy")
         return accepted, tokens
+
+
+def project_workspace_bytes(H, P, N, G, T, d_model) -> int:
+    d = L.Dims(1, H, P, N, G)
+    return int(L.lib().mil_ssm_project_workspace_bytes(ctypes.byref(d), T, d_model))
+
+
+def project(u, w_x, w_B, w_C, w_dt, H, P, N, G, dt_bias=None, out_dtype=torch.bfloat16, out=None, ws=None):
+    """Input projections of the layer (mil_ssm_project): u [..., d_model] bf16 and the four
+    bf16 weight blocks w_x [H*P][d], w_B and w_C [G*N][d], w_dt [H][d].  Returns
+    (x [..., H, P], B [..., G, N], C [..., G, N], dt [..., H]) in out_dtype, the layouts
+    verify and prefill take; `out` may supply those four tensors."""
+    lead = tuple(u.shape[:-1])
+    d_model = int(u.shape[-1])
+    T = 1
+    for s in lead:
+        T *= int(s)
+    dev = u.device
+    want = {"w_x": (w_x, (H * P, d_model)), "w_B": (w_B, (G * N, d_model)), "w_C": (w_C, (G * N, d_model)),
+            "w_dt": (w_dt, (H, d_model))}
+    for name, t in [("u", u)] + [(k, v[0]) for k, v in want.items()]:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != dev:
+            raise TypeError(f"project: {name} must be a contiguous bfloat16 tensor on {dev}")
+    for name, (t, shape) in want.items():
+        if tuple(t.shape) != shape:
+            raise ValueError(f"project: {name} has shape {tuple(t.shape)}, expected {shape}")
+    if dt_bias is not None and (dt_bias.dtype != torch.float32 or tuple(dt_bias.shape) != (H,)
+                                or not dt_bias.is_contiguous() or dt_bias.device != dev):
+        raise ValueError(f"project: dt_bias must be a contiguous float32 tensor of shape ({H},) on {dev}")
+    code = _dtype_code(out_dtype)
+    tdt = _TORCH[code]
+    shapes = [lead + (H, P), lead + (G, N), lead + (G, N), lead + (H,)]
+    if out is None:
+        out = [torch.empty(s, dtype=tdt, device=dev) for s in shapes]
+    for t, s in zip(out, shapes):
+        if tuple(t.shape) != s or t.dtype != tdt or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"project: an output tensor does not have shape {s} and dtype {tdt}")
+    dims = L.Dims(1, H, P, N, G)
+    need = int(L.lib().mil_ssm_project_workspace_bytes(ctypes.byref(dims), T, d_model))
+    wp, wbytes = None, 0
+    if need > 0:
+        if ws is None:
+            ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+        wp = ctypes.c_void_p((ws.data_ptr() + 255) // 256 * 256)
+        wbytes = ws.numel() - (wp.value - ws.data_ptr())
+    st = L.lib().mil_ssm_project(ctypes.byref(dims), T, d_model, _ptr(u), _ptr(w_x), _ptr(w_B), _ptr(w_C),
+                                 _ptr(w_dt), _ptr(dt_bias), code, _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                 _ptr(out[3]), wp, wbytes, _stream(dev))
+    L.check(st, "mil_ssm_project")
+    return tuple(out)

@@ -100,6 +100,45 @@ def draw_tokens(rng: np.random.Generator, batch: int, T: int, H: int, P: int, N:
                   quantize(softplus(z), dtype))
 
 
+@dataclasses.dataclass
+class Projection:
+    """Layer input rows and the four projection weight blocks (all bf16) plus the fp32
+    step-size bias, for the input step before the layer."""
+
+    u: Tensor      # [T][d]
+    w_x: Tensor    # [H*P][d]  value rows
+    w_B: Tensor    # [G*N][d]  key rows
+    w_C: Tensor    # [G*N][d]  query rows
+    w_dt: Tensor   # [H][d]
+    bias: Tensor   # [H] fp32
+
+
+def draw_projection(rng: np.random.Generator, T: int, d: int, H: int, P: int, N: int, G: int) -> Projection:
+    """Seeded stand-ins for trained weights (none are available): u ~ N(0, 1); the x, B, C
+    rows ~ N(0, 1/(16 d)) and the step-size rows ~ N(0, 1/(4 d)) with bias -1, so that the
+    projected values have about the per-token distributions of the recipe above
+    (N(0,1)/4, and softplus of N(-1, 0.5)).  Draw order: u, w_x, w_B, w_C, w_dt."""
+    u = rng.normal(0.0, 1.0, size=(T, d))
+    sx = 0.25 / math.sqrt(d)
+    w_x = rng.normal(0.0, sx, size=(H * P, d))
+    w_B = rng.normal(0.0, sx, size=(G * N, d))
+    w_C = rng.normal(0.0, sx, size=(G * N, d))
+    w_dt = rng.normal(0.0, 0.5 / math.sqrt(d), size=(H, d))
+    return Projection(quantize(u, BF16), quantize(w_x, BF16), quantize(w_B, BF16), quantize(w_C, BF16),
+                      quantize(w_dt, BF16), quantize(np.full(H, -1.0), F32))
+
+
+def integer_projection(rng: np.random.Generator, T: int, d: int, H: int, P: int, N: int, G: int,
+                       lo: int = -2, hi: int = 2) -> Projection:
+    """Small integers (exact in bf16, and every sum of products exact in fp32 while
+    d * max|u| * max|w| < 2^24), no bias."""
+    def ints(shape):
+        return rng.integers(lo, hi + 1, size=shape).astype(np.float64)
+    return Projection(quantize(ints((T, d)), BF16), quantize(ints((H * P, d)), BF16),
+                      quantize(ints((G * N, d)), BF16), quantize(ints((G * N, d)), BF16),
+                      quantize(ints((H, d)), BF16), quantize(np.zeros(H), F32))
+
+
 def draw_accept_uniform(rng: np.random.Generator, batch: int, K: int) -> np.ndarray:
     """Accepted lengths j ~ U{0..K} (inclusive), int32."""
     return rng.integers(0, K + 1, size=batch).astype(np.int32)

@@ -225,3 +225,39 @@ def test_commit_greedy_checks(lib):
     assert call() == L.MIL_E_ORDER  # no verify before it (the checks after a verify are GPU tests)
     assert call(cache=L.CacheDesc()) == L.MIL_E_INVALID  # never initialised
     assert lib.mil_ssm_cache_phase(ctypes.byref(c)) == L.PHASE_READY
+
+
+def test_project_workspace_bytes(lib):
+    d = dims(batch=1, H=32, P=128, N=128, G=8)
+    ncols = 32 * 128 + 2 * 8 * 128 + 32
+    # a decode round's rows (few): the inputs are split, so partial sums need room
+    w = lib.mil_ssm_project_workspace_bytes(ctypes.byref(d), 128, 4096)
+    assert w >= 2 * 128 * ncols * 4 and w % 256 == 0
+    assert lib.mil_ssm_project_workspace_bytes(ctypes.byref(d), 4, 4096) >= 2 * 4 * ncols * 4
+    # a long prompt fills the GPU without a split: no workspace
+    assert lib.mil_ssm_project_workspace_bytes(ctypes.byref(d), 8192, 4096) == 0
+    # unsupported widths and bad sizes report 0
+    assert lib.mil_ssm_project_workspace_bytes(ctypes.byref(d), 128, 100) == 0
+    assert lib.mil_ssm_project_workspace_bytes(ctypes.byref(d), 0, 4096) == 0
+
+
+def test_project_argument_checks(lib):
+    d = dims(batch=1, H=32, P=128, N=128, G=8)
+    f = lib.mil_ssm_project
+    need = lib.mil_ssm_project_workspace_bytes(ctypes.byref(d), 128, 4096)
+
+    def call(dd=d, T=128, dm=4096, u=P(), wx=P(), bias=None, odt=L.MIL_BF16, x=P(), ws=P(), ws_bytes=need):
+        return f(ctypes.byref(dd), T, dm, u, wx, P(), P(), P(), bias, odt, x, P(), P(), P(), ws, ws_bytes, None)
+
+    assert call(u=None) == L.MIL_E_INVALID
+    assert call(wx=None) == L.MIL_E_INVALID
+    assert call(x=None) == L.MIL_E_INVALID
+    assert call(T=0) == L.MIL_E_INVALID
+    assert call(odt=7) == L.MIL_E_INVALID
+    assert call(dm=100) == L.MIL_E_UNSUPPORTED
+    assert call(ws=None) == L.MIL_E_WORKSPACE
+    assert call(ws_bytes=need - 1) == L.MIL_E_WORKSPACE
+    assert call(u=P(8)) == L.MIL_E_ALIGN
+    assert call(x=P(1)) == L.MIL_E_ALIGN
+    assert call(bias=P(2)) == L.MIL_E_ALIGN
+    assert call(dd=dims(batch=1, H=3, P=128, N=128, G=2)) == L.MIL_E_INVALID  # H % G != 0
