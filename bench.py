@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
-KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept"]
+KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept", "project"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -102,7 +102,7 @@ def _to_dev_factory(torch, synth, dev):
 def step_kind(w):
     if w.name == "llama8b_long_prefill":
         return "prefill"
-    if w.name in ("llama8b_batched", "hybrid_decode", "llama8b_batched_greedy"):
+    if w.name in ("llama8b_batched", "hybrid_decode", "llama8b_batched_greedy", "llama8b_batched_project"):
         return "verify"
     return "full"
 
@@ -111,6 +111,13 @@ def accept_work(w, batch, K):
     """Greedy acceptance: every logit read once, drafts in, accepted lengths and tokens out."""
     le = 2  # bf16 logits
     return batch * K * w.vocab * le + batch * K * 4 * 2 + batch * 4, 0
+
+
+def project_work(w, T):
+    """Input projections of T rows: every weight element and input row read once, the
+    projected x, B, C, dt written once (bf16); 2 flops per weight element per row."""
+    cols = w.H * w.P + 2 * w.G * w.N + w.H
+    return cols * w.d_model * 2 + T * w.d_model * 2 + T * cols * 2 + w.H * 4, 2 * T * cols * w.d_model
 
 
 def run_gpu(args, w):
@@ -123,7 +130,7 @@ def run_gpu(args, w):
 
     from speculative_decode_amd import _lib as L
     from speculative_decode_amd import synth
-    from speculative_decode_amd.ssm import SSMCache
+    from speculative_decode_amd.ssm import SSMCache, project, project_workspace_bytes
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -176,6 +183,8 @@ def run_gpu(args, w):
         state_bytes = Bt * w.H * w.N * w.P * 4
         if w.accept == "greedy":
             state_bytes += Bt * K * w.vocab * 2  # the logits are rotated with the caches
+        if w.d_model:
+            state_bytes += project_work(w, Bt * K)[0]  # and so are the projection weights
         R = args.rotate or (1 if nlayers > 1 else max(2, min(64, int(np.ceil(320e6 / state_bytes)))))
         proto = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
         for b in range(Bt):
@@ -184,7 +193,7 @@ def run_gpu(args, w):
                           chunk=128 if w.N > 128 else w.chunk, want_y=False)
         torch.cuda.synchronize()
         for r in range(R):
-            caches, drfs, js, jns, yvs, greedy = [], [], [], [], [], []
+            caches, drfs, js, jns, yvs, greedy, proj = [], [], [], [], [], [], []
             for li in range(nlayers):
                 c = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
                 c.buffer.copy_(proto.buffer)
@@ -199,12 +208,20 @@ def run_gpu(args, w):
                                        ws=torch.empty(c.greedy_workspace_bytes(K, w.vocab) + 256,
                                                       dtype=torch.uint8, device=dev)))
                     del lg
+                if w.d_model:
+                    # the drafts come from input rows through this set's own weights
+                    pr = synth.draw_projection(rng, Bt * K, w.d_model, w.H, w.P, w.N, w.G)
+                    wsb = project_workspace_bytes(w.H, w.P, w.N, w.G, Bt * K, w.d_model)
+                    proj.append(dict(u=to_dev(pr.u).view(Bt, K, w.d_model),
+                                     w=[to_dev(t) for t in (pr.w_x, pr.w_B, pr.w_C, pr.w_dt)], bias=to_dev(pr.bias),
+                                     ws=torch.empty(wsb + 256, dtype=torch.uint8, device=dev)))
+                    del pr
                 caches.append(c)
                 drfs.append([to_dev(t) for t in (drf.x, drf.B, drf.C, drf.dt)])
                 js.append(torch.from_numpy(j).to(dev))
                 jns.append(j)
                 yvs.append(torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev))
-            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy))
+            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy, proj=proj))
         del proto
         torch.cuda.synchronize()
     R = len(sets)
@@ -219,6 +236,16 @@ def run_gpu(args, w):
         if kind in ("full", "verify"):
             for li, c in enumerate(st["caches"]):
                 dx, dB, dC, ddt = st["drf"][li]
+                if st.get("proj"):
+                    # the drafts' x, B, C, dt projected from the input rows into the same buffers
+                    pj = st["proj"][li]
+                    tr = mark and li == 0 and trace_project[0]
+                    if tr:
+                        evs["ta"][s].record()
+                    project(pj["u"], *pj["w"], w.H, w.P, w.N, w.G, dt_bias=pj["bias"], out=(dx, dB, dC, ddt),
+                            ws=pj["ws"])
+                    if tr:
+                        evs["tb"][s].record()
                 c.verify(dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
                 if st.get("greedy"):
                     gr = st["greedy"][li]
@@ -226,8 +253,13 @@ def run_gpu(args, w):
                 else:
                     c.commit(st["j"][li], dx, dB, ddt)
 
+    trace_project = [False]  # the projection is traced with events on torch's stream, around the call
+
     def set_trace(s, name):
         st = sets[s % R]
+        trace_project[0] = name == "project"
+        if name == "project":
+            return
         for c in st["caches"]:
             if name is None:
                 lib.mil_ssm_cache_trace(ctypes.byref(c.desc), 0, None, None)
@@ -240,6 +272,8 @@ def run_gpu(args, w):
     kernels = {"full": KERNELS[:5], "prefill": KERNELS[:3], "verify": KERNELS[3:5]}[kind]
     if w.accept == "greedy":
         kernels = kernels + ["accept"]
+    if w.d_model:
+        kernels = kernels + ["project"]
     n_ev = max(args.steps, args.warmup, len(kernels) * 4)
     evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in ("beg", "mid", "end", "ta", "tb")}
     for e in evs["ta"] + evs["tb"]:
@@ -329,6 +363,8 @@ def run_gpu(args, w):
         work["commit"] = commit_work(w, [float(jall.mean())] * Bt)
         if w.accept == "greedy":
             work["accept"] = accept_work(w, Bt, K)
+        if w.d_model:
+            work["project"] = project_work(w, Bt * K)
     return dict(R=R, kind=kind, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant,
                 dom_ms=dom_ms, ktime=ktime, work=work, device=torch.cuda.get_device_name(dev), eager_ms=eager_ms)
 
@@ -376,7 +412,8 @@ def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
 
 KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
     "prefill_state": "chunk_state_", "prefill_pass": "state_pass", "prefill_out": "chunk_out_",
-    "verify": "ssm_verify_kernel", "commit": "_commit_kernel", "accept": "greedy_argmax", "copy": "elementwise",
+    "verify": "ssm_verify_kernel", "commit": "_commit_kernel", "accept": "greedy_argmax", "project": "project_",
+    "copy": "elementwise",
 }
 
 
@@ -468,7 +505,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the SSM path has no cross-GPU step in this build)", file=sys.stderr)
+              "(nothing in the SSM path runs across GPUs)", file=sys.stderr)
         sys.exit(2)
     from speculative_decode_amd import synth
     w = synth.WORKLOADS[args.workload]
@@ -477,7 +514,8 @@ def main():
         w = dataclasses.replace(w, chunk=args.chunk)
     args.steps = max(1, args.steps)
     if args.graph and step_kind(w) != "verify":
-        ap.error("--graph applies to the verify workloads (llama8b_batched, llama8b_batched_greedy, hybrid_decode)")
+        ap.error("--graph applies to the verify workloads (llama8b_batched, llama8b_batched_greedy, "
+                 "llama8b_batched_project, hybrid_decode)")
     g = run_gpu(args, w)
     kind = g["kind"]
 
@@ -520,8 +558,10 @@ def main():
     cfg = {"workload": w.name, "batch": Bt, "heads": w.H, "headdim": w.P, "dstate": w.N, "groups": w.G,
            "layers": w.layers, "chunk": w.chunk, "rotating_sets": g["R"], "parallelism": "single GPU",
            "step": {"full": f"prefill {L} + verify {K} + commit", "prefill": f"prefill {L}",
-                    "verify": f"{w.layers} x (verify {K} + " + ("greedy commit)" if w.accept == "greedy"
-                                                                       else "commit)")}[kind]}
+                    "verify": f"{w.layers} x (" + ("project + " if w.d_model else "") + f"verify {K} + "
+                              + ("greedy commit)" if w.accept == "greedy" else "commit)")}[kind]}
+    if w.d_model:
+        cfg["d_model"] = w.d_model
     if kind != "prefill":
         cfg.update({"drafts_K": K, "accept": {"geometric": "j ~ min(Geom(0.3)-1, K)", "uniform": "j ~ U{0..K}",
                                               "greedy": f"greedy on the device, bf16 logits over {w.vocab} tokens "

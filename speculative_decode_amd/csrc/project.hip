@@ -12,8 +12,8 @@
 // Work decomposition: a workgroup (4 waves) owns BM token rows x 128 output columns of one
 // block (a column tile never straddles two blocks) and a slice of the d inputs.  Wave w
 // owns 32 columns; its lanes stream those weight rows from HBM straight into registers
-// (each weight element is read by one lane of one workgroup, non-temporal), kDepth blocks
-// of 64 inputs ahead of the products.  The u rows go through LDS, shared by the 4 waves.  For few token rows (a decode round) the d inputs
+// (each weight element is read by one lane of one workgroup), kDepth blocks of 64 inputs
+// ahead of the products.  The u rows go through LDS, shared by the 4 waves.  For few token rows (a decode round) the d inputs
 // are split over S workgroups so that every CU streams weights; each writes fp32 partial
 // sums and a second kernel adds the S partials in a fixed order, so the result does not
 // depend on scheduling.
@@ -39,7 +39,7 @@ constexpr int kBN = 128;     // output columns per workgroup (4 waves x 32)
 constexpr int kKB = 64;      // inputs per block
 constexpr int kDepth = 4;    // weight blocks in flight per lane
 constexpr int kUS = kKB + 8; // padded LDS row of u (elements)
-constexpr int kWgTarget = 384;
+constexpr int kWgTarget = 192;  // about one 4-wave workgroup per CU (more splits measured slower)
 
 struct ProjParams {
     const uint16_t *u;           // [T][d] bf16
@@ -54,10 +54,12 @@ struct ProjParams {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
-// weights are read once: non-temporal (cache-policy bit 1 on gfx94x / gfx950)
-// (16-byte values are kept as ext_vector_type: arrays of them stay in registers)
+// Weight loads use the default cache policy: a lane's four loads of one block touch the
+// same 128-byte lines, which the later three find in the vector L1 (with the non-temporal
+// policy they were fetched again, measured 1.3-1.5x slower).  16-byte values are kept as
+// ext_vector_type: arrays of them stay in registers.
 __device__ __forceinline__ i32x4v wload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4v v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256) void project_reduce(const ProjParams p) {
     }
 }
 
-int block_m(int T) { return T > 64 ? 128 : T > 32 ? 64 : 32; }
+int block_m(int T) { return T > 128 ? 128 : T > 32 ? 64 : 32; }
 
 struct Plan {
     int BM, S, nkb, ntiles, ncols;

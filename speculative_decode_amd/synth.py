@@ -217,6 +217,8 @@ class Workload:
     layers: int = 1
     accept: str = "uniform"  # or "geometric", or "greedy" (decided on the device from verifier logits)
     vocab: int = 0           # vocabulary size of the verifier logits ("greedy")
+    d_model: int = 0         # > 0: the drafts' x, B, C, dt are projected on the device from
+                             # layer input rows of this width (the step before the layer)
     seed: int = 1000
 
 
@@ -235,6 +237,10 @@ WORKLOADS = {
     "llama8b_batched_greedy": Workload("llama8b_batched_greedy", batch=16, H=32, P=128, N=128, G=8,
                                        dtype=BF16, K=8, ctx_range=(256, 4096), accept="greedy",
                                        vocab=128256, seed=1006),
+    # the batched round from the layer's input rows: the drafts' x, B, C, dt projected on
+    # the device (Llama-3-8B width 4096; seeded stand-in weights) before verify and commit
+    "llama8b_batched_project": Workload("llama8b_batched_project", batch=16, H=32, P=128, N=128, G=8,
+                                        dtype=BF16, K=8, ctx_range=(256, 4096), d_model=4096, seed=1007),
     # one long prefill scan
     "llama8b_long_prefill": Workload("llama8b_long_prefill", batch=1, H=32, P=128, N=128, G=8,
                                      dtype=BF16, L=8192, chunk=256, seed=1004),
