@@ -7,8 +7,9 @@ Only `tests/`, `__graft_entry__.smoke()` and the bench's `cpu_baseline` leg
 may import this package.  It shares no code with the GPU library.
 
 Besides the recurrence (`scan`, `prefill`, `verify`, `commit`) it holds the two steps
-on either side of it: the input projections (`project`) and greedy acceptance
-(`greedy_accept`).
+on either side of it, the input projections (`project`) and greedy acceptance
+(`greedy_accept`), and the tree-draft forms of verify and commit (`verify_tree`,
+`commit_tree`).
 
 All arrays are float64 numpy arrays in the token-row layouts
   x [batch][T][H][P], B and C [batch][T][G][N], dt [batch][T][H], A and D [H],
@@ -172,3 +173,66 @@ def project(u, w_x, w_B, w_C, w_dt, dt_bias=None):
     if dt_bias is not None:
         z = z + np.asarray(dt_bias, dtype=np.float64)[None, :]
     return x, B, C, softplus(z)
+
+
+def tree_paths(parent):
+    """Root-first node list of every node of every sequence's draft tree.
+
+    Tree drafts (the pages name tree-organised candidates among speculative decoding
+    variants; skycaiji.com summary, related-work paragraph): K candidate tokens per
+    sequence, node k following node parent[b][k] (-1: the committed state itself), with
+    parents numbered before their children.  A node's path is the chain of tokens from the
+    committed state to it, which is what the recurrence must run through for that node.
+    """
+    par = np.asarray(parent)
+    batch, K = par.shape
+    paths = []
+    for b in range(batch):
+        row = []
+        for k in range(K):
+            p = int(par[b, k])
+            if p < -1 or p >= k:
+                raise ValueError("parent[b][k] must lie in -1..k-1")
+            row.append((row[p] if p >= 0 else []) + [k])
+        paths.append(row)
+    return paths
+
+
+def verify_tree(state, x, B, C, dt, A, D, parent, nthreads=None, lib=None):
+    """y[b][k] for every node of a draft tree: the plain recurrence run from a copy of the
+    committed state along node k's root path, read out at node k.  The state is left as
+    it was (every branch starts from the same cached state)."""
+    paths = tree_paths(parent)
+    batch, K = np.asarray(parent).shape
+    H, P = x.shape[2], x.shape[3]
+    y = np.zeros((batch, K, H, P))
+    for b in range(batch):
+        for k in range(K):
+            idx = paths[b][k]
+            yk = verify(state[b:b + 1], x[b:b + 1, idx], B[b:b + 1, idx], C[b:b + 1, idx], dt[b:b + 1, idx], A, D,
+                        nthreads=nthreads, lib=lib)
+            y[b, k] = yk[0, -1]
+    return y
+
+
+def commit_tree(state, x, B, dt, A, D, parent, accepted_node, nthreads=None, lib=None):
+    """State after the accepted branch: the tokens on the root path of accepted_node[b]
+    (-1: none accepted, state unchanged), in root-first order.  Returns (new state,
+    accepted path lengths)."""
+    paths = tree_paths(parent)
+    batch, K = np.asarray(parent).shape
+    acc = np.asarray(accepted_node, dtype=np.int64)
+    if np.any(acc < -1) or np.any(acc >= K):
+        raise ValueError("accepted node outside -1..K-1")
+    out = np.array(state, dtype=np.float64, copy=True)
+    lengths = np.zeros(batch, dtype=np.int32)
+    for b in range(batch):
+        if acc[b] < 0:
+            continue
+        idx = paths[b][int(acc[b])]
+        lengths[b] = len(idx)
+        sub = out[b:b + 1].copy()
+        scan(x[b:b + 1, idx], B[b:b + 1, idx], None, dt[b:b + 1, idx], A, D, sub, want_y=False,
+             nthreads=nthreads, lib=lib)
+        out[b] = sub[0]
+    return out, lengths
