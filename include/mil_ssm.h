@@ -79,7 +79,8 @@ typedef struct {
  *           (cache dtype): accepted draft tokens not yet folded into `state`.
  *   pos     int32 [batch]: tokens the sequence has absorbed (prefill + accepted drafts).
  *   pending int32 [batch]: how many rows of pend_* are accepted but not yet folded in.
- *   err     int32 [batch]: 0, or MIL_DEVERR_ACCEPT after an out-of-range accepted length.
+ *   err     int32 [batch]: 0, or the OR of MIL_DEVERR_ACCEPT (an out-of-range accepted
+ *           length or node) and MIL_DEVERR_TREE (a tree link outside -1..k-1).
  * The logical state of slot b is `state` advanced through its `pending` rows.
  */
 typedef struct {
@@ -90,6 +91,7 @@ typedef struct {
 } mil_ssm_layout;
 
 #define MIL_DEVERR_ACCEPT 1
+#define MIL_DEVERR_TREE 2      /* a tree link outside -1..k-1 (verify_tree / commit_tree) */
 
 /* Host-side cache descriptor.  The caller provides the storage; mil_ssm_cache_init
  * fills it.  It holds the device buffer address, the shape and the protocol phase. */
@@ -206,6 +208,34 @@ int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_
                           const void *x, const void *B, const void *dt,
                           const float *A, const float *D, void *ws, size_t ws_bytes,
                           uint32_t flags, mil_stream_t stream);
+
+/* ---- Tree drafts ----
+ *
+ * Speculative decoding with tree-organised candidates (named among the variants in the
+ * skycaiji.com summary, related-work paragraph): the K drafts of a sequence form a tree,
+ * draft k following draft parent[b][k] instead of draft k-1, parent -1 meaning the
+ * committed state itself; parents are numbered before their children (parent[b][k] in
+ * -1..k-1).  Every branch starts from the same cached state, which is read once.
+ *
+ * mil_ssm_verify_tree: as mil_ssm_verify, with y[b][k] the output at draft k after the
+ *   recurrence has run over k's root path (the drafts from the state to k, root first).
+ *   A chain (parent[b][k] = k-1) gives exactly mil_ssm_verify's results, and draft k's
+ *   output is bit-identical to a chain verify of its path's tokens.  A link outside
+ *   -1..k-1 is taken as -1 and reported as MIL_DEVERR_TREE in err[b].
+ * mil_ssm_commit_tree: as mil_ssm_commit, with the accepted branch given as one node,
+ *   accepted_node[b] in -1..K-1 (device int32; -1 accepts nothing): the tokens on its
+ *   root path, root first, are accepted (j = the path's length).  An out-of-range node
+ *   (MIL_DEVERR_ACCEPT) or a bad link on the path (MIL_DEVERR_TREE) sets err[b] and
+ *   leaves slot b's logical state and pos unchanged.
+ * parent   device int32 [batch][K], 4-byte aligned; the same array for both calls of a round.
+ * Everything else (buffers, order, K, flags) is as for mil_ssm_verify and mil_ssm_commit.
+ */
+int mil_ssm_verify_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent,
+                        const void *x, const void *B, const void *C, const void *dt,
+                        const float *A, const float *D, float *y, mil_stream_t stream);
+int mil_ssm_commit_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent,
+                        const int32_t *accepted_node, const void *x, const void *B, const void *dt,
+                        const float *A, const float *D, uint32_t flags, mil_stream_t stream);
 
 /* ---- Input projections (the step before the layer) ----
  *

@@ -17,6 +17,7 @@ MIL_F32, MIL_BF16 = 0, 1
 MIL_PREFILL_CONTINUE = 1
 MIL_COMMIT_MATERIALIZE = 1
 MIL_DEVERR_ACCEPT = 1
+MIL_DEVERR_TREE = 2
 MIL_KMAX_LIMIT = 16
 PHASE_UNINIT, PHASE_READY, PHASE_VERIFIED = 0, 1, 2
 
@@ -26,6 +27,7 @@ EXPORTS = [
     "mil_ssm_cache_init", "mil_ssm_cache_attach", "mil_ssm_prefill_workspace_bytes", "mil_ssm_prefill", "mil_ssm_verify",
     "mil_ssm_commit", "mil_ssm_cache_status", "mil_ssm_cache_phase", "mil_ssm_cache_trace",
     "mil_ssm_greedy_workspace_bytes", "mil_ssm_commit_greedy", "mil_ssm_project_workspace_bytes", "mil_ssm_project",
+    "mil_ssm_verify_tree", "mil_ssm_commit_tree",
 ]
 TRACE = {"off": 0, "verify": 1, "fold": 2, "commit": 3, "prefill_state": 4, "prefill_pass": 5, "prefill_out": 6,
          "accept": 7}
@@ -85,6 +87,8 @@ def lib():
         "mil_ssm_commit_greedy": ([cache_p, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
                                   ctypes.c_int),
         "mil_ssm_project_workspace_bytes": ([dims_p, i32, i32], sz),
+        "mil_ssm_verify_tree": ([cache_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "mil_ssm_commit_tree": ([cache_p, i32, vp, vp, vp, vp, vp, vp, vp, u32, vp], ctypes.c_int),
         "mil_ssm_project": ([dims_p, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
                             ctypes.c_int),
     }

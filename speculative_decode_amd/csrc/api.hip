@@ -234,6 +234,51 @@ int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, con
     return MIL_OK;
 }
 
+int mil_ssm_verify_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const void *x, const void *B,
+                        const void *C, const void *dt, const float *A, const float *D, float *y,
+                        mil_stream_t stream) {
+    CacheImpl *c = impl(cache);
+    if (!c) return MIL_E_INVALID;
+    if (c->phase != kReady) return MIL_E_ORDER;
+    if (K < 1 || K > c->k_max) return MIL_E_INVALID;
+    if (!parent || !x || !B || !C || !dt || !A || !D || !y) return MIL_E_INVALID;
+    const int eb = elt_bytes(c->dtype);
+    if (!aligned(parent, 4) || !aligned(x, eb) || !aligned(B, eb) || !aligned(C, eb) || !aligned(dt, eb) ||
+        !aligned(A, 4) || !aligned(D, 4) || !aligned(y, 4))
+        return MIL_E_ALIGN;
+    hipError_t e = launch_verify(*c, K, x, B, C, dt, A, D, y, reinterpret_cast<hipStream_t>(stream), parent);
+    if (e != hipSuccess) return MIL_E_HIP;
+    c->phase = kVerified;
+    c->verified_k = K;
+    return MIL_OK;
+}
+
+int mil_ssm_commit_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const int32_t *accepted_node,
+                        const void *x, const void *B, const void *dt, const float *A, const float *D,
+                        uint32_t flags, mil_stream_t stream) {
+    CacheImpl *c = impl(cache);
+    if (!c) return MIL_E_INVALID;
+    if (c->phase != kVerified) return MIL_E_ORDER;
+    if (flags & ~MIL_COMMIT_MATERIALIZE) return MIL_E_INVALID;
+    if (K != c->verified_k) return MIL_E_INVALID;
+    if (!parent || !accepted_node || !x || !B || !dt) return MIL_E_INVALID;
+    const bool mat = (flags & MIL_COMMIT_MATERIALIZE) != 0;
+    if (mat && (!A || !D)) return MIL_E_INVALID;
+    const int eb = elt_bytes(c->dtype);
+    if (!aligned(parent, 4) || !aligned(accepted_node, 4) || !aligned(x, 4) || !aligned(B, 4) || !aligned(dt, eb))
+        return MIL_E_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch_commit_tree(*c, K, parent, accepted_node, x, B, dt, s);
+    if (e == hipSuccess && mat) {
+        e = launch_verify(*c, 0, nullptr, nullptr, nullptr, nullptr, A, D, nullptr, s);
+        if (e == hipSuccess) e = launch_clear_pending(*c, s);
+    }
+    if (e != hipSuccess) return MIL_E_HIP;
+    c->phase = kReady;
+    c->verified_k = 0;
+    return MIL_OK;
+}
+
 size_t mil_ssm_greedy_workspace_bytes(const mil_ssm_dims *d, int32_t K, int32_t vocab) {
     if (check_dims(d) != MIL_OK || K < 1 || K > MIL_KMAX_LIMIT || vocab < 1) return 0;
     return (size_t)greedy_workspace_bytes(d->batch, K);

@@ -66,6 +66,66 @@ __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
         reinterpret_cast<uint16_t *>(dd)[i] = reinterpret_cast<const uint16_t *>(ds)[i];
 }
 
+// ------------------------------------------------------------------ tree drafts
+// The commit of a tree round (tree-organised candidates; skycaiji.com summary,
+// related-work paragraph): the accepted branch is the root path of one node, and its
+// tokens, root first, become the pending rows, exactly as the j accepted drafts of a
+// chain do.  grid (K, batch): every workgroup of slot b walks the parent links up from
+// accepted_node[b] (at most K steps, each link checked to lie in -1..i-1); workgroup k
+// copies the path's k-th token row, workgroup 0 does the bookkeeping.  A node outside
+// -1..K-1 or a bad link on the path sets err[b] and pending = 0 and leaves pos alone.
+struct TreeCommitParams {
+    CommitParams c;
+    const int32_t *parent;         // [batch][K]
+    const int32_t *accepted_node;  // [batch]
+};
+
+template <typename V>
+__global__ __launch_bounds__(256) void ssm_commit_tree_kernel(const TreeCommitParams tp) {
+    const CommitParams &p = tp.c;
+    __shared__ int spath[MIL_KMAX_LIMIT];
+    __shared__ int sj, sbad;
+    const int k = blockIdx.x, b = blockIdx.y;
+    if (threadIdx.x == 0) {
+        const int a = tp.accepted_node[b];
+        int bad = (a < -1 || a >= p.K) ? MIL_DEVERR_ACCEPT : 0;
+        int depth = 0;
+        // first walk: the depth (links strictly decrease, so at most K steps)
+        for (int i = a; !bad && i >= 0; ++depth) {
+            const int q = tp.parent[(size_t)b * p.K + i];
+            if (q < -1 || q >= i) bad = MIL_DEVERR_TREE;
+            i = q;
+        }
+        // second walk: the path, root first
+        if (!bad)
+            for (int i = a, d = depth - 1; i >= 0; --d) {
+                spath[d] = i;
+                i = tp.parent[(size_t)b * p.K + i];
+            }
+        sj = bad ? 0 : depth;
+        sbad = bad;
+    }
+    __syncthreads();
+    const int j = sj;
+    if (k == 0 && threadIdx.x == 0) {
+        if (!sbad) {
+            p.pending[b] = j;
+            p.pos[b] += j;
+        } else {
+            p.err[b] = sbad;
+            p.pending[b] = 0;
+        }
+    }
+    if (k >= j) return;
+    const size_t src = (size_t)b * p.K + spath[k], dst = (size_t)b * p.k_max + k;
+    copy_row<V>(p.px + dst * p.x_row, p.x + src * p.x_row, p.x_row);
+    copy_row<V>(p.pB + dst * p.B_row, p.B + src * p.B_row, p.B_row);
+    const char *ds = p.dt + src * p.dt_row;
+    char *dd = p.pdt + dst * p.dt_row;
+    for (int i = threadIdx.x; i < p.dt_row / 2; i += blockDim.x)
+        reinterpret_cast<uint16_t *>(dd)[i] = reinterpret_cast<const uint16_t *>(ds)[i];
+}
+
 // ------------------------------------------------------------------ greedy acceptance
 // The same commit with the accepted lengths decided on the device (QbitAI walkthrough:
 // keep the drafts the verifier confirms, cut at the first one it rejects; read here as
@@ -258,6 +318,22 @@ CommitParams commit_params(const CacheImpl &c, int K, const int32_t *accepted, c
     return p;
 }
 }  // namespace
+
+hipError_t launch_commit_tree(const CacheImpl &c, int K, const int32_t *parent, const int32_t *accepted_node,
+                              const void *x, const void *B, const void *dt, hipStream_t s) {
+    TreeCommitParams tp;
+    tp.c = commit_params(c, K, nullptr, x, B, dt);
+    tp.parent = parent;
+    tp.accepted_node = accepted_node;
+    const bool v16 = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+    trace_begin(c, MIL_TRACE_COMMIT, s);
+    if (v16)
+        hipLaunchKernelGGL(ssm_commit_tree_kernel<uint4>, dim3(K, c.dims.batch), dim3(256), 0, s, tp);
+    else
+        hipLaunchKernelGGL(ssm_commit_tree_kernel<uint32_t>, dim3(K, c.dims.batch), dim3(256), 0, s, tp);
+    trace_end(c, MIL_TRACE_COMMIT, s);
+    return hipGetLastError();
+}
 
 hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, const void *x,
                          const void *B, const void *dt, hipStream_t s) {

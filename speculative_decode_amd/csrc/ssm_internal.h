@@ -53,8 +53,11 @@ hipError_t launch_fill_zero(void *p, int64_t words, hipStream_t s);
 
 // Fold every slot's pending rows into the stored state, then, when K > 0, emit y for
 // K drafts from that state.  K == 0 is the fold alone (x/B/C/dt/y unused).
+// With `parent` ([batch][K], -1..k-1), the drafts form a tree and each one's output runs
+// over its root path; null means a chain.
 hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B, const void *C,
-                         const void *dt, const float *A, const float *D, float *y, hipStream_t s);
+                         const void *dt, const float *A, const float *D, float *y, hipStream_t s,
+                         const int32_t *parent = nullptr);
 // A verify launch shape exists for these sizes (K drafts, up to kmax pending rows).
 bool verify_supported(int batch, int H, int P, int N, int K, int kmax);
 
@@ -62,6 +65,11 @@ bool verify_supported(int batch, int H, int P, int N, int K, int kmax);
 // set pending[b] = accepted[b], pos[b] += accepted[b]; a bad value sets err[b] and pending[b] = 0.
 hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, const void *x,
                          const void *B, const void *dt, hipStream_t s);
+
+// The commit of a tree round: the root path of accepted_node[b] (-1..K-1, -1 = none)
+// becomes the pending rows in root-first order; a bad node or parent link sets err[b].
+hipError_t launch_commit_tree(const CacheImpl &c, int K, const int32_t *parent, const int32_t *accepted_node,
+                              const void *x, const void *B, const void *dt, hipStream_t s);
 
 // pending[b] = 0 for every slot (after a fold that has consumed them).
 hipError_t launch_clear_pending(const CacheImpl &c, hipStream_t s);

@@ -8,7 +8,8 @@ bool verify_supported(int batch, int H, int P, int N, int K, int kmax) {
 }
 
 hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B, const void *C,
-                         const void *dt, const float *A, const float *D, float *y, hipStream_t s) {
+                         const void *dt, const float *A, const float *D, float *y, hipStream_t s,
+                         const int32_t *parent) {
     VerifyParams vp;
     vp.state = cache_state(c);
     vp.head_stride = c.lay.state_head_stride / 4;
@@ -31,6 +32,8 @@ hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B
     vp.k_max = c.k_max;
     vp.cs = 1;  // set by the launcher from the chosen shape
     vp.vec = (((uintptr_t)x | (uintptr_t)B | (uintptr_t)C) & 15) == 0;
+    vp.parent = parent;
+    vp.err = cache_err(c);
     const int batch = c.dims.batch;
     const int id = K > 0 ? MIL_TRACE_VERIFY : MIL_TRACE_FOLD;
     trace_begin(c, id, s);

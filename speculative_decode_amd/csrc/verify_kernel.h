@@ -17,6 +17,16 @@
 //   alpha_k = prod_{i<=k} abar_i,  beta_{k,s} = prod_{s<i<=k} abar_i,  abar_i = exp(dt_i A).
 // No draft token ever touches the stored state; a later commit decides which ones count.
 //
+// Tree drafts (the pages name tree-organised candidates among speculative-decoding
+// variants; skycaiji.com summary, related-work paragraph): with a parent array, draft k
+// follows draft parent[k] (-1: the folded state h0) instead of draft k-1, and the same
+// closed form runs over k's root path P(k) instead of 0..k:
+//   y_k = alpha_k (C_k^T h0) + sum_{s in P(k)} beta_{k,s} dt_s (C_k . B_s) x_s + D x_k,
+//   alpha_k = prod_{i in P(k)} abar_i,  beta_{k,s} = prod_{i in P(k), i > s} abar_i.
+// Every branch starts from the one state read; products run in ascending node order, so a
+// chain (parent[k] = k-1) is exactly the flat case and a node's output equals, bit for
+// bit, a flat verify of its path's tokens.
+//
 // Work decomposition (gfx950, wave64): one workgroup per (slot, head, column tile of
 // P/CS columns), S waves.  A lane owns 4 adjacent columns (16-byte loads) of ROWS
 // consecutive state rows; P/(4 CS) lanes cover a row tile, so a wave reads 64 * 16
@@ -79,6 +89,8 @@ struct VerifyParams {
     int H, P, N, G, K, k_max;
     int cs;   // column tiles per head
     int vec;  // draft x, B, C 16-byte aligned: token rows staged in 16-byte chunks
+    const int32_t *parent;  // [batch][K] tree links (-1..k-1), or null for a chain
+    int32_t *err;           // [batch] device error words (a bad parent link is reported)
 };
 
 // Launch shape: CS column tiles per head, S waves per workgroup, ROWS rows per lane.
@@ -91,7 +103,7 @@ constexpr int max_threads(int rows) { return rows >= 16 ? 512 : 1024; }
 
 // LDS floats of one workgroup covering Pc columns.
 inline size_t verify_lds_floats(int N, int Pc, int K, int kmax, int S) {
-    return (size_t)kmax * N + 2 * K * N + (size_t)kmax * Pc + K * Pc + 2 * kmax + 4 * K + K * K + (size_t)S * K * Pc;
+    return (size_t)kmax * N + 2 * K * N + (size_t)kmax * Pc + K * Pc + 2 * kmax + 5 * K + K * K + (size_t)S * K * Pc;
 }
 constexpr size_t kVerifyLdsMax = 160 * 1024;
 
@@ -141,6 +153,24 @@ __device__ __forceinline__ void put16(float *dst, const uint4 v, const float *) 
     *reinterpret_cast<uint4 *>(dst) = v;
 }
 
+// Draft k's root path as a bit mask (bit i: node i is on it), walking the parent links
+// up from k.  A link outside -1..i-1 ends the walk (the node is taken as a child of the
+// state) and is reported through *bad.
+__device__ __forceinline__ uint32_t path_mask(const int *par, int k, bool &bad) {
+    uint32_t m = 0;
+    int a = k;
+    while (a >= 0) {
+        m |= 1u << a;
+        const int q = par[a];
+        if (q < -1 || q >= a) {
+            bad = true;
+            break;
+        }
+        a = q;
+    }
+    return m;
+}
+
 template <typename T, int ROWS>
 __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const VerifyParams p) {
     extern __shared__ __align__(16) float lds[];
@@ -161,6 +191,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     float *sAlpha = sDdt + K;      // [K]        alpha_k
     float *sW = sAlpha + K;        // [K][K]     beta_{k,s} dt_s (C_k . B_s)
     float *sRed = sW + K * K;      // [S][K][Pc] per-wave partial C_k . h0
+    int *sPar = reinterpret_cast<int *>(sRed + S * K * Pc);  // [K] parent links
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c4 = lane % LPR, rsub = lane / LPR;
@@ -266,21 +297,27 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     if (tid < K) {
         sDdt[tid] = ddt;
         sDA[tid] = expf(ddt * Ah);
+        sPar[tid] = p.parent ? p.parent[(size_t)b * K + tid] : tid - 1;
     }
 
     __syncthreads();
 
-    // ---- per-draft scalars: alpha_k and w_{k,s}, eight lanes per (k, s) pair ----
+    // ---- per-draft scalars: alpha_k and w_{k,s}, eight lanes per (k, s) pair, over each
+    // draft's root path (all of 0..k for a chain) ----
+    bool bad = false;
     if (tid < K) {
+        const uint32_t pm = path_mask(sPar, tid, bad);
         float a = 1.f;
-        for (int i = 0; i <= tid; ++i) a *= sDA[i];
+        for (int i = 0; i <= tid; ++i)
+            if ((pm >> i) & 1u) a *= sDA[i];
         sAlpha[tid] = a;
     }
     for (int base = 0; base < K * K * 8; base += NT) {
         const int i = base + tid;
         const int pair = i >> 3, part = i & 7;
         const int k = pair / max(K, 1), s = pair - k * K;
-        const bool live = pair < K * K && s <= k;
+        const uint32_t pm = pair < K * K ? path_mask(sPar, k, bad) : 0u;
+        const bool live = pair < K * K && s <= k && ((pm >> s) & 1u);
         float dot = 0.f;
         if (live)
             for (int n = part; n < N; n += 8) dot = __builtin_fmaf(sDC[k * N + n], sDB[s * N + n], dot);
@@ -291,12 +328,15 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
             float w = 0.f;
             if (live) {
                 float beta = 1.f;
-                for (int j = s + 1; j <= k; ++j) beta *= sDA[j];
+                for (int j = s + 1; j <= k; ++j)
+                    if ((pm >> j) & 1u) beta *= sDA[j];
                 w = beta * sDdt[s] * dot;
             }
             sW[k * K + s] = w;
         }
     }
+
+    if (bad && p.err) atomicOr(p.err + b, MIL_DEVERR_TREE);
 
     // ---- fold the m pending rows, token by token ----
     for (int s = 0; s < m; ++s) {

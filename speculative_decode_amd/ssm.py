@@ -178,6 +178,39 @@ class SSMCache:
                                     _stream(self.device))
         L.check(st, "mil_ssm_commit")
 
+    def _check_int_rows(self, what, t, shape):
+        if t.dtype != torch.int32 or t.device != self.device:
+            raise TypeError(f"{what} must be an int32 tensor on the cache's device")
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous tensor of shape {shape}")
+
+    def verify_tree(self, parent, x, B, C, dt, A, D, y=None):
+        """Outputs y [batch][K][H][P] for a tree of K drafts per slot: parent [batch][K]
+        int32 (-1..k-1, -1 = the committed state); draft k's output runs over its root path."""
+        K = x.shape[1]
+        self._check_tokens("verify_tree", x, B, C, dt)
+        self._check_int_rows("verify_tree: parent", parent, (self.batch, K))
+        if y is None:
+            y = torch.empty((self.batch, K, self.H, self.P), dtype=torch.float32, device=self.device)
+        self._check_shapes("verify_tree", self.batch, K, x, B, C, dt, A, D, y)
+        st = L.lib().mil_ssm_verify_tree(ctypes.byref(self.desc), K, _ptr(parent), _ptr(x), _ptr(B), _ptr(C),
+                                         _ptr(dt), _ptr(A), _ptr(D), _ptr(y), _stream(self.device))
+        L.check(st, "mil_ssm_verify_tree")
+        return y
+
+    def commit_tree(self, parent, accepted_node, x, B, dt, A=None, D=None, materialize=False):
+        """Keep the root path of accepted_node[b] (device int32 [batch], -1..K-1; -1 keeps
+        nothing) of each slot's draft tree."""
+        K = x.shape[1]
+        self._check_tokens("commit_tree", x, B, dt)
+        self._check_int_rows("commit_tree: parent", parent, (self.batch, K))
+        self._check_int_rows("commit_tree: accepted_node", accepted_node, (self.batch,))
+        self._check_shapes("commit_tree", self.batch, K, x, B, None, dt, A, D, None)
+        st = L.lib().mil_ssm_commit_tree(ctypes.byref(self.desc), K, _ptr(parent), _ptr(accepted_node), _ptr(x),
+                                         _ptr(B), _ptr(dt), _ptr(A), _ptr(D),
+                                         L.MIL_COMMIT_MATERIALIZE if materialize else 0, _stream(self.device))
+        L.check(st, "mil_ssm_commit_tree")
+
     def greedy_workspace_bytes(self, K: int, vocab: int) -> int:
         return int(L.lib().mil_ssm_greedy_workspace_bytes(ctypes.byref(self.dims), K, vocab))
 

@@ -139,6 +139,24 @@ def integer_projection(rng: np.random.Generator, T: int, d: int, H: int, P: int,
                       quantize(ints((H, d)), BF16), quantize(np.zeros(H), F32))
 
 
+def draw_tree(rng: np.random.Generator, batch: int, K: int, kind: str = "random") -> np.ndarray:
+    """Draft-tree links parent [batch][K] int32 (-1..k-1; -1 = the committed state):
+    "random": parent[b][k] ~ U{-1..k-1}; "chain": k-1; "binary": node 0 follows the state
+    and node k >= 1 follows node (k-1)//2; "fan": every node follows the state."""
+    if kind == "chain":
+        return np.tile(np.arange(-1, K - 1, dtype=np.int32), (batch, 1))
+    if kind == "binary":
+        row = np.array([-1] + [(k - 1) // 2 for k in range(1, K)], dtype=np.int32)
+        return np.tile(row, (batch, 1))
+    if kind == "fan":
+        return np.full((batch, K), -1, dtype=np.int32)
+    par = np.zeros((batch, K), dtype=np.int32)
+    for b in range(batch):
+        for k in range(K):
+            par[b, k] = rng.integers(-1, k)
+    return par
+
+
 def draw_accept_uniform(rng: np.random.Generator, batch: int, K: int) -> np.ndarray:
     """Accepted lengths j ~ U{0..K} (inclusive), int32."""
     return rng.integers(0, K + 1, size=batch).astype(np.int32)

@@ -261,3 +261,22 @@ def test_project_argument_checks(lib):
     assert call(x=P(1)) == L.MIL_E_ALIGN
     assert call(bias=P(2)) == L.MIL_E_ALIGN
     assert call(dd=dims(batch=1, H=3, P=128, N=128, G=2)) == L.MIL_E_INVALID  # H % G != 0
+
+
+def test_tree_call_checks(lib):
+    c = attached(lib, k_max=8)
+    vt, ct = lib.mil_ssm_verify_tree, lib.mil_ssm_commit_tree
+
+    def verify(cache=c, K=4, parent=P(), y=P()):
+        return vt(ctypes.byref(cache), K, parent, P(), P(), P(), P(), P(), P(), y, None)
+
+    def commit(cache=c, K=4, parent=P(), node=P(), flags=0):
+        return ct(ctypes.byref(cache), K, parent, node, P(), P(), P(), None, None, flags, None)
+
+    assert commit() == L.MIL_E_ORDER  # no verify before it
+    assert verify(parent=None) == L.MIL_E_INVALID
+    assert verify(K=0) == L.MIL_E_INVALID
+    assert verify(K=9) == L.MIL_E_INVALID  # above k_max
+    assert verify(parent=P(FAKE + 2)) == L.MIL_E_ALIGN
+    assert verify(cache=L.CacheDesc()) == L.MIL_E_INVALID
+    assert lib.mil_ssm_cache_phase(ctypes.byref(c)) == L.PHASE_READY
