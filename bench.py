@@ -102,7 +102,8 @@ def _to_dev_factory(torch, synth, dev):
 def step_kind(w):
     if w.name == "llama8b_long_prefill":
         return "prefill"
-    if w.name in ("llama8b_batched", "hybrid_decode", "llama8b_batched_greedy", "llama8b_batched_project"):
+    if w.name in ("llama8b_batched", "hybrid_decode", "llama8b_batched_greedy", "llama8b_batched_project",
+                  "llama8b_batched_tree"):
         return "verify"
     return "full"
 
@@ -111,6 +112,17 @@ def accept_work(w, batch, K):
     """Greedy acceptance: every logit read once, drafts in, accepted lengths and tokens out."""
     le = 2  # bf16 logits
     return batch * K * w.vocab * le + batch * K * 4 * 2 + batch * 4, 0
+
+
+def path_lengths(parent, node):
+    """Length of the root path of node[b] in draft tree parent[b] (0 for node -1)."""
+    out = np.zeros(len(node), dtype=np.int64)
+    for b, a in enumerate(node):
+        a = int(a)
+        while a >= 0:
+            out[b] += 1
+            a = int(parent[b, a])
+    return out
 
 
 def project_work(w, T):
@@ -193,13 +205,19 @@ def run_gpu(args, w):
                           chunk=128 if w.N > 128 else w.chunk, want_y=False)
         torch.cuda.synchronize()
         for r in range(R):
-            caches, drfs, js, jns, yvs, greedy, proj = [], [], [], [], [], [], []
+            caches, drfs, js, jns, yvs, greedy, proj, trees = [], [], [], [], [], [], [], []
             for li in range(nlayers):
                 c = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
                 c.buffer.copy_(proto.buffer)
                 drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
                 j = (synth.draw_accept_geometric(rng, Bt, K) if w.accept == "geometric"
                      else synth.draw_accept_uniform(rng, Bt, K))
+                if w.tree:
+                    # a random tree per sequence and one accepted node; j = its path length
+                    par = synth.draw_tree(rng, Bt, K, w.tree)
+                    node = rng.integers(-1, K, size=Bt).astype(np.int32)
+                    j = path_lengths(par, node).astype(np.int32)
+                    trees.append(dict(par=torch.from_numpy(par).to(dev), node=torch.from_numpy(node).to(dev)))
                 if w.accept == "greedy":
                     # logits planted so that greedy verification accepts j[b] drafts
                     dtok, lg = synth.draw_greedy(rng, Bt, K, w.vocab, synth.BF16, j)
@@ -221,7 +239,7 @@ def run_gpu(args, w):
                 js.append(torch.from_numpy(j).to(dev))
                 jns.append(j)
                 yvs.append(torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev))
-            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy, proj=proj))
+            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy, proj=proj, tree=trees))
         del proto
         torch.cuda.synchronize()
     R = len(sets)
@@ -246,6 +264,11 @@ def run_gpu(args, w):
                             ws=pj["ws"])
                     if tr:
                         evs["tb"][s].record()
+                if st.get("tree"):
+                    tr = st["tree"][li]
+                    c.verify_tree(tr["par"], dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
+                    c.commit_tree(tr["par"], tr["node"], dx, dB, ddt)
+                    continue
                 c.verify(dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
                 if st.get("greedy"):
                     gr = st["greedy"][li]
@@ -412,14 +435,15 @@ def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
 
 KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
     "prefill_state": "chunk_state_", "prefill_pass": "state_pass", "prefill_out": "chunk_out_",
-    "verify": "ssm_verify_kernel", "commit": "_commit_kernel", "accept": "greedy_argmax", "project": "project_",
+    "verify": "ssm_verify_kernel", "commit": ("_commit_kernel", "_commit_tree_kernel"), "accept": "greedy_argmax",
+    "project": "project_",
     "copy": "elementwise",
 }
 
 
 def _family(name):
     for k, pat in KERNEL_PATTERNS.items():
-        if pat in name:
+        if any(q in name for q in ((pat,) if isinstance(pat, str) else pat)):
             return k
     return None
 
@@ -515,7 +539,7 @@ def main():
     args.steps = max(1, args.steps)
     if args.graph and step_kind(w) != "verify":
         ap.error("--graph applies to the verify workloads (llama8b_batched, llama8b_batched_greedy, "
-                 "llama8b_batched_project, hybrid_decode)")
+                 "llama8b_batched_project, llama8b_batched_tree, hybrid_decode)")
     g = run_gpu(args, w)
     kind = g["kind"]
 
@@ -558,14 +582,17 @@ def main():
     cfg = {"workload": w.name, "batch": Bt, "heads": w.H, "headdim": w.P, "dstate": w.N, "groups": w.G,
            "layers": w.layers, "chunk": w.chunk, "rotating_sets": g["R"], "parallelism": "single GPU",
            "step": {"full": f"prefill {L} + verify {K} + commit", "prefill": f"prefill {L}",
-                    "verify": f"{w.layers} x (" + ("project + " if w.d_model else "") + f"verify {K} + "
-                              + ("greedy commit)" if w.accept == "greedy" else "commit)")}[kind]}
+                    "verify": f"{w.layers} x (" + ("project + " if w.d_model else "")
+                              + ("tree " if w.tree else "") + f"verify {K} + "
+                              + {"greedy": "greedy commit)", "tree": "tree commit)"}.get(w.accept, "commit)")}[kind]}
     if w.d_model:
         cfg["d_model"] = w.d_model
     if kind != "prefill":
         cfg.update({"drafts_K": K, "accept": {"geometric": "j ~ min(Geom(0.3)-1, K)", "uniform": "j ~ U{0..K}",
                                               "greedy": f"greedy on the device, bf16 logits over {w.vocab} tokens "
-                                                        "planted for j ~ U{0..K}"}[w.accept]})
+                                                        "planted for j ~ U{0..K}",
+                                              "tree": f"{w.tree} draft tree (parent ~ U{{-1..k-1}}), accepted node "
+                                                      "~ U{-1..K-1}, j = its root path's length"}[w.accept]})
     if kind != "verify":
         cfg["prefill_len"] = L
     if w.ctx_range:

@@ -237,6 +237,7 @@ class Workload:
     vocab: int = 0           # vocabulary size of the verifier logits ("greedy")
     d_model: int = 0         # > 0: the drafts' x, B, C, dt are projected on the device from
                              # layer input rows of this width (the step before the layer)
+    tree: str = ""           # draft-tree shape (draw_tree kinds); accept "tree" takes one node
     seed: int = 1000
 
 
@@ -259,6 +260,10 @@ WORKLOADS = {
     # the device (Llama-3-8B width 4096; seeded stand-in weights) before verify and commit
     "llama8b_batched_project": Workload("llama8b_batched_project", batch=16, H=32, P=128, N=128, G=8,
                                         dtype=BF16, K=8, ctx_range=(256, 4096), d_model=4096, seed=1007),
+    # the batched round with tree drafts: 8 candidate tokens per sequence in a random tree
+    # (parent ~ U{-1..k-1}), one accepted node ~ U{-1..7} whose root path is kept
+    "llama8b_batched_tree": Workload("llama8b_batched_tree", batch=16, H=32, P=128, N=128, G=8, dtype=BF16,
+                                     K=8, ctx_range=(256, 4096), accept="tree", tree="random", seed=1008),
     # one long prefill scan
     "llama8b_long_prefill": Workload("llama8b_long_prefill", batch=1, H=32, P=128, N=128, G=8,
                                      dtype=BF16, L=8192, chunk=256, seed=1004),
