@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
-KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept", "project"]
+KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept", "project", "prefill_scan"]
+PREFILL_KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "prefill_scan"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -292,7 +293,11 @@ def run_gpu(args, w):
             lib.mil_ssm_cache_trace(ctypes.byref(st["caches"][0].desc), L.TRACE[name],
                                     ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event))
 
-    kernels = {"full": KERNELS[:5], "prefill": KERNELS[:3], "verify": KERNELS[3:5]}[kind]
+    kernels = {"full": KERNELS[3:5], "prefill": [], "verify": KERNELS[3:5]}[kind]
+    if kind in ("full", "prefill"):
+        # the prefill kernels this shape launches (one launch, or three phases)
+        mask = lib.mil_ssm_prefill_kernels(ctypes.byref(sets[0]["caches"][0].desc), Bt, w.L, w.chunk)
+        kernels = [k for k in PREFILL_KERNELS if mask & (1 << L.TRACE[k])] + kernels
     if w.accept == "greedy":
         kernels = kernels + ["accept"]
     if w.d_model:
@@ -375,6 +380,7 @@ def run_gpu(args, w):
     if kind in ("full", "prefill"):
         pw = prefill_work(w, w.L)
         work.update({k: (pw[k][0] * Bt, pw[k][1] * Bt) for k in ("prefill_state", "prefill_pass", "prefill_out")})
+        work["prefill_scan"] = (pw["all"][0] * Bt, pw["all"][1] * Bt)
     if kind in ("full", "verify"):
         # rows pending at a verify: none after a prefill ("full"); else the previous
         # commit's accepted lengths, whose mean is that of the j distribution
@@ -435,6 +441,7 @@ def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
 
 KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
     "prefill_state": "chunk_state_", "prefill_pass": "state_pass", "prefill_out": "chunk_out_",
+    "prefill_scan": "chunk_scan_",
     "verify": "ssm_verify_kernel", "commit": ("_commit_kernel", "_commit_tree_kernel"), "accept": "greedy_argmax",
     "project": "project_",
     "copy": "elementwise",
@@ -557,7 +564,7 @@ def main():
     byt, fl = g["work"][dom]
     t = g["dom_ms"] * 1e-3
     bf16 = w.dtype == "bf16"
-    if dom in ("prefill_out", "prefill_state") and bf16 and fl / byt > (BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3):
+    if dom in ("prefill_out", "prefill_state", "prefill_scan") and bf16 and fl / byt > (BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3):
         roof = dict(bound="mfma", achieved=fl / t / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
     else:
         roof = dict(bound="hbm", achieved=byt / t / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")

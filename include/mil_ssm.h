@@ -80,7 +80,12 @@ typedef struct {
  *   pos     int32 [batch]: tokens the sequence has absorbed (prefill + accepted drafts).
  *   pending int32 [batch]: how many rows of pend_* are accepted but not yet folded in.
  *   err     int32 [batch]: 0, or the OR of MIL_DEVERR_ACCEPT (an out-of-range accepted
- *           length or node) and MIL_DEVERR_TREE (a tree link outside -1..k-1).
+ *           length or node), MIL_DEVERR_TREE (a tree link outside -1..k-1) and
+ *           MIL_DEVERR_SCAN (a prefill's chunk-to-chunk handoff timed out; the slot's
+ *           prefill results are then wrong).
+ *   scan    int32 [batch][H][8][9]: single-launch prefill flags (one per chunk of up to 8
+ *           chunks, then a counter, per column slab), zero between calls (the prefill leaves
+ *           them zero; mil_ssm_cache_init zeroes them).
  * The logical state of slot b is `state` advanced through its `pending` rows.
  */
 typedef struct {
@@ -88,10 +93,12 @@ typedef struct {
     int64_t state_off, state_head_stride;
     int64_t pend_x_off, pend_B_off, pend_dt_off;
     int64_t pos_off, pending_off, err_off;
+    int64_t scan_off;
 } mil_ssm_layout;
 
 #define MIL_DEVERR_ACCEPT 1
 #define MIL_DEVERR_TREE 2      /* a tree link outside -1..k-1 (verify_tree / commit_tree) */
+#define MIL_DEVERR_SCAN 4      /* a prefill chunk waited too long for the state of the chunk before it */
 
 /* Host-side cache descriptor.  The caller provides the storage; mil_ssm_cache_init
  * fills it.  It holds the device buffer address, the shape and the protocol phase. */
@@ -291,8 +298,16 @@ enum mil_trace_kernel {
     MIL_TRACE_PREFILL_STATE = 4, /* prefill phase 1: per-chunk states */
     MIL_TRACE_PREFILL_PASS = 5,  /* prefill phase 2: sequential pass across chunks */
     MIL_TRACE_PREFILL_OUT = 6,   /* prefill phase 3: per-chunk outputs */
-    MIL_TRACE_ACCEPT = 7         /* greedy acceptance: vocabulary argmax per draft position */
+    MIL_TRACE_ACCEPT = 7,        /* greedy acceptance: vocabulary argmax per draft position */
+    MIL_TRACE_PREFILL_SCAN = 8   /* prefill in one launch (chunk states, handoff and outputs) */
 };
+
+/* Which traceable kernels a mil_ssm_prefill of these sizes launches on this cache (with y
+ * requested and 16-byte aligned x, B, C): a bit mask with bit k set for mil_trace_kernel
+ * k.  Bf16 caches whose chunk is 256 and whose shapes the one-launch kernel covers get
+ * (1 << MIL_TRACE_PREFILL_SCAN); other shapes get the three phases (STATE, PASS, OUT).
+ * Returns 0 for a bad descriptor or sizes.  Host-side only. */
+int mil_ssm_prefill_kernels(const mil_ssm_cache *cache, int32_t nseq, int32_t L, int32_t chunk);
 
 /* Profiling hook: until changed, every launch of `kernel` made through this descriptor
  * is bracketed by hipEventRecord(ev_start) and hipEventRecord(ev_stop) on the call's

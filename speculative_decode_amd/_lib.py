@@ -18,6 +18,7 @@ MIL_PREFILL_CONTINUE = 1
 MIL_COMMIT_MATERIALIZE = 1
 MIL_DEVERR_ACCEPT = 1
 MIL_DEVERR_TREE = 2
+MIL_DEVERR_SCAN = 4
 MIL_KMAX_LIMIT = 16
 PHASE_UNINIT, PHASE_READY, PHASE_VERIFIED = 0, 1, 2
 
@@ -27,10 +28,10 @@ EXPORTS = [
     "mil_ssm_cache_init", "mil_ssm_cache_attach", "mil_ssm_prefill_workspace_bytes", "mil_ssm_prefill", "mil_ssm_verify",
     "mil_ssm_commit", "mil_ssm_cache_status", "mil_ssm_cache_phase", "mil_ssm_cache_trace",
     "mil_ssm_greedy_workspace_bytes", "mil_ssm_commit_greedy", "mil_ssm_project_workspace_bytes", "mil_ssm_project",
-    "mil_ssm_verify_tree", "mil_ssm_commit_tree",
+    "mil_ssm_verify_tree", "mil_ssm_commit_tree", "mil_ssm_prefill_kernels",
 ]
 TRACE = {"off": 0, "verify": 1, "fold": 2, "commit": 3, "prefill_state": 4, "prefill_pass": 5, "prefill_out": 6,
-         "accept": 7}
+         "accept": 7, "prefill_scan": 8}
 
 
 class MilError(RuntimeError):
@@ -47,7 +48,7 @@ class Dims(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("bytes", "state_off", "state_head_stride", "pend_x_off",
                                               "pend_B_off", "pend_dt_off", "pos_off", "pending_off",
-                                              "err_off")]
+                                              "err_off", "scan_off")]
 
 
 class CacheDesc(ctypes.Structure):
@@ -88,6 +89,7 @@ def lib():
                                   ctypes.c_int),
         "mil_ssm_project_workspace_bytes": ([dims_p, i32, i32], sz),
         "mil_ssm_verify_tree": ([cache_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+        "mil_ssm_prefill_kernels": ([cache_p, i32, i32, i32], ctypes.c_int),
         "mil_ssm_commit_tree": ([cache_p, i32, vp, vp, vp, vp, vp, vp, vp, u32, vp], ctypes.c_int),
         "mil_ssm_project": ([dims_p, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
                             ctypes.c_int),

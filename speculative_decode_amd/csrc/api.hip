@@ -92,6 +92,8 @@ int mil_ssm_cache_layout(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mi
     off += Bt * 4;
     L.err_off = off = round_up(off, kAlign);
     off += Bt * 4;
+    L.scan_off = off = round_up(off, kAlign);
+    off += Bt * H * kScanSlabs * (kScanChunks + 1) * 4;
     L.bytes = round_up(off, kAlign);
     *out = L;
     return MIL_OK;
@@ -365,11 +367,24 @@ int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t 
         }
     free(host);
     if (clear) {
+        // the error words, and the prefill handoff counters (only a timed-out handoff
+        // can leave one set)
         e = launch_fill_zero(cache_err(*c), Bt, s);
+        if (e == hipSuccess)
+            e = launch_fill_zero(cache_scan(*c), (int64_t)Bt * c->dims.nheads * kScanSlabs * (kScanChunks + 1), s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) return MIL_E_HIP;
     }
     return *bad_slot < 0 ? MIL_OK : MIL_E_INVALID;
+}
+
+int mil_ssm_prefill_kernels(const mil_ssm_cache *cache, int32_t nseq, int32_t L, int32_t chunk) {
+    const CacheImpl *c = impl(cache);
+    if (!c || nseq < 1 || nseq > c->dims.batch || L < 1 || (chunk != 64 && chunk != 128 && chunk != 256)) return 0;
+    const mil_ssm_dims &d = c->dims;
+    if (c->dtype == MIL_BF16 && prefill_single_launch(nseq, L, chunk, d.nheads, d.headdim, d.dstate))
+        return 1 << MIL_TRACE_PREFILL_SCAN;
+    return (1 << MIL_TRACE_PREFILL_STATE) | (1 << MIL_TRACE_PREFILL_PASS) | (1 << MIL_TRACE_PREFILL_OUT);
 }
 
 int mil_ssm_cache_phase(const mil_ssm_cache *cache) {
@@ -379,7 +394,7 @@ int mil_ssm_cache_phase(const mil_ssm_cache *cache) {
 
 int mil_ssm_cache_trace(mil_ssm_cache *cache, int32_t kernel, void *ev_start, void *ev_stop) {
     CacheImpl *c = impl(cache);
-    if (!c || kernel < MIL_TRACE_OFF || kernel > MIL_TRACE_ACCEPT) return MIL_E_INVALID;
+    if (!c || kernel < MIL_TRACE_OFF || kernel > MIL_TRACE_PREFILL_SCAN) return MIL_E_INVALID;
     if (kernel == MIL_TRACE_OFF || !ev_start || !ev_stop) {
         c->trace_kernel = MIL_TRACE_OFF;
         c->trace_start = c->trace_stop = nullptr;

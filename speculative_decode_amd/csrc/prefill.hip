@@ -17,6 +17,8 @@
 //
 // This file holds the fp32 vector-ALU form, used for fp32 inputs and for shapes the
 // matrix-core form (prefill_mfma.hip, bf16 inputs) does not cover.
+#include <algorithm>
+
 #include "ssm_internal.h"
 
 namespace mil {
@@ -277,7 +279,10 @@ int64_t prefill_workspace_bytes(const mil_ssm_dims &d, int nseq, int L, int chun
     const int64_t nch = (L + chunk - 1) / chunk;
     const int64_t states = (int64_t)nseq * nch * d.nheads * d.dstate * d.headdim * 4;
     const int64_t tots = (int64_t)nseq * nch * d.nheads * 4;
-    return (states + 255) / 256 * 256 + (tots + 255) / 256 * 256;
+    // the single-launch form publishes each chunk's own state (and its decay, padded to 16
+    // floats per column slab, at most kScanSlabs slabs) instead
+    const int64_t chain = (int64_t)nseq * d.nheads * nch * ((int64_t)d.dstate * d.headdim + 16 * kScanSlabs) * 4;
+    return std::max((states + 255) / 256 * 256 + (tots + 255) / 256 * 256, (chain + 255) / 256 * 256);
 }
 
 hipError_t launch_prefill(const CacheImpl &c, int slot0, int nseq, int L, int chunk, const void *x,

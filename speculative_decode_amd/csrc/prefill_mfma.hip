@@ -69,6 +69,10 @@ struct MParams {
     int L, Q, nch, H, P, N, G;
     int slot0, nseq, batch, cont;
     int PS, nslab;         // phase 1: state rows p per workgroup, slabs per chunk-head
+    // single-launch scan
+    int32_t *scan;         // handoff counters [batch][H][kScanSlabs] (zero between calls)
+    int32_t *err;          // [batch] device error words
+    float *chain;          // [nseq][H][P/PC][nch][N*PC + 16] published chunk states (register order), E_c
 };
 
 // Work-item order with consecutive items on one XCD: workgroups are dealt to the 8 XCDs
@@ -615,6 +619,457 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
     }
 }
 
+// ------------------------------------------------------------------ single launch
+// All three phases in one launch for prompts of up to kScanChunks chunks, one workgroup per
+// (chunk, sequence, head, column slab), chunk-major.  The workgroup stages its chunk's B,
+// C, X and dt once, computes the chunk's own state contribution S_c = sum_s (w_s B_s) x_s^T
+// on the matrix cores and publishes it with the chunk's total decay E_c (a flag per chunk),
+// forms the intra-chunk outputs, and then folds the state entering its chunk from h0
+// through chunks 0..c-1 in order (h <- E_i h + S_i): the operations of a sequential pass in
+// its order, so the result does not depend on timing, and no workgroup waits on a chain
+// of others, only on the publications, which come right after each chunk's S.  The last
+// workgroup of a chain to finish reading writes the final state (every chunk reads h0 from
+// the cache first) and resets the chain's flags.  Longer prompts keep the three launches
+// (their per-chunk reads of all earlier chunks would grow with the square of the count).
+//
+// Ordering: workgroups start in chunk-major order and every one publishes before it
+// waits, so the flags a workgroup waits for are always raised; the wait is bounded in time
+// anyway (MIL_DEVERR_SCAN is reported and the kernel carries on), so nothing can hang.
+// Flags, counters and published states use agent-coherent accesses (see shared_load).
+constexpr long long kScanWaitTicks = 50000000;  // 0.5 s of the 100 MHz real-time counter
+
+// Everything that crosses workgroups (the published states and decays, the flags, the
+// counter) is read and written with agent-coherent accesses (relaxed agent-scope atomics:
+// loads and stores that bypass the non-coherent cache levels), and each wave waits for
+// its stores to complete (s_waitcnt vmcnt(0)) before the workgroup raises a flag.  So no
+// access needs the whole-cache write-back or invalidation that release / acquire
+// orderings would add (measured: they made the handoffs several times slower).
+__device__ __forceinline__ int scan_load(const int32_t *f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void scan_store(int32_t *f, int v) {
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float shared_load(const float *q) {
+    return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void shared_store(float *q, float v) {
+    __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int N, int PC>
+__global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
+    extern __shared__ __align__(16) char lds[];
+    const int H = p.H, G = p.G, Q = p.Q, P = p.P;
+    const int nps = P / PC;
+    const int per_chunk = p.nseq * H * nps;
+    const int c = blockIdx.x / per_chunk;
+    const int u = blockIdx.x - c * per_chunk;
+    // within a chunk, consecutive items (heads of one B/C group, and their slabs) on one XCD
+    const int sub = (per_chunk % 8 == 0) ? (u % 8) * (per_chunk / 8) + u / 8 : u;
+    const int slab = sub % nps, hs = sub / nps;
+    const int h = hs % H, seq = hs / H;
+    const int pc0 = slab * PC;
+    const int g = h / (H / G);
+    const int c0 = c * Q, len = min(Q, p.L - c0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+    const int NT = blockDim.x, NW = NT >> 6;
+    const int BS = N + 8, XS = Q + 8;
+    constexpr int PT = PC / kT, NK = N / 16, HS = N * 2 + 8;
+    constexpr int NTL = N / kT;                        // state row tiles
+    constexpr int STILES = NTL * PT;                   // state tiles of this slab
+    constexpr int TPW = STILES >= 8 ? STILES / 8 : 1;  // per wave (8 waves)
+
+    bf16 *sB = reinterpret_cast<bf16 *>(lds);
+    bf16 *sXT = sB + Q * BS;
+    bf16 *sH = reinterpret_cast<bf16 *>(lds);
+    const size_t big = max((size_t)Q * BS + (size_t)PC * XS, (size_t)PC * HS) * 2;
+    float *sDt = reinterpret_cast<float *>(lds + big);
+    float *sDtA = sDt + Q, *sR = sDtA + Q, *sSuf = sR + Q, *sColf = sSuf + Q, *sEin = sColf + Q;
+    float *sWst = sEin + Q;                         // [Q] dt_s * decay(s, chunk end)
+    float *sTot = sWst + Q;                         // [8]
+    float *sMid = sTot + 8;                         // [8][8]
+
+    if (blockIdx.x == 0) {
+        for (int i = tid; i < p.batch; i += NT) {
+            const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
+            if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
+            if (mine || p.cont) p.pending[i] = 0;
+        }
+    }
+
+    const size_t tok0 = (size_t)seq * p.L + c0;
+    const float Ah = p.A[h], Dh = p.D[h];
+    const int nt = Q / kT;
+    const int I = wave < nt / 2 ? wave : nt - 1 - (wave - nt / 2);
+    const bool active = I * kT < len;
+    const int t = I * kT + l32;
+
+    // ---- staging, as in the output phase ----
+    bf16x8 cf[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+        cf[kk] = (active && t < len)
+                     ? *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + t) * G + g) * N + kk * 16 + hf * 8)
+                     : bf16x8{};
+    const float dv = tid < Q && tid < len ? bf2f(p.dt[(tok0 + tid) * H + h]) : 0.f;
+    constexpr int BI = N / 16;
+    uint4 vb[BI];
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int it = tid + j * NT;
+        const int sr = it / (N / 8), ng = it % (N / 8);
+        vb[j] = sr < len ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + sr) * G + g) * N + ng * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
+    constexpr int XI = (PC + 63) / 64;
+    uint4 vx[XI][4];
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+        const int it = tid + j * NT;
+        const int pg = it / (Q / 4), sq = it % (Q / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int sr = sq * 4 + r;
+            vx[j][r] = (it < (Q / 4) * (PC / 8) && sr < len)
+                           ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + sr) * H + h) * P + pc0 + pg * 8)
+                           : make_uint4(0, 0, 0, 0);
+        }
+    }
+    if (tid < Q) {
+        sDt[tid] = dv;
+        sDtA[tid] = dv * Ah;
+    }
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int it = tid + j * NT;
+        const int sr = it / (N / 8), ng = it % (N / 8);
+        *reinterpret_cast<uint4 *>(sB + sr * BS + ng * 8) = vb[j];
+    }
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+        const int it = tid + j * NT;
+        if (it >= (Q / 4) * (PC / 8)) break;
+        const int pg = it / (Q / 4), sq = it % (Q / 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * XS + sq * 4) =
+                column4(vx[j][0], vx[j][1], vx[j][2], vx[j][3], i);
+    }
+    __syncthreads();
+    chunk_factors(sDtA, len, sR, sSuf, sTot, tid, NT);
+    const int ntile = (len + kT - 1) / kT;
+    for (int s = tid; s < Q; s += NT) {
+        if (s < len) {
+            sColf[s] = sDt[s] * __expf(sSuf[s]);
+            float m = sR[s];
+            for (int q = 0; q < s / kT; ++q) m += sTot[q];
+            sEin[s] = __expf(m);
+            float e = sSuf[s];  // decay from s to the chunk end: rest of s's tile, then later tiles
+            for (int q = s / kT + 1; q < ntile; ++q) e += sTot[q];
+            sWst[s] = __expf(e) * sDt[s];
+        } else {
+            sWst[s] = 0.f;  // tokens past the chunk end carry no weight
+        }
+    }
+    if (tid < 64) {
+        const int Ii = tid / 8, J = tid % 8;
+        float m = 0.f;
+        for (int q = J + 1; q < Ii; ++q) m += sTot[q];
+        sMid[tid] = (J < Ii && Ii < ntile) ? __expf(m) : 0.f;
+    }
+    __syncthreads();
+    float ttot = 0.f;
+    for (int q = 0; q < ntile; ++q) ttot += sTot[q];
+    const float Ec = __expf(ttot);
+
+    // ---- the chunk's own state S[n][p] (this slab), n rows from B^T read column-wise out
+    // of the B rows, (w X) split hi + lo; lane: column p, register r: row 8(r/4) + 4hf + r%4
+    f32x16 sacc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) sacc[i] = f32x16{};
+    const bool swave = wave < STILES;  // fewer tiles than waves: the extra waves idle here
+    const int snt = wave % NTL;        // this wave's row tile (shared by its tiles)
+    if (swave) {
+        for (int ks = 0; ks < (len + 15) / 16; ++ks) {
+            const int s0 = ks * 16 + 8 * hf;
+            bf16x8 a;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) a[v] = sB[(s0 + v) * BS + snt * kT + l32];
+            const float4 w0 = *reinterpret_cast<const float4 *>(sWst + s0);
+            const float4 w1 = *reinterpret_cast<const float4 *>(sWst + s0 + 4);
+            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int spt = (wave + i * 8) / NTL;
+                const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(sXT + (spt * kT + l32) * XS + s0);
+                bf16x8 bh, bl;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) {
+                    bf16 x1, x2;
+                    split(wv[v] * bf2f(xv[v]), x1, x2);
+                    bh[v] = x1;
+                    bl[v] = x2;
+                }
+                sacc[i] = mfma(a, bh, sacc[i]);
+                sacc[i] = mfma(a, bl, sacc[i]);
+            }
+        }
+    }
+
+    // ---- publish this chunk's own state S and decay E_c (no waiting before it) ----
+    const int slot = p.slot0 + seq;
+    int32_t *flags = p.scan + (((size_t)slot * H + h) * kScanSlabs + slab) * (kScanChunks + 1);
+    const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: S in register order, then E_c
+    float *aggs = p.chain + (((size_t)seq * H + h) * nps + slab) * (size_t)p.nch * AGG;
+    float *cache = p.state + (size_t)(seq * H + h) * p.head_stride;
+    if (p.nch > 1) {
+        float *dst = aggs + (size_t)c * AGG;
+        if (swave) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tl = wave + i * 8;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) shared_store(dst + (size_t)(tl * 16 + r) * 64 + lane, sacc[i][r]);
+            }
+        }
+        if (tid == 0) shared_store(dst + N * PC, Ec);
+        // every wave's stores complete before the barrier, and the flag goes up after it
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) scan_store(flags + c, 1);
+    }
+    // ---- outputs: intra-chunk products, as in the output phase (only when y is wanted) ----
+    const bool want_y = p.y != nullptr;
+    f32x16 acc[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) acc[i] = f32x16{};
+    if (active && want_y) {
+        const float et = __expf(sR[min(t, Q - 1)]);
+        for (int J = 0; J < I; ++J) {
+            f32x16 z = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
+                z = mfma(bfr, cf[kk], z);
+            }
+            const float rowf = sMid[I * 8 + J] * et;
+            bf16x8 ah[2], al[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 cf4 = *reinterpret_cast<const float4 *>(sColf + J * kT + 8 * q + 4 * hf);
+                const float cv[4] = {cf4.x, cf4.y, cf4.z, cf4.w};
+#pragma unroll
+                for (int u2 = 0; u2 < 4; ++u2) {
+                    const int r = 4 * q + u2;
+                    bf16 a1, b1;
+                    split(z[r] * cv[u2] * rowf, a1, b1);
+                    ah[r / 8][r % 8] = a1;
+                    al[r / 8][r % 8] = b1;
+                }
+            }
+            accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
+        }
+        {
+            const int J = I;
+            f32x16 z = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
+                z = mfma(bfr, cf[kk], z);
+            }
+            const float Rt = sR[min(t, Q - 1)];
+            bf16x8 ah[2], al[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 r4 = *reinterpret_cast<const float4 *>(sR + J * kT + 8 * q + 4 * hf);
+                const float4 d4 = *reinterpret_cast<const float4 *>(sDt + J * kT + 8 * q + 4 * hf);
+                const float rv[4] = {r4.x, r4.y, r4.z, r4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int u2 = 0; u2 < 4; ++u2) {
+                    const int r = 4 * q + u2;
+                    const int sl = 8 * q + 4 * hf + u2;
+                    float m = z[r] * dv4[u2] * __expf(Rt - rv[u2]);
+                    m = sl < l32 ? m : (sl == l32 ? m + Dh : 0.f);
+                    bf16 a1, b1;
+                    split(m, a1, b1);
+                    ah[r / 8][r % 8] = a1;
+                    al[r / 8][r % 8] = b1;
+                }
+            }
+            accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
+        }
+    }
+    // ---- the state entering this chunk: h0 (or zeros) folded through chunks 0..c-1 in
+    // order, h <- E_i h + S_i, the same operations in the same order as a sequential pass,
+    // so the result does not depend on which workgroup got where first ----
+    const bool has_hin = p.cont || c > 0;
+    f32x16 hin[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) hin[i] = f32x16{};
+    if (c > 0) {
+        if (tid == 0) {
+            const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+            bool late = false;
+            for (int i = 0; i < c && !late; ++i) {
+                while (scan_load(flags + i) == 0) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kScanWaitTicks) {
+                        atomicOr(p.err + slot, MIL_DEVERR_SCAN);
+                        late = true;
+                        break;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (swave && has_hin) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tl = wave + i * 8, spt = tl / NTL;
+            if (p.cont) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                    hin[i][r] = cache[(size_t)n * P + pc0 + spt * kT + l32];
+                }
+            }
+            for (int j = 0; j < c; ++j) {
+                const float *src = aggs + (size_t)j * AGG;
+                const float Ej = shared_load(src + N * PC);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    hin[i][r] = __builtin_fmaf(Ej, hin[i][r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
+            }
+        }
+    }
+    // ---- the final state.  Every chunk reads h0 from the cache, so it is written only
+    // once they all have: by the workgroup of the chain that finishes reading last (a
+    // counter), folding h0 through all the published chunks in order (one chunk: directly).
+    // That workgroup also resets the chain's flags and counter for the next call. ----
+    if (p.nch == 1) {
+        if (swave) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tl = wave + i * 8, spt = tl / NTL;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                    cache[(size_t)n * P + pc0 + spt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
+                }
+            }
+        }
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        int *sFlag = reinterpret_cast<int *>(sMid + 64);
+        if (tid == 0) {
+            const int done = __hip_atomic_fetch_add(flags + kScanChunks, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool final_one = done == p.nch - 1;
+            if (final_one) {
+                for (int i = 0; i < p.nch; ++i) scan_store(flags + i, 0);
+                scan_store(flags + kScanChunks, 0);
+            }
+            *sFlag = final_one ? 1 : 0;
+        }
+        __syncthreads();
+        if (*sFlag && swave) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tl = wave + i * 8, spt = tl / NTL;
+                f32x16 hf16 = f32x16{};
+                if (p.cont) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                        hf16[r] = cache[(size_t)n * P + pc0 + spt * kT + l32];
+                    }
+                }
+                for (int j = 0; j < p.nch; ++j) {
+                    const float *src = aggs + (size_t)j * AGG;
+                    const float Ej = shared_load(src + N * PC);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        hf16[r] = __builtin_fmaf(Ej, hf16[r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                    cache[(size_t)n * P + pc0 + spt * kT + l32] = hf16[r];
+                }
+            }
+        }
+    }
+    if (p.y == nullptr) return;
+    if (has_hin) {
+        __syncthreads();  // every wave is done with B and X^T: the carried state goes there
+        if (swave) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tl = wave + i * 8, spt = tl / NTL;
+                bf16 *row = sH + (spt * kT + l32) * HS;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int grp = snt * 4 + q;  // n group of 8: 8 hi then 8 lo
+                    bf16x4 hi4, lo4;
+#pragma unroll
+                    for (int u2 = 0; u2 < 4; ++u2) {
+                        bf16 a1, b1;
+                        split(hin[i][4 * q + u2], a1, b1);
+                        hi4[u2] = a1;
+                        lo4[u2] = b1;
+                    }
+                    *reinterpret_cast<bf16x4 *>(row + grp * 16 + 4 * hf) = hi4;
+                    *reinterpret_cast<bf16x4 *>(row + grp * 16 + 8 + 4 * hf) = lo4;
+                }
+            }
+        }
+        __syncthreads();
+        if (active) {
+            f32x16 acc2[PT];
+#pragma unroll
+            for (int i = 0; i < PT; ++i) acc2[i] = f32x16{};
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const bf16 *row = sH + (pt * kT + l32) * HS;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const bf16 *grp = row + (kk * 2 + hf) * 16;
+                    const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(grp);
+                    const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(grp + 8);
+                    acc2[pt] = mfma(cf[kk], bh, acc2[pt]);
+                    acc2[pt] = mfma(cf[kk], bl, acc2[pt]);
+                }
+            }
+            float ein[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ein[r] = sEin[min(I * kT + 8 * (r / 4) + 4 * hf + (r % 4), Q - 1)];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[pt][r] = __builtin_fmaf(ein[r], acc2[pt][r], acc[pt][r]);
+            }
+        }
+    }
+    if (!active) return;
+    float *yb = p.y + ((tok0 + I * kT) * H + h) * P + pc0 + l32;
+    const int ystride = H * P;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int tl = 8 * (r / 4) + 4 * hf + (r % 4);
+        if (I * kT + tl < len) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) yb[tl * ystride + pt * kT] = acc[pt][r];
+        }
+    }
+}
+
+size_t scan_lds_bytes(int Q, int N, int P) {
+    const size_t big = std::max((size_t)Q * (N + 8) + (size_t)P * (Q + 8), (size_t)P * (N * 2 + 8)) * 2;
+    return big + 7 * Q * 4 + 8 * 4 + 64 * 4 + 16;
+}
+
 size_t out_lds_bytes(int Q, int N, int P) {
     const size_t big = std::max((size_t)Q * (N + 8) + (size_t)P * (Q + 8), (size_t)P * (N * 2 + 8)) * 2;
     return big + 6 * Q * 4 + 8 * 4 + 64 * 4;
@@ -622,9 +1077,35 @@ size_t out_lds_bytes(int Q, int N, int P) {
 size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 + (4 * 256 + 8) * 4; }
 
 constexpr size_t kLdsMax = 160 * 1024;
-constexpr int64_t kOutItemsTarget = 256;  // phase-3 workgroups wanted (one per compute unit)
+constexpr int64_t kOutItemsTarget = 256;  // output workgroups wanted (one per compute unit)
+
+// Column slab width of the output work (and of the single launch): P split until the grid
+// has a workgroup per compute unit.
+int slab_width(int nseq, int nch, int H, int P) {
+    int pc = P;
+    while (pc > kT && (int64_t)nseq * nch * H * (P / pc) < kOutItemsTarget) pc /= 2;
+    return pc;
+}
+
+// The single-launch kernel for these sizes, or null (its LDS does not fit, a chunk other
+// than 256 tokens, which it is not built for, or more chunks than it keeps flags for).
+const void *scan_kernel(int chunk, int nch, int N, int pc) {
+    if (chunk != 256 || nch > kScanChunks || scan_lds_bytes(chunk, N, pc) > kLdsMax) return nullptr;
+#define MIL_SCAN_CASE(n, pp) \
+    if (N == n && pc == pp) return reinterpret_cast<const void *>(chunk_scan_mfma<n, pp>);
+    MIL_SCAN_CASE(64, 32) MIL_SCAN_CASE(64, 64) MIL_SCAN_CASE(64, 128)
+    MIL_SCAN_CASE(128, 32) MIL_SCAN_CASE(128, 64) MIL_SCAN_CASE(128, 128)
+#undef MIL_SCAN_CASE
+    return nullptr;
+}
 
 }  // namespace
+
+bool prefill_single_launch(int nseq, int L, int chunk, int H, int P, int N) {
+    if (!prefill_mfma_supported(chunk, N, P)) return false;
+    const int nch = (L + chunk - 1) / chunk;
+    return scan_kernel(chunk, nch, N, slab_width(nseq, nch, H, P)) != nullptr;
+}
 
 // Shapes the matrix-core path covers: bf16 inputs, N and P multiples of 32 up to 256,
 // a chunk the LDS can hold.
@@ -670,9 +1151,24 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     p.PS = p.P < 32768 / p.N ? p.P : 32768 / p.N;
     p.nslab = p.P / p.PS;
 
-    // phase-3 column slabs: split P until the grid has a workgroup per compute unit
-    int pc = p.P;
-    while (pc > kT && (int64_t)nseq * p.nch * p.H * (p.P / pc) < kOutItemsTarget) pc /= 2;
+    const int pc = slab_width(nseq, p.nch, p.H, p.P);
+
+    // one launch for all three phases where its LDS fits (chunks of 256, 8 waves)
+    const void *kf = scan_kernel(chunk, p.nch, p.N, pc);
+    if (kf) {
+        p.scan = cache_scan(c);
+        p.err = cache_err(c);
+        p.chain = static_cast<float *>(ws);
+        hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+        if (e != hipSuccess) return e;
+        void *args[] = {&p};
+        trace_begin(c, MIL_TRACE_PREFILL_SCAN, s);
+        e = hipLaunchKernel(kf, dim3(p.nch * nseq * p.H * (p.P / pc)), dim3(512), args,
+                            scan_lds_bytes(chunk, p.N, pc), s);
+        trace_end(c, MIL_TRACE_PREFILL_SCAN, s);
+        if (e != hipSuccess) return e;
+        return hipGetLastError();
+    }
     const size_t l1 = state_lds_bytes(p.PS, p.N), l3 = out_lds_bytes(chunk, p.N, pc);
     const int tpw = (p.PS / kT) * (p.N / kT) / 4;
     const void *k1 = tpw == 1 ? reinterpret_cast<const void *>(chunk_state_mfma<1>)

@@ -44,6 +44,11 @@ inline void *cache_pend_dt(const CacheImpl &c) { return c.base + c.lay.pend_dt_o
 inline int32_t *cache_pos(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.pos_off); }
 inline int32_t *cache_pending(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.pending_off); }
 inline int32_t *cache_err(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.err_off); }
+// single-launch prefill handoff flags: [slot][head][kScanSlabs][kScanChunks + 1] (a flag
+// per chunk, then a counter), zero between calls
+constexpr int kScanSlabs = 8;
+constexpr int kScanChunks = 8;  // chunks per prompt the single-launch prefill handles
+inline int32_t *cache_scan(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.scan_off); }
 inline int elt_bytes(int32_t dtype) { return dtype == MIL_BF16 ? 2 : 4; }
 
 // ---- launchers (each returns the launch's hipError_t) ----
@@ -89,6 +94,8 @@ hipError_t launch_prefill(const CacheImpl &c, int slot0, int nseq, int L, int ch
 
 // Matrix-core form of the three prefill phases (bf16 inputs; see prefill_mfma_supported).
 bool prefill_mfma_supported(int Q, int N, int P);
+// The matrix-core prefill of these sizes runs as one launch (chunk states, handoff, outputs).
+bool prefill_single_launch(int nseq, int L, int chunk, int H, int P, int N);
 hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, int chunk, const void *x,
                                const void *B, const void *C, const void *dt, const float *A,
                                const float *D, float *y, void *ws, bool cont, hipStream_t s);

@@ -59,13 +59,13 @@ def test_layout_is_head_major_and_aligned(lib, shape, dtype, k_max):
     Bt, H, P, N, G = shape
     e = 2 if dtype == L.MIL_BF16 else 4
     offs = [lay.state_off, lay.pend_x_off, lay.pend_B_off, lay.pend_dt_off, lay.pos_off,
-            lay.pending_off, lay.err_off, lay.bytes]
+            lay.pending_off, lay.err_off, lay.scan_off, lay.bytes]
     assert all(o % 256 == 0 for o in offs)
     assert lay.state_head_stride % 256 == 0 and lay.state_head_stride >= N * P * 4
     assert lay.state_head_stride < N * P * 4 + 256
     # regions in order, each big enough, no overlap
     sizes = [Bt * H * lay.state_head_stride, Bt * k_max * H * P * e, Bt * k_max * G * N * e,
-             Bt * k_max * H * e, Bt * 4, Bt * 4, Bt * 4]
+             Bt * k_max * H * e, Bt * 4, Bt * 4, Bt * 4, Bt * H * 8 * 9 * 4]
     for a, b, sz in zip(offs, offs[1:], sizes):
         assert b - a >= sz
     assert lib.mil_ssm_cache_bytes(ctypes.byref(d), k_max, dtype) == lay.bytes

@@ -144,8 +144,9 @@ def test_integer_linear_attention_is_exact(dtype, shape):
                           oracle.commit(rs, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j))
 
 
+@pytest.mark.parametrize("chunk", [64, 256])
 @pytest.mark.parametrize("shape", [VALU_SHAPE, MFMA_SHAPE])
-def test_prefill_continue_after_pending_rows(shape):
+def test_prefill_continue_after_pending_rows(shape, chunk):
     """prefill L1, verify K, commit j (deferred), prefill L2 with CONTINUE == prefill of
     L1 + j accepted drafts + L2."""
     rng = np.random.default_rng(41)
@@ -158,18 +159,41 @@ def test_prefill_continue_after_pending_rows(shape):
     c = synth.slice_tokens(tok, 0, Bt, L1 + K, L1 + K + L2)
     cache = SSMCache(Bt, H, P, N, G, K, dtype)
     A, D = dev_layer(layer)
-    cache.prefill(*dev_tokens(a), A, D, chunk=64)
+    cache.prefill(*dev_tokens(a), A, D, chunk=chunk)
     dx, dB, dC, ddt = dev_tokens(d)
     cache.verify(dx, dB, dC, ddt, A, D)
     j = np.array([2, 4], dtype=np.int32)
     cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt)
-    y2 = sync_np(cache.prefill(*dev_tokens(c), A, D, chunk=64, cont=True))
+    y2 = sync_np(cache.prefill(*dev_tokens(c), A, D, chunk=chunk, cont=True))
     _, h1 = oracle.prefill(a.x.f64, a.B.f64, a.C.f64, a.dt.f64, layer.A.f64, layer.D.f64)
     h1 = oracle.commit(h1, d.x.f64, d.B.f64, d.dt.f64, layer.A.f64, layer.D.f64, j)
     ry, rs = oracle.prefill(c.x.f64, c.B.f64, c.C.f64, c.dt.f64, layer.A.f64, layer.D.f64, h0=h1)
     assert y_err(y2, ry) <= TOL[dtype]
     assert state_err(logical_state(cache), rs) <= TOL[dtype]
     assert cache.pos().cpu().tolist() == [L1 + int(j[0]) + L2, L1 + int(j[1]) + L2]
+
+
+@pytest.mark.parametrize("L", [257, 1000, 2048, 2100])
+def test_prefill_leaves_handoff_counters_zero(L):
+    """The single-launch prefill hands the state from chunk to chunk through counters in
+    the cache; every call leaves them at zero, reports no error, and back-to-back calls
+    on other slots give the same results as separate caches."""
+    Bt, H, P, N, G = 3, 8, 128, 128, 4
+    rng = np.random.default_rng(4200 + L)
+    layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, synth.BF16, "tiny")
+    A, D = dev_layer(layer)
+    cache = SSMCache(Bt, H, P, N, G, 4, synth.BF16)
+    ys = []
+    for b in range(Bt):   # one slot at a time: the counters are reused call after call
+        one = synth.slice_tokens(tok, b, b + 1, 0, L)
+        ys.append(sync_np(cache.prefill(*dev_tokens(one), A, D, slot0=b, chunk=256)))
+    lay = cache.layout
+    scan = cache.buffer[lay.scan_off:lay.scan_off + Bt * H * 8 * 9 * 4].view(torch.int32).cpu().numpy()
+    assert not scan.any()
+    assert cache.status() == -1
+    ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
+    assert y_err(np.concatenate(ys), ry) <= TOL[synth.BF16]
+    assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
 
 
 # --------------------------------------------------------------------------- verify / commit
