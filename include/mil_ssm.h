@@ -83,9 +83,9 @@ typedef struct {
  *           length or node), MIL_DEVERR_TREE (a tree link outside -1..k-1) and
  *           MIL_DEVERR_SCAN (a prefill's chunk-to-chunk handoff timed out; the slot's
  *           prefill results are then wrong).
- *   scan    int32 [batch][H][8][9]: single-launch prefill flags (one per chunk of up to 8
- *           chunks, then a counter, per column slab), zero between calls (the prefill leaves
- *           them zero; mil_ssm_cache_init zeroes them).
+ *   scan    int32 [batch][H][8][8]: single-launch prefill flags (one per chunk of up to 8
+ *           chunks, per column slab); mil_ssm_cache_init zeroes them, and each prefill
+ *           writes values no other call in the process uses.
  * The logical state of slot b is `state` advanced through its `pending` rows.
  */
 typedef struct {

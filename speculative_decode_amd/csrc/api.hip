@@ -93,7 +93,7 @@ int mil_ssm_cache_layout(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mi
     L.err_off = off = round_up(off, kAlign);
     off += Bt * 4;
     L.scan_off = off = round_up(off, kAlign);
-    off += Bt * H * kScanSlabs * (kScanChunks + 1) * 4;
+    off += Bt * H * kScanSlabs * kScanChunks * 4;
     L.bytes = round_up(off, kAlign);
     *out = L;
     return MIL_OK;
@@ -367,11 +367,7 @@ int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t 
         }
     free(host);
     if (clear) {
-        // the error words, and the prefill handoff counters (only a timed-out handoff
-        // can leave one set)
         e = launch_fill_zero(cache_err(*c), Bt, s);
-        if (e == hipSuccess)
-            e = launch_fill_zero(cache_scan(*c), (int64_t)Bt * c->dims.nheads * kScanSlabs * (kScanChunks + 1), s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) return MIL_E_HIP;
     }

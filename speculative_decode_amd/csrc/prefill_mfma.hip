@@ -19,6 +19,7 @@
 // output row t (= its column) and 16 source tokens s: exactly an A operand for M X
 // once the k-slot (hf, v) <-> s correspondence is applied to how X is read from LDS.
 #include <algorithm>
+#include <atomic>
 
 #include "ssm_internal.h"
 
@@ -70,7 +71,8 @@ struct MParams {
     int slot0, nseq, batch, cont;
     int PS, nslab;         // phase 1: state rows p per workgroup, slabs per chunk-head
     // single-launch scan
-    int32_t *scan;         // handoff counters [batch][H][kScanSlabs] (zero between calls)
+    int32_t *scan;         // handoff flags [batch][H][kScanSlabs][kScanChunks]
+    int epoch;             // this call's flag value (never reused in the process)
     int32_t *err;          // [batch] device error words
     float *chain;          // [nseq][H][P/PC][nch][N*PC + 16] published chunk states (register order), E_c
 };
@@ -623,14 +625,15 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
 // All three phases in one launch for prompts of up to kScanChunks chunks, one workgroup per
 // (chunk, sequence, head, column slab), chunk-major.  The workgroup stages its chunk's B,
 // C, X and dt once, computes the chunk's own state contribution S_c = sum_s (w_s B_s) x_s^T
-// on the matrix cores and publishes it with the chunk's total decay E_c (a flag per chunk),
-// forms the intra-chunk outputs, and then folds the state entering its chunk from h0
+// on the matrix cores and publishes it with the chunk's total decay E_c (chunk 0 publishes
+// its outgoing state E_0 h0 + S_0 instead, so that it alone reads h0), forms the
+// intra-chunk outputs, raises its flag, and then folds the state entering its chunk
 // through chunks 0..c-1 in order (h <- E_i h + S_i): the operations of a sequential pass in
 // its order, so the result does not depend on timing, and no workgroup waits on a chain
-// of others, only on the publications, which come right after each chunk's S.  The last
-// workgroup of a chain to finish reading writes the final state (every chunk reads h0 from
-// the cache first) and resets the chain's flags.  Longer prompts keep the three launches
-// (their per-chunk reads of all earlier chunks would grow with the square of the count).
+// of others, only on the publications.  The last chunk writes the final state.  Flags
+// hold a per-call value (never reused in the process), so nothing needs resetting.
+// Longer prompts keep the three launches (their per-chunk reads of all earlier chunks
+// would grow with the square of the count).
 //
 // Ordering: workgroups start in chunk-major order and every one publishes before it
 // waits, so the flags a workgroup waits for are always raised; the wait is bounded in time
@@ -817,27 +820,45 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
     }
 
-    // ---- publish this chunk's own state S and decay E_c (no waiting before it) ----
+    // ---- publish: chunk 0 its outgoing state E_0 h0 + S_0 (it alone reads h0), chunks
+    // 1..nch-2 their own S_c, each with its decay E_c; the flag goes up after the
+    // intra-chunk products, which hide the stores' latency ----
     const int slot = p.slot0 + seq;
-    int32_t *flags = p.scan + (((size_t)slot * H + h) * kScanSlabs + slab) * (kScanChunks + 1);
-    const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: S in register order, then E_c
+    int32_t *flags = p.scan + (((size_t)slot * H + h) * kScanSlabs + slab) * kScanChunks;
+    const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: state in register order, then E_c
     float *aggs = p.chain + (((size_t)seq * H + h) * nps + slab) * (size_t)p.nch * AGG;
     float *cache = p.state + (size_t)(seq * H + h) * p.head_stride;
-    if (p.nch > 1) {
+    const bool has_hin = p.cont || c > 0;
+    const bool last = c == p.nch - 1;
+    f32x16 hin[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) hin[i] = f32x16{};
+    if (c == 0 && p.cont && swave) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int spt = (wave + i * 8) / NTL;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                hin[i][r] = cache[(size_t)n * P + pc0 + spt * kT + l32];
+            }
+        }
+    }
+    const bool publish = !last;
+    if (publish) {
         float *dst = aggs + (size_t)c * AGG;
         if (swave) {
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tl = wave + i * 8;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) shared_store(dst + (size_t)(tl * 16 + r) * 64 + lane, sacc[i][r]);
+                for (int r = 0; r < 16; ++r) {
+                    const float v = c == 0 ? __builtin_fmaf(Ec, hin[i][r], sacc[i][r]) : sacc[i][r];
+                    shared_store(dst + (size_t)(tl * 16 + r) * 64 + lane, v);
+                }
             }
         }
         if (tid == 0) shared_store(dst + N * PC, Ec);
-        // every wave's stores complete before the barrier, and the flag goes up after it
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) scan_store(flags + c, 1);
     }
     // ---- outputs: intra-chunk products, as in the output phase (only when y is wanted) ----
     const bool want_y = p.y != nullptr;
@@ -900,104 +921,56 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
     }
-    // ---- the state entering this chunk: h0 (or zeros) folded through chunks 0..c-1 in
-    // order, h <- E_i h + S_i, the same operations in the same order as a sequential pass,
-    // so the result does not depend on which workgroup got where first ----
-    const bool has_hin = p.cont || c > 0;
-    f32x16 hin[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) hin[i] = f32x16{};
+    if (publish) {
+        // every wave's stores complete before the barrier, and the flag goes up after it
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) scan_store(flags + c, p.epoch);
+    }
+
+    // ---- the state entering this chunk: chunk 0's outgoing state folded through chunks
+    // 1..c-1 in order, h <- E_i h + S_i: the operations of a sequential pass in its order,
+    // so the result does not depend on which workgroup got where first.  Wave 0 waits for
+    // the c flags at once (lane i polls chunk i). ----
     if (c > 0) {
-        if (tid == 0) {
+        if (wave == 0) {
             const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
-            bool late = false;
-            for (int i = 0; i < c && !late; ++i) {
-                while (scan_load(flags + i) == 0) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kScanWaitTicks) {
-                        atomicOr(p.err + slot, MIL_DEVERR_SCAN);
-                        late = true;
-                        break;
-                    }
+            while (true) {
+                const bool ok = lane >= c || scan_load(flags + lane) == p.epoch;
+                if (__all(ok)) break;
+                __builtin_amdgcn_s_sleep(2);
+                if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kScanWaitTicks) {
+                    if (lane == 0) atomicOr(p.err + slot, MIL_DEVERR_SCAN);
+                    break;
                 }
             }
         }
         __syncthreads();
-    }
-    if (swave && has_hin) {
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int tl = wave + i * 8, spt = tl / NTL;
-            if (p.cont) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                    hin[i][r] = cache[(size_t)n * P + pc0 + spt * kT + l32];
-                }
-            }
-            for (int j = 0; j < c; ++j) {
-                const float *src = aggs + (size_t)j * AGG;
-                const float Ej = shared_load(src + N * PC);
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    hin[i][r] = __builtin_fmaf(Ej, hin[i][r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
-            }
-        }
-    }
-    // ---- the final state.  Every chunk reads h0 from the cache, so it is written only
-    // once they all have: by the workgroup of the chain that finishes reading last (a
-    // counter), folding h0 through all the published chunks in order (one chunk: directly).
-    // That workgroup also resets the chain's flags and counter for the next call. ----
-    if (p.nch == 1) {
         if (swave) {
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
-                const int tl = wave + i * 8, spt = tl / NTL;
+                const int tl = wave + i * 8;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                    cache[(size_t)n * P + pc0 + spt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
-                }
-            }
-        }
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        int *sFlag = reinterpret_cast<int *>(sMid + 64);
-        if (tid == 0) {
-            const int done = __hip_atomic_fetch_add(flags + kScanChunks, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool final_one = done == p.nch - 1;
-            if (final_one) {
-                for (int i = 0; i < p.nch; ++i) scan_store(flags + i, 0);
-                scan_store(flags + kScanChunks, 0);
-            }
-            *sFlag = final_one ? 1 : 0;
-        }
-        __syncthreads();
-        if (*sFlag && swave) {
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int tl = wave + i * 8, spt = tl / NTL;
-                f32x16 hf16 = f32x16{};
-                if (p.cont) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                        hf16[r] = cache[(size_t)n * P + pc0 + spt * kT + l32];
-                    }
-                }
-                for (int j = 0; j < p.nch; ++j) {
+                for (int r = 0; r < 16; ++r) hin[i][r] = shared_load(aggs + (size_t)(tl * 16 + r) * 64 + lane);
+                for (int j = 1; j < c; ++j) {
                     const float *src = aggs + (size_t)j * AGG;
                     const float Ej = shared_load(src + N * PC);
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        hf16[r] = __builtin_fmaf(Ej, hf16[r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
+                        hin[i][r] = __builtin_fmaf(Ej, hin[i][r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
                 }
+            }
+        }
+    }
+    // ---- the final state, from the last chunk (nothing reads h0 after chunk 0 has) ----
+    if (last && swave) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                    cache[(size_t)n * P + pc0 + spt * kT + l32] = hf16[r];
-                }
+        for (int i = 0; i < TPW; ++i) {
+            const int spt = (wave + i * 8) / NTL;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                cache[(size_t)n * P + pc0 + spt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
             }
         }
     }
@@ -1079,6 +1052,19 @@ size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 +
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr int64_t kOutItemsTarget = 256;  // output workgroups wanted (one per compute unit)
 
+// Flag value of one single-launch call: a process-wide counter, so a flag left by any
+// earlier call (the flags are zero when a cache is set up) never equals a later call's.
+int next_scan_epoch() {
+    static std::atomic<int> counter{0};
+    int e = counter.fetch_add(1) + 1;
+    while (e <= 0) {  // after 2^31 calls: start again at 1
+        int expected = e - 1;
+        counter.compare_exchange_strong(expected, 1);
+        e = counter.fetch_add(1) + 1;
+    }
+    return e;
+}
+
 // Column slab width of the output work (and of the single launch): P split until the grid
 // has a workgroup per compute unit.
 int slab_width(int nseq, int nch, int H, int P) {
@@ -1157,6 +1143,7 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     const void *kf = scan_kernel(chunk, p.nch, p.N, pc);
     if (kf) {
         p.scan = cache_scan(c);
+        p.epoch = next_scan_epoch();
         p.err = cache_err(c);
         p.chain = static_cast<float *>(ws);
         hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);

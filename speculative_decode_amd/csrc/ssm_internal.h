@@ -44,8 +44,8 @@ inline void *cache_pend_dt(const CacheImpl &c) { return c.base + c.lay.pend_dt_o
 inline int32_t *cache_pos(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.pos_off); }
 inline int32_t *cache_pending(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.pending_off); }
 inline int32_t *cache_err(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.err_off); }
-// single-launch prefill handoff flags: [slot][head][kScanSlabs][kScanChunks + 1] (a flag
-// per chunk, then a counter), zero between calls
+// single-launch prefill handoff flags: [slot][head][kScanSlabs][kScanChunks], zeroed when
+// the cache is set up; each call writes its own (process-unique) value
 constexpr int kScanSlabs = 8;
 constexpr int kScanChunks = 8;  // chunks per prompt the single-launch prefill handles
 inline int32_t *cache_scan(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.scan_off); }

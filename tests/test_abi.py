@@ -65,7 +65,7 @@ def test_layout_is_head_major_and_aligned(lib, shape, dtype, k_max):
     assert lay.state_head_stride < N * P * 4 + 256
     # regions in order, each big enough, no overlap
     sizes = [Bt * H * lay.state_head_stride, Bt * k_max * H * P * e, Bt * k_max * G * N * e,
-             Bt * k_max * H * e, Bt * 4, Bt * 4, Bt * 4, Bt * H * 8 * 9 * 4]
+             Bt * k_max * H * e, Bt * 4, Bt * 4, Bt * 4, Bt * H * 8 * 8 * 4]
     for a, b, sz in zip(offs, offs[1:], sizes):
         assert b - a >= sz
     assert lib.mil_ssm_cache_bytes(ctypes.byref(d), k_max, dtype) == lay.bytes
