@@ -693,14 +693,6 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     float *sTot = sWst + Q;                         // [8]
     float *sMid = sTot + 8;                         // [8][8]
 
-    if (blockIdx.x == 0) {
-        for (int i = tid; i < p.batch; i += NT) {
-            const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
-            if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
-            if (mine || p.cont) p.pending[i] = 0;
-        }
-    }
-
     const size_t tok0 = (size_t)seq * p.L + c0;
     const float Ah = p.A[h], Dh = p.D[h];
     const int nt = Q / kT;
@@ -708,22 +700,18 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     const bool active = I * kT < len;
     const int t = I * kT + l32;
 
-    // ---- staging, as in the output phase ----
-    bf16x8 cf[NK];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-        cf[kk] = (active && t < len)
-                     ? *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + t) * G + g) * N + kk * 16 + hf * 8)
-                     : bf16x8{};
-    const float dv = tid < Q && tid < len ? bf2f(p.dt[(tok0 + tid) * H + h]) : 0.f;
+    // ---- staging: B, X and dt first (the chunk state needs them), then the C rows (only
+    // the outputs need them), so that writing B and X to LDS waits for them alone ----
+    // every staging load is unconditional (rows past the chunk end clamped, their values
+    // zeroed after), so no branch makes the compiler wait for one load before the next
+    const float dv0 = bf2f(p.dt[(tok0 + min(tid, len - 1)) * H + h]);
     constexpr int BI = N / 16;
     uint4 vb[BI];
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
         const int it = tid + j * NT;
         const int sr = it / (N / 8), ng = it % (N / 8);
-        vb[j] = sr < len ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + sr) * G + g) * N + ng * 8)
-                         : make_uint4(0, 0, 0, 0);
+        vb[j] = *reinterpret_cast<const uint4 *>(p.B + ((tok0 + min(sr, len - 1)) * G + g) * N + ng * 8);
     }
     constexpr int XI = (PC + 63) / 64;
     uint4 vx[XI][4];
@@ -734,11 +722,32 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int sr = sq * 4 + r;
-            vx[j][r] = (it < (Q / 4) * (PC / 8) && sr < len)
-                           ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + sr) * H + h) * P + pc0 + pg * 8)
-                           : make_uint4(0, 0, 0, 0);
+            vx[j][r] = *reinterpret_cast<const uint4 *>(p.x + ((tok0 + min(sr, len - 1)) * H + h) * P + pc0 +
+                                                         min(pg, PC / 8 - 1) * 8);
         }
     }
+    asm volatile("" ::: "memory");  // keep the C loads after the others in issue order
+    bf16x8 cf[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+        cf[kk] = *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + min(t, len - 1)) * G + g) * N + kk * 16 + hf * 8);
+    asm volatile("" ::: "memory");
+    const float dv = tid < len ? dv0 : 0.f;
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int sr = (tid + j * NT) / (N / 8);
+        if (sr >= len) vb[j] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+        const int sq = (tid + j * NT) % (Q / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (sq * 4 + r >= len) vx[j][r] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+        if (!(active && t < len)) cf[kk] = bf16x8{};
     if (tid < Q) {
         sDt[tid] = dv;
         sDtA[tid] = dv * Ah;
@@ -974,7 +983,16 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             }
         }
     }
-    if (p.y == nullptr) return;
+    if (p.y == nullptr) {
+        if (blockIdx.x == 0) {
+            for (int i = tid; i < p.batch; i += NT) {
+                const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
+                if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
+                if (mine || p.cont) p.pending[i] = 0;
+            }
+        }
+        return;
+    }
     if (has_hin) {
         __syncthreads();  // every wave is done with B and X^T: the carried state goes there
         if (swave) {
@@ -1023,6 +1041,13 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[pt][r] = __builtin_fmaf(ein[r], acc2[pt][r], acc[pt][r]);
             }
+        }
+    }
+    if (blockIdx.x == 0) {  // the slots' bookkeeping, off the start of the critical chunk
+        for (int i = tid; i < p.batch; i += NT) {
+            const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
+            if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
+            if (mine || p.cont) p.pending[i] = 0;
         }
     }
     if (!active) return;
