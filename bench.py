@@ -13,7 +13,10 @@ Printed JSON line:
   hbm_gbs              verify's algorithmic bytes / verify kernel time
   ms_per_step          whole step (prefill + verify + commit), HIP events
   roofline             for the kernel with the largest time per step (HIP events around
-                       its launches, recorded by the library's trace hook)
+                       its launches, recorded by the library's trace hook), against the
+                       published peaks and against ceilings measured in the same run (a
+                       512 MiB copy, an 8192^3 bf16 matrix product), with the fraction of
+                       the attainable roofline max(bytes/8 TB/s, flops/peak) / time
   cpu_baseline         the CPU oracle on a bounded sample of the same step
 """
 from __future__ import annotations
@@ -400,6 +403,42 @@ def run_gpu(args, w):
 
 # --------------------------------------------------------------------------- CPU baseline
 
+def measured_peaks():
+    """Measured ceilings on this GPU, beside the published peaks: a plain 512 MiB
+    device-to-device copy (read + write bytes / time) and a large bf16 matrix product
+    through torch (hipBLASLt / rocBLAS) for the matrix-core rate."""
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return copy_gbs, gemm_tflops
+
+
 def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
     """The oracle, as it stands, on the same step (prefill + verify + commit) of the same
     shapes, repeated on one seeded sample until about budget_s seconds of CPU work."""
@@ -584,6 +623,15 @@ def main():
                 roof["traffic"] = ent["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             pass
+    # measured ceilings and the fraction of the attainable roofline: the larger of the
+    # byte time and the flop time at the published peaks, over the kernel's time
+    copy_gbs, gemm_tflops = measured_peaks()
+    roof["measured_copy_gbs"] = copy_gbs
+    roof["measured_bf16_gemm_tflops"] = gemm_tflops
+    roof["frac_of_measured"] = (byt / t / 1e9 / copy_gbs if roof["bound"] == "hbm"
+                                else fl / t / 1e12 / gemm_tflops)
+    t_attain = max(byt / (HBM_PEAK_GBS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12 if bf16 else F32_PEAK_TFLOPS * 1e12))
+    roof["attainable_frac"] = t_attain / t
     kern = {k: dict(ms=g["ktime"][k], GBps=g["work"][k][0] / (g["ktime"][k] * 1e-3) / 1e9,
                     TFLOPs=g["work"][k][1] / (g["ktime"][k] * 1e-3) / 1e12) for k in g["ktime"]}
     cfg = {"workload": w.name, "batch": Bt, "heads": w.H, "headdim": w.P, "dstate": w.N, "groups": w.G,
