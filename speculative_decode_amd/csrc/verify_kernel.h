@@ -107,7 +107,8 @@ inline size_t verify_lds_floats(int N, int Pc, int K, int kmax, int S) {
 }
 constexpr size_t kVerifyLdsMax = 160 * 1024;
 
-// Shape policy.  Whole rows per workgroup (CS = 1) whenever LDS allows: each workgroup
+// General shape search (after the preference for <= 8 waves in shape_for).  Whole rows
+// per workgroup (CS = 1) whenever LDS allows: each workgroup
 // then streams one contiguous N x P block, which HBM serves better than the strided
 // halves or quarters of rows that column tiles read.  Within that, the fewest waves with
 // at most kRowsTarget rows per lane and at least kWavesTarget waves in the grid, else the
@@ -116,10 +117,28 @@ constexpr size_t kVerifyLdsMax = 160 * 1024;
 constexpr int kRowsTarget = 8;
 constexpr int64_t kWavesTarget = 2048;
 
-// Launch shape for K drafts with up to kmax pending rows; S = 0 when none fits.
+// Launch shape for K drafts with up to kmax pending rows; S = 0 when none fits.  First
+// workgroups of at most 8 waves (16-wave workgroups measured slower: their cross-wave
+// reduction and barriers cost more than the extra waves bring), whole rows preferred:
+// the first shape with at most kRowsTarget rows per lane and kWavesTarget waves, else
+// with a quarter of that (few sequences: a single sequence's 32 heads); then the general
+// search below.
 inline Shape shape_for(int batch, int H, int P, int N, int K, int kmax) {
     Shape best{0, 0, 0};
     if (P < 16 || P > 256 || (P & (P - 1)) || N < 16 || N > 256 || (N & (N - 1))) return best;
+    for (int64_t target : {kWavesTarget, kWavesTarget / 4}) {
+        for (int cs = 1; cs <= 4 && P / cs >= 16; cs *= 2) {
+            const int Pc = P / cs, RGW = 256 / Pc;
+            for (int S = 1; S <= 8; S *= 2) {
+                const int rg = S * RGW;
+                if (rg > N) break;
+                const int rows = N / rg;
+                if (rows > kRowsTarget || S * 64 > max_threads(rows)) continue;
+                if (verify_lds_floats(N, Pc, K, kmax, S) * sizeof(float) > kVerifyLdsMax) continue;
+                if ((int64_t)batch * H * cs * S >= target) return Shape{S, rows, cs};
+            }
+        }
+    }
     for (int cs = 1; cs <= 4 && P / cs >= 16; cs *= 2) {
         const int Pc = P / cs;
         const int RGW = 256 / Pc;  // row groups per wave (Pc/4 lanes per row)
