@@ -41,12 +41,27 @@ PREFILL_KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "prefill_scan
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_hash() -> str:
+# the sources each kernel family is compiled from (besides the shared headers): a stored
+# traffic figure stays valid while these are unchanged
+SHARED_SOURCES = ["ssm_internal.h", "../../include/mil_ssm.h"]
+FAMILY_SOURCES = {
+    "verify": ["verify_kernel.h", "verify.hip", "verify_bf16.hip", "verify_f32.hip"],
+    "commit": ["commit.hip"], "accept": ["commit.hip"],
+    "project": ["project.hip"],
+    "prefill_state": ["prefill_mfma.hip", "prefill.hip"], "prefill_pass": ["prefill_mfma.hip", "prefill.hip"],
+    "prefill_out": ["prefill_mfma.hip", "prefill.hip"], "prefill_scan": ["prefill_mfma.hip"],
+}
+
+
+def source_hash(family: str | None = None) -> str:
+    """Hash of the kernel sources: of one family's files (and the shared headers), or of
+    every file under csrc/ when family is None."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "speculative_decode_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    files = sorted(os.listdir(d)) if family is None else SHARED_SOURCES + FAMILY_SOURCES[family]
+    for f in files:
         with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+            h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -535,7 +550,7 @@ def traffic(fetch_db, write_db, workload, copy_mib):
     for k in fe:
         if k != "copy" and k in wr:
             out[f"{k}/{workload}"] = {"fetch_bytes": fe[k] * kf, "write_bytes": wr[k] * kw,
-                                      "bytes_per_launch": fe[k] * kf + wr[k] * kw, "source_sha": source_hash()}
+                                      "bytes_per_launch": fe[k] * kf + wr[k] * kw, "source_sha": source_hash(k)}
     return out
 
 
@@ -619,7 +634,7 @@ def main():
         try:
             tr = json.load(open(TRAFFIC_FILE))
             ent = tr.get(f"{dom}/{args.workload}")
-            if ent and ent.get("source_sha") == source_hash():
+            if ent and ent.get("source_sha") == source_hash(dom):
                 roof["traffic"] = ent["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             pass
