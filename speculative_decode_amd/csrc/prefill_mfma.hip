@@ -660,6 +660,26 @@ __device__ __forceinline__ void shared_store(float *q, float v) {
     __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+constexpr size_t kLdsMax = 160 * 1024;
+constexpr int kScanQ = 256;  // the single-launch kernel's chunk length
+
+// LDS of the single-launch kernel: the staged B rows and X^T (later the carried state's
+// hi / lo rows), seven per-token float arrays, the tile totals and the 8 x 8 tile factors;
+// then, where it fits, the partial chunk-state tiles of the token parts that their
+// owners add (one 32 x 32 fp32 tile per part other than the owner's, per state tile).
+constexpr size_t scan_base_lds(int Q, int N, int PC) {
+    return ((size_t)Q * (N + 8) + (size_t)PC * (Q + 8) > (size_t)PC * (N * 2 + 8)
+                ? (size_t)Q * (N + 8) + (size_t)PC * (Q + 8)
+                : (size_t)PC * (N * 2 + 8)) * 2 +
+           7 * (size_t)Q * 4 + 8 * 4 + 64 * 4 + 16;
+}
+constexpr size_t scan_xchg_bytes(int N, int PC) {
+    return (size_t)(PC / kT) * (8 / (N / kT) - 1) * (N / kT) * kT * kT * 4;
+}
+constexpr bool scan_split_tokens(int N, int PC) {
+    return scan_base_lds(kScanQ, N, PC) + scan_xchg_bytes(N, PC) <= kLdsMax;
+}
+
 template <int N, int PC>
 __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     extern __shared__ __align__(16) char lds[];
@@ -771,14 +791,21 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     __syncthreads();
     chunk_factors(sDtA, len, sR, sSuf, sTot, tid, NT);
     const int ntile = (len + kT - 1) / kT;
+    // the tile totals in registers (two LDS reads), summed in ascending tile order as a
+    // sequential loop would; totals past the last tile are never selected
+    const float4 tq0 = *reinterpret_cast<const float4 *>(sTot), tq1 = *reinterpret_cast<const float4 *>(sTot + 4);
+    const float tv[8] = {tq0.x, tq0.y, tq0.z, tq0.w, tq1.x, tq1.y, tq1.z, tq1.w};
     for (int s = tid; s < Q; s += NT) {
         if (s < len) {
+            const int ti = s / kT;
             sColf[s] = sDt[s] * __expf(sSuf[s]);
             float m = sR[s];
-            for (int q = 0; q < s / kT; ++q) m += sTot[q];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) m = q < ti ? m + tv[q] : m;
             sEin[s] = __expf(m);
             float e = sSuf[s];  // decay from s to the chunk end: rest of s's tile, then later tiles
-            for (int q = s / kT + 1; q < ntile; ++q) e += sTot[q];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) e = (q > ti && q < ntile) ? e + tv[q] : e;
             sWst[s] = __expf(e) * sDt[s];
         } else {
             sWst[s] = 0.f;  // tokens past the chunk end carry no weight
@@ -787,46 +814,115 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     if (tid < 64) {
         const int Ii = tid / 8, J = tid % 8;
         float m = 0.f;
-        for (int q = J + 1; q < Ii; ++q) m += sTot[q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = (q > J && q < Ii) ? m + tv[q] : m;
         sMid[tid] = (J < Ii && Ii < ntile) ? __expf(m) : 0.f;
     }
-    __syncthreads();
     float ttot = 0.f;
-    for (int q = 0; q < ntile; ++q) ttot += sTot[q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ttot = q < ntile ? ttot + tv[q] : ttot;
     const float Ec = __expf(ttot);
+    __syncthreads();
 
-    // ---- the chunk's own state S[n][p] (this slab), n rows from B^T read column-wise out
-    // of the B rows, (w X) split hi + lo; lane: column p, register r: row 8(r/4) + 4hf + r%4
-    f32x16 sacc[TPW];
+    // ---- the chunk's own state S[n][p] (this slab): S = sum_s (w_s B_s) x_s^T with
+    // A operand (w B)^T and B operand X^T (as staged).  The rows n of B^T come off the
+    // matrix cores: the product D = B_blk E with E the identity holds, per lane, one
+    // column n of a 32-token block over 16 tokens (registers r: tokens 8(r/4) + 4hf + r%4),
+    // which is the A-operand layout once scaled by w_s and split hi + lo.  The waves
+    // sharing a row tile take consecutive parts of the tokens (when LDS has room to add
+    // their partial tiles), each part over every column tile, then the partials are added
+    // in part order; otherwise each wave covers all tokens for the tiles it owns.
+    // Wave w owns tiles tl = w + 8i (row tile w % NTL, column tile tl / NTL). ----
+    constexpr bool SPLIT = scan_split_tokens(N, PC);
+    constexpr int WPN = 8 / NTL;              // waves per row tile
+    constexpr int SP = SPLIT ? WPN : 1;       // token parts
+    constexpr int NPT = SPLIT ? PT : TPW;     // column tiles a wave accumulates
+    const bool swave = wave < STILES;         // owns a tile
+    const int snt = wave % NTL;               // this wave's row tile
+    const int jpart = SPLIT ? wave / NTL : 0; // its token part
+    f32x16 part[NPT];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) sacc[i] = f32x16{};
-    const bool swave = wave < STILES;  // fewer tiles than waves: the extra waves idle here
-    const int snt = wave % NTL;        // this wave's row tile (shared by its tiles)
-    if (swave) {
-        for (int ks = 0; ks < (len + 15) / 16; ++ks) {
-            const int s0 = ks * 16 + 8 * hf;
-            bf16x8 a;
+    for (int i = 0; i < NPT; ++i) part[i] = f32x16{};
+    if (SPLIT || swave) {
+        bf16x8 eye[2];  // identity: slot v of k-step kk is 1 where 16 kk + 8 hf + v = l32
 #pragma unroll
-            for (int v = 0; v < 8; ++v) a[v] = sB[(s0 + v) * BS + snt * kT + l32];
-            const float4 w0 = *reinterpret_cast<const float4 *>(sWst + s0);
-            const float4 w1 = *reinterpret_cast<const float4 *>(sWst + s0 + 4);
-            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int spt = (wave + i * 8) / NTL;
-                const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(sXT + (spt * kT + l32) * XS + s0);
-                bf16x8 bh, bl;
+            for (int v = 0; v < 8; ++v) eye[kk][v] = static_cast<bf16>(16 * kk + 8 * hf + v == l32 ? 1.f : 0.f);
+        const int bpp = (Q / kT) / SP;
+        const int blk1 = min((len + kT - 1) / kT, (jpart + 1) * bpp);
+        for (int blk = jpart * bpp; blk < blk1; ++blk) {
+            const int s0 = blk * kT;
+            f32x16 tb = f32x16{};
 #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    bf16 x1, x2;
-                    split(wv[v] * bf2f(xv[v]), x1, x2);
-                    bh[v] = x1;
-                    bl[v] = x2;
+            for (int kk = 0; kk < 2; ++kk)
+                tb = mfma(*reinterpret_cast<const bf16x8 *>(sB + (s0 + l32) * BS + snt * kT + kk * 16 + 8 * hf), eye[kk],
+                          tb);
+            bf16x8 ah[2], al[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(sWst + s0 + 8 * q + 4 * hf);
+                const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                for (int u2 = 0; u2 < 4; ++u2) {
+                    const int r = 4 * q + u2;
+                    bf16 a1, b1;
+                    split(tb[r] * wv[u2], a1, b1);
+                    ah[r / 8][r % 8] = a1;
+                    al[r / 8][r % 8] = b1;
                 }
-                sacc[i] = mfma(a, bh, sacc[i]);
-                sacc[i] = mfma(a, bl, sacc[i]);
+            }
+            const bf16 *xr = sXT + l32 * XS + s0 + 4 * hf;
+            if (SPLIT) {
+                accumulate_mx<PT>(part, ah, al, xr, XS);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NPT; ++i) {
+                    const int pt = (wave + i * 8) / NTL;
+                    accumulate_mx<1>(part + i, ah, al, xr + pt * kT * XS, XS);
+                }
             }
         }
+    }
+    f32x16 sacc[TPW];
+    if (SPLIT) {
+        // column tile pt of row tile snt belongs to wave snt + NTL (pt % WPN), as its tile
+        // i = pt / WPN; every other part goes through LDS, and the owner adds the parts in
+        // token order
+        float *sXg = reinterpret_cast<float *>(lds + scan_base_lds(Q, N, PC));
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int own = pt % WPN;
+            if (jpart != own) {
+                const int slot = (pt * (SP - 1) + (jpart - own - 1 + SP) % SP) * NTL + snt;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sXg[(slot * 16 + r) * 64 + lane] = part[pt][r];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int own = pt % WPN;
+            if (jpart == own) {
+                f32x16 sum = f32x16{};
+#pragma unroll
+                for (int j = 0; j < SP; ++j) {
+                    if (j == own) {
+                        sum = j == 0 ? part[pt] : sum + part[pt];
+                    } else {
+                        const int slot = (pt * (SP - 1) + (j - own - 1 + SP) % SP) * NTL + snt;
+                        f32x16 v;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) v[r] = sXg[(slot * 16 + r) * 64 + lane];
+                        sum = j == 0 ? v : sum + v;
+                    }
+                }
+                sacc[pt / WPN] = sum;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) sacc[i] = part[i];
     }
 
     // ---- publish: chunk 0 its outgoing state E_0 h0 + S_0 (it alone reads h0), chunks
@@ -1064,8 +1160,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 }
 
 size_t scan_lds_bytes(int Q, int N, int P) {
-    const size_t big = std::max((size_t)Q * (N + 8) + (size_t)P * (Q + 8), (size_t)P * (N * 2 + 8)) * 2;
-    return big + 7 * Q * 4 + 8 * 4 + 64 * 4 + 16;
+    return scan_base_lds(Q, N, P) + (scan_split_tokens(N, P) ? scan_xchg_bytes(N, P) : 0);
 }
 
 size_t out_lds_bytes(int Q, int N, int P) {
@@ -1074,7 +1169,6 @@ size_t out_lds_bytes(int Q, int N, int P) {
 }
 size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 + (4 * 256 + 8) * 4; }
 
-constexpr size_t kLdsMax = 160 * 1024;
 constexpr int64_t kOutItemsTarget = 256;  // output workgroups wanted (one per compute unit)
 
 // Flag value of one single-launch call: a process-wide counter, so a flag left by any

@@ -8,6 +8,8 @@ bit for bit.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -191,6 +193,34 @@ def test_prefill_back_to_back_single_launch(L):
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
     assert y_err(np.concatenate(ys), ry) <= TOL[synth.BF16]
     assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
+
+
+# (N, column slab width): the slab follows from the number of chunk-heads (P halved until
+# there is a workgroup per compute unit), so (sequences, heads) pick it: with P = 128 and
+# 4 chunks, 64 / 32 / 16 sequence-heads give slabs of 128 / 64 / 32 columns.  The slabs of
+# 32 and 64 columns split each state tile's tokens over waves; 128 keeps them whole.
+SCAN_CONFIGS = [(64, 32), (64, 64), (64, 128), (128, 32), (128, 64), (128, 128)]
+
+
+@pytest.mark.parametrize("N,pc", SCAN_CONFIGS, ids=[f"N{n}_pc{c}" for n, c in SCAN_CONFIGS])
+def test_prefill_single_launch_configs(N, pc):
+    """Every state size and column slab of the single-launch prefill, on a ragged last
+    chunk (1000 tokens = 3 x 256 + 232)."""
+    from speculative_decode_amd import _lib
+    H, P, G, L = 8, 128, 2, 1000
+    Bt = {128: 8, 64: 4, 32: 2}[pc]
+    rng = np.random.default_rng(4300 + N + pc)
+    layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, synth.BF16)
+    cache = SSMCache(Bt, H, P, N, G, 4, synth.BF16)
+    mask = _lib.lib().mil_ssm_prefill_kernels(ctypes.byref(cache.desc), Bt, L, 256)
+    assert mask == 1 << _lib.TRACE["prefill_scan"], mask
+    print(f"single-launch prefill N={N} slab={pc} batch={Bt}", flush=True)
+    y = sync_np(cache.prefill(*dev_tokens(tok), *dev_layer(layer), chunk=256))
+    assert cache.status() == -1
+    ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
+    ey, es = y_err(y, ry), state_err(logical_state(cache), rs)
+    print(f"  y {ey:.2e} state {es:.2e}")
+    assert ey <= TOL[synth.BF16] and es <= TOL[synth.BF16]
 
 
 # --------------------------------------------------------------------------- verify / commit
