@@ -663,18 +663,18 @@ __device__ __forceinline__ void shared_store(float *q, float v) {
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr int kScanQ = 256;  // the single-launch kernel's chunk length
 
-// LDS of the single-launch kernel: the staged B rows and X^T (later the carried state's
-// hi / lo rows), seven per-token float arrays, the tile totals and the 8 x 8 tile factors;
-// then, where it fits, the partial chunk-state tiles of the token parts that their
-// owners add (one 32 x 32 fp32 tile per part other than the owner's, per state tile).
+// LDS of the single-launch kernel: the staged B rows and X^T, seven per-token float
+// arrays, the tile totals, the 8 x 8 tile factors and a counter; then an area that first
+// holds the partial chunk-state tiles of the token parts that their owners add (one
+// 32 x 32 fp32 tile per part other than the owner's, per state tile) and later the
+// carried state's hi / lo rows.
 constexpr size_t scan_base_lds(int Q, int N, int PC) {
-    return ((size_t)Q * (N + 8) + (size_t)PC * (Q + 8) > (size_t)PC * (N * 2 + 8)
-                ? (size_t)Q * (N + 8) + (size_t)PC * (Q + 8)
-                : (size_t)PC * (N * 2 + 8)) * 2 +
-           7 * (size_t)Q * 4 + 8 * 4 + 64 * 4 + 16;
+    return ((size_t)Q * (N + 8) + (size_t)PC * (Q + 8)) * 2 + 7 * (size_t)Q * 4 + 8 * 4 + 64 * 4 + 16;
 }
 constexpr size_t scan_xchg_bytes(int N, int PC) {
-    return (size_t)(PC / kT) * (8 / (N / kT) - 1) * (N / kT) * kT * kT * 4;
+    return (size_t)(PC / kT) * (8 / (N / kT) - 1) * (N / kT) * kT * kT * 4 > (size_t)PC * (N * 2 + 8) * 2
+               ? (size_t)(PC / kT) * (8 / (N / kT) - 1) * (N / kT) * kT * kT * 4
+               : (size_t)PC * (N * 2 + 8) * 2;
 }
 constexpr bool scan_split_tokens(int N, int PC) {
     return scan_base_lds(kScanQ, N, PC) + scan_xchg_bytes(N, PC) <= kLdsMax;
@@ -701,12 +701,10 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     constexpr int PT = PC / kT, NK = N / 16, HS = N * 2 + 8;
     constexpr int NTL = N / kT;                        // state row tiles
     constexpr int STILES = NTL * PT;                   // state tiles of this slab
-    constexpr int TPW = STILES >= 8 ? STILES / 8 : 1;  // per wave (8 waves)
 
     bf16 *sB = reinterpret_cast<bf16 *>(lds);
     bf16 *sXT = sB + Q * BS;
-    bf16 *sH = reinterpret_cast<bf16 *>(lds);
-    const size_t big = max((size_t)Q * BS + (size_t)PC * XS, (size_t)PC * HS) * 2;
+    const size_t big = ((size_t)Q * BS + (size_t)PC * XS) * 2;
     float *sDt = reinterpret_cast<float *>(lds + big);
     float *sDtA = sDt + Q, *sR = sDtA + Q, *sSuf = sR + Q, *sColf = sSuf + Q, *sEin = sColf + Q;
     float *sWst = sEin + Q;                         // [Q] dt_s * decay(s, chunk end)
@@ -772,6 +770,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         sDt[tid] = dv;
         sDtA[tid] = dv * Ah;
     }
+    if (tid == 0) *reinterpret_cast<int *>(sMid + 64) = 0;  // the light waves' counter
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
         const int it = tid + j * NT;
@@ -833,17 +832,14 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     // their partial tiles), each part over every column tile, then the partials are added
     // in part order; otherwise each wave covers all tokens for the tiles it owns.
     // Wave w owns tiles tl = w + 8i (row tile w % NTL, column tile tl / NTL). ----
-    constexpr bool SPLIT = scan_split_tokens(N, PC);
-    constexpr int WPN = 8 / NTL;              // waves per row tile
-    constexpr int SP = SPLIT ? WPN : 1;       // token parts
-    constexpr int NPT = SPLIT ? PT : TPW;     // column tiles a wave accumulates
-    const bool swave = wave < STILES;         // owns a tile
-    const int snt = wave % NTL;               // this wave's row tile
-    const int jpart = SPLIT ? wave / NTL : 0; // its token part
-    f32x16 part[NPT];
+    static_assert(scan_split_tokens(N, PC), "the single launch splits each row tile's tokens over its waves");
+    constexpr int SP = 8 / NTL;    // token parts: the waves of one row tile
+    const int snt = wave % NTL;    // this wave's row tile
+    const int jpart = wave / NTL;  // its token part
+    f32x16 part[PT];
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) part[i] = f32x16{};
-    if (SPLIT || swave) {
+    for (int i = 0; i < PT; ++i) part[i] = f32x16{};
+    {
         bf16x8 eye[2];  // identity: slot v of k-step kk is 1 where 16 kk + 8 hf + v = l32
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -872,62 +868,57 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                     al[r / 8][r % 8] = b1;
                 }
             }
-            const bf16 *xr = sXT + l32 * XS + s0 + 4 * hf;
-            if (SPLIT) {
-                accumulate_mx<PT>(part, ah, al, xr, XS);
-            } else {
-#pragma unroll
-                for (int i = 0; i < NPT; ++i) {
-                    const int pt = (wave + i * 8) / NTL;
-                    accumulate_mx<1>(part + i, ah, al, xr + pt * kT * XS, XS);
-                }
-            }
+            accumulate_mx<PT>(part, ah, al, sXT + l32 * XS + s0 + 4 * hf, XS);
         }
     }
-    f32x16 sacc[TPW];
-    if (SPLIT) {
-        // column tile pt of row tile snt belongs to wave snt + NTL (pt % WPN), as its tile
-        // i = pt / WPN; every other part goes through LDS, and the owner adds the parts in
-        // token order
-        float *sXg = reinterpret_cast<float *>(lds + scan_base_lds(Q, N, PC));
+    // ---- the chunk's state tiles belong to the four light waves (w < 4: the waves with
+    // the short causal rows of the intra-chunk products), which publish them and raise
+    // the chunk's flag while the other four run their longer rows: tile (row tile snt,
+    // column tile pt) to wave snt + NTL (pt % LW), as its tile i = pt / LW.  The other
+    // token parts' partial tiles go through LDS, and the owner adds the parts in token
+    // order. ----
+    constexpr int LW = 4 / NTL;                   // token parts held by light waves
+    constexpr int TPWL = PT >= LW ? PT / LW : 1;  // tiles per owning wave
+    const bool light = wave < 4;
+    const bool owner = light && jpart < PT;
+    float *sXg = reinterpret_cast<float *>(lds + scan_base_lds(Q, N, PC));
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int own = pt % WPN;
-            if (jpart != own) {
-                const int slot = (pt * (SP - 1) + (jpart - own - 1 + SP) % SP) * NTL + snt;
+    for (int pt = 0; pt < PT; ++pt) {
+        const int own = pt % LW;
+        if (jpart != own) {
+            const int xs = (pt * (SP - 1) + (jpart - own - 1 + SP) % SP) * NTL + snt;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sXg[(slot * 16 + r) * 64 + lane] = part[pt][r];
-            }
+            for (int r = 0; r < 16; ++r) sXg[(xs * 16 + r) * 64 + lane] = part[pt][r];
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    f32x16 sacc[TPWL];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int own = pt % WPN;
-            if (jpart == own) {
-                f32x16 sum = f32x16{};
+    for (int i = 0; i < TPWL; ++i) sacc[i] = f32x16{};
 #pragma unroll
-                for (int j = 0; j < SP; ++j) {
-                    if (j == own) {
-                        sum = j == 0 ? part[pt] : sum + part[pt];
-                    } else {
-                        const int slot = (pt * (SP - 1) + (j - own - 1 + SP) % SP) * NTL + snt;
-                        f32x16 v;
+    for (int pt = 0; pt < PT; ++pt) {
+        const int own = pt % LW;
+        if (jpart == own) {
+            f32x16 sum = f32x16{};
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) v[r] = sXg[(slot * 16 + r) * 64 + lane];
-                        sum = j == 0 ? v : sum + v;
-                    }
+            for (int j = 0; j < SP; ++j) {
+                if (j == own) {
+                    sum = j == 0 ? part[pt] : sum + part[pt];
+                } else {
+                    const int xs = (pt * (SP - 1) + (j - own - 1 + SP) % SP) * NTL + snt;
+                    f32x16 v;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) v[r] = sXg[(xs * 16 + r) * 64 + lane];
+                    sum = j == 0 ? v : sum + v;
                 }
-                sacc[pt / WPN] = sum;
             }
+            sacc[pt / LW] = sum;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) sacc[i] = part[i];
     }
 
     // ---- publish: chunk 0 its outgoing state E_0 h0 + S_0 (it alone reads h0), chunks
-    // 1..nch-2 their own S_c, each with its decay E_c; the flag goes up after the
-    // intra-chunk products, which hide the stores' latency ----
+    // 1..nch-2 their own S_c, each with its decay E_c.  Each light wave waits for its own
+    // stores, then counts itself in LDS; the fourth raises the flag. ----
     const int slot = p.slot0 + seq;
     int32_t *flags = p.scan + (((size_t)slot * H + h) * kScanSlabs + slab) * kScanChunks;
     const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: state in register order, then E_c
@@ -935,35 +926,44 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     float *cache = p.state + (size_t)(seq * H + h) * p.head_stride;
     const bool has_hin = p.cont || c > 0;
     const bool last = c == p.nch - 1;
-    f32x16 hin[TPW];
+    const bool publish = !last;
+    int *sCnt = reinterpret_cast<int *>(sMid + 64);
+    f32x16 hin[TPWL];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) hin[i] = f32x16{};
-    if (c == 0 && p.cont && swave) {
+    for (int i = 0; i < TPWL; ++i) hin[i] = f32x16{};
+    if (c == 0 && p.cont && owner) {
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int spt = (wave + i * 8) / NTL;
+        for (int i = 0; i < TPWL; ++i) {
+            const int pt = jpart + LW * i;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                hin[i][r] = cache[(size_t)n * P + pc0 + spt * kT + l32];
+                hin[i][r] = cache[(size_t)n * P + pc0 + pt * kT + l32];
             }
         }
     }
-    const bool publish = !last;
-    if (publish) {
-        float *dst = aggs + (size_t)c * AGG;
-        if (swave) {
+    if (light) {
+        if (publish) {
+            float *dst = aggs + (size_t)c * AGG;
+            if (owner) {
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int tl = wave + i * 8;
+                for (int i = 0; i < TPWL; ++i) {
+                    const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float v = c == 0 ? __builtin_fmaf(Ec, hin[i][r], sacc[i][r]) : sacc[i][r];
-                    shared_store(dst + (size_t)(tl * 16 + r) * 64 + lane, v);
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = c == 0 ? __builtin_fmaf(Ec, hin[i][r], sacc[i][r]) : sacc[i][r];
+                        shared_store(dst + (size_t)(tl * 16 + r) * 64 + lane, v);
+                    }
                 }
             }
+            if (tid == 0) shared_store(dst + N * PC, Ec);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
         }
-        if (tid == 0) shared_store(dst + N * PC, Ec);
+        // this wave has also read its partial tiles: the exchange area is free of it
+        if (lane == 0) {
+            const int before = atomicAdd(sCnt, 1);
+            if (publish && before == 3) scan_store(flags + c, p.epoch);
+        }
     }
     // ---- outputs: intra-chunk products, as in the output phase (only when y is wanted) ----
     const bool want_y = p.y != nullptr;
@@ -1026,56 +1026,44 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
     }
-    if (publish) {
-        // every wave's stores complete before the barrier, and the flag goes up after it
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) scan_store(flags + c, p.epoch);
-    }
-
     // ---- the state entering this chunk: chunk 0's outgoing state folded through chunks
     // 1..c-1 in order, h <- E_i h + S_i: the operations of a sequential pass in its order,
-    // so the result does not depend on which workgroup got where first.  Wave 0 waits for
-    // the c flags at once (lane i polls chunk i). ----
-    if (c > 0) {
-        if (wave == 0) {
-            const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
-            while (true) {
-                const bool ok = lane >= c || scan_load(flags + lane) == p.epoch;
-                if (__all(ok)) break;
-                __builtin_amdgcn_s_sleep(2);
-                if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kScanWaitTicks) {
-                    if (lane == 0) atomicOr(p.err + slot, MIL_DEVERR_SCAN);
-                    break;
-                }
+    // so the result does not depend on which workgroup got where first.  Each owning wave
+    // waits for the c flags at once (lane i polls chunk i). ----
+    if (c > 0 && owner) {
+        const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+        while (true) {
+            const bool ok = lane >= c || scan_load(flags + lane) == p.epoch;
+            if (__all(ok)) break;
+            __builtin_amdgcn_s_sleep(2);
+            if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kScanWaitTicks) {
+                if (lane == 0) atomicOr(p.err + slot, MIL_DEVERR_SCAN);
+                break;
             }
         }
-        __syncthreads();
-        if (swave) {
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int tl = wave + i * 8;
+        for (int i = 0; i < TPWL; ++i) {
+            const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) hin[i][r] = shared_load(aggs + (size_t)(tl * 16 + r) * 64 + lane);
-                for (int j = 1; j < c; ++j) {
-                    const float *src = aggs + (size_t)j * AGG;
-                    const float Ej = shared_load(src + N * PC);
+            for (int r = 0; r < 16; ++r) hin[i][r] = shared_load(aggs + (size_t)(tl * 16 + r) * 64 + lane);
+            for (int j = 1; j < c; ++j) {
+                const float *src = aggs + (size_t)j * AGG;
+                const float Ej = shared_load(src + N * PC);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        hin[i][r] = __builtin_fmaf(Ej, hin[i][r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
-                }
+                for (int r = 0; r < 16; ++r)
+                    hin[i][r] = __builtin_fmaf(Ej, hin[i][r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
             }
         }
     }
     // ---- the final state, from the last chunk (nothing reads h0 after chunk 0 has) ----
-    if (last && swave) {
+    if (last && owner) {
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int spt = (wave + i * 8) / NTL;
+        for (int i = 0; i < TPWL; ++i) {
+            const int pt = jpart + LW * i;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                cache[(size_t)n * P + pc0 + spt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
+                cache[(size_t)n * P + pc0 + pt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
             }
         }
     }
@@ -1090,12 +1078,18 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         return;
     }
     if (has_hin) {
-        __syncthreads();  // every wave is done with B and X^T: the carried state goes there
-        if (swave) {
+        // the carried state as [p][n] groups of 8 hi + 8 lo bf16, in the exchange area once
+        // all four light waves have counted themselves out of it
+        bf16 *sH = reinterpret_cast<bf16 *>(sXg);
+        if (owner) {
+            for (int spin = 0; spin < (1 << 20); ++spin) {
+                if (__hip_atomic_load(sCnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int tl = wave + i * 8, spt = tl / NTL;
-                bf16 *row = sH + (spt * kT + l32) * HS;
+            for (int i = 0; i < TPWL; ++i) {
+                const int pt = jpart + LW * i;
+                bf16 *row = sH + (pt * kT + l32) * HS;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int grp = snt * 4 + q;  // n group of 8: 8 hi then 8 lo
@@ -1159,9 +1153,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     }
 }
 
-size_t scan_lds_bytes(int Q, int N, int P) {
-    return scan_base_lds(Q, N, P) + (scan_split_tokens(N, P) ? scan_xchg_bytes(N, P) : 0);
-}
+size_t scan_lds_bytes(int Q, int N, int P) { return scan_base_lds(Q, N, P) + scan_xchg_bytes(N, P); }
 
 size_t out_lds_bytes(int Q, int N, int P) {
     const size_t big = std::max((size_t)Q * (N + 8) + (size_t)P * (Q + 8), (size_t)P * (N * 2 + 8)) * 2;
@@ -1192,14 +1184,17 @@ int slab_width(int nseq, int nch, int H, int P) {
     return pc;
 }
 
+// Column slab width of the single launch: the output work's, at most 64 columns (wider
+// slabs leave no LDS for adding the token parts of the chunk state).
+int scan_slab(int nseq, int nch, int H, int P) { return std::min(slab_width(nseq, nch, H, P), 64); }
+
 // The single-launch kernel for these sizes, or null (its LDS does not fit, a chunk other
 // than 256 tokens, which it is not built for, or more chunks than it keeps flags for).
 const void *scan_kernel(int chunk, int nch, int N, int pc) {
     if (chunk != 256 || nch > kScanChunks || scan_lds_bytes(chunk, N, pc) > kLdsMax) return nullptr;
 #define MIL_SCAN_CASE(n, pp) \
     if (N == n && pc == pp) return reinterpret_cast<const void *>(chunk_scan_mfma<n, pp>);
-    MIL_SCAN_CASE(64, 32) MIL_SCAN_CASE(64, 64) MIL_SCAN_CASE(64, 128)
-    MIL_SCAN_CASE(128, 32) MIL_SCAN_CASE(128, 64) MIL_SCAN_CASE(128, 128)
+    MIL_SCAN_CASE(64, 32) MIL_SCAN_CASE(64, 64) MIL_SCAN_CASE(128, 32) MIL_SCAN_CASE(128, 64)
 #undef MIL_SCAN_CASE
     return nullptr;
 }
@@ -1209,7 +1204,7 @@ const void *scan_kernel(int chunk, int nch, int N, int pc) {
 bool prefill_single_launch(int nseq, int L, int chunk, int H, int P, int N) {
     if (!prefill_mfma_supported(chunk, N, P)) return false;
     const int nch = (L + chunk - 1) / chunk;
-    return scan_kernel(chunk, nch, N, slab_width(nseq, nch, H, P)) != nullptr;
+    return scan_kernel(chunk, nch, N, scan_slab(nseq, nch, H, P)) != nullptr;
 }
 
 // Shapes the matrix-core path covers: bf16 inputs, N and P multiples of 32 up to 256,
@@ -1259,7 +1254,8 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     const int pc = slab_width(nseq, p.nch, p.H, p.P);
 
     // one launch for all three phases where its LDS fits (chunks of 256, 8 waves)
-    const void *kf = scan_kernel(chunk, p.nch, p.N, pc);
+    const int spc = scan_slab(nseq, p.nch, p.H, p.P);
+    const void *kf = scan_kernel(chunk, p.nch, p.N, spc);
     if (kf) {
         p.scan = cache_scan(c);
         p.epoch = next_scan_epoch();
@@ -1269,8 +1265,8 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
         if (e != hipSuccess) return e;
         void *args[] = {&p};
         trace_begin(c, MIL_TRACE_PREFILL_SCAN, s);
-        e = hipLaunchKernel(kf, dim3(p.nch * nseq * p.H * (p.P / pc)), dim3(512), args,
-                            scan_lds_bytes(chunk, p.N, pc), s);
+        e = hipLaunchKernel(kf, dim3(p.nch * nseq * p.H * (p.P / spc)), dim3(512), args,
+                            scan_lds_bytes(chunk, p.N, spc), s);
         trace_end(c, MIL_TRACE_PREFILL_SCAN, s);
         if (e != hipSuccess) return e;
         return hipGetLastError();

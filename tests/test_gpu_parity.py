@@ -195,26 +195,26 @@ def test_prefill_back_to_back_single_launch(L):
     assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
 
 
-# (N, column slab width): the slab follows from the number of chunk-heads (P halved until
-# there is a workgroup per compute unit), so (sequences, heads) pick it: with P = 128 and
-# 4 chunks, 64 / 32 / 16 sequence-heads give slabs of 128 / 64 / 32 columns.  The slabs of
-# 32 and 64 columns split each state tile's tokens over waves; 128 keeps them whole.
-SCAN_CONFIGS = [(64, 32), (64, 64), (64, 128), (128, 32), (128, 64), (128, 128)]
+# The single launch's column slab follows from the number of chunk-heads (P halved until
+# there is a workgroup per compute unit, at most 64 columns), so the number of sequences
+# picks it: with P = 128, 8 heads and 4 chunks, 2 sequences give slabs of 32 columns, 4
+# give 64, and 8 give 64 with two workgroups per compute unit (the later chunks' waits
+# span dispatch rounds).
+SCAN_CONFIGS = [(64, 2), (64, 4), (64, 8), (128, 2), (128, 4), (128, 8)]
 
 
-@pytest.mark.parametrize("N,pc", SCAN_CONFIGS, ids=[f"N{n}_pc{c}" for n, c in SCAN_CONFIGS])
-def test_prefill_single_launch_configs(N, pc):
+@pytest.mark.parametrize("N,Bt", SCAN_CONFIGS, ids=[f"N{n}_batch{b}" for n, b in SCAN_CONFIGS])
+def test_prefill_single_launch_configs(N, Bt):
     """Every state size and column slab of the single-launch prefill, on a ragged last
     chunk (1000 tokens = 3 x 256 + 232)."""
     from speculative_decode_amd import _lib
     H, P, G, L = 8, 128, 2, 1000
-    Bt = {128: 8, 64: 4, 32: 2}[pc]
-    rng = np.random.default_rng(4300 + N + pc)
+    rng = np.random.default_rng(4300 + N + Bt)
     layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, synth.BF16)
     cache = SSMCache(Bt, H, P, N, G, 4, synth.BF16)
     mask = _lib.lib().mil_ssm_prefill_kernels(ctypes.byref(cache.desc), Bt, L, 256)
     assert mask == 1 << _lib.TRACE["prefill_scan"], mask
-    print(f"single-launch prefill N={N} slab={pc} batch={Bt}", flush=True)
+    print(f"single-launch prefill N={N} batch={Bt}", flush=True)
     y = sync_np(cache.prefill(*dev_tokens(tok), *dev_layer(layer), chunk=256))
     assert cache.status() == -1
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
