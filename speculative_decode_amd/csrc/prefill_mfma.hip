@@ -1041,18 +1041,35 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                 break;
             }
         }
+        // chunk by chunk, every owned tile at once, with the next chunk's loads (clamped to
+        // the last one, so that no branch makes the compiler wait for all loads) in flight
+        // while this one is folded in
+        f32x16 nx[TPWL];
+        float en = 0.f;
 #pragma unroll
         for (int i = 0; i < TPWL; ++i) {
             const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) hin[i][r] = shared_load(aggs + (size_t)(tl * 16 + r) * 64 + lane);
-            for (int j = 1; j < c; ++j) {
-                const float *src = aggs + (size_t)j * AGG;
-                const float Ej = shared_load(src + N * PC);
+            for (int r = 0; r < 16; ++r) nx[i][r] = shared_load(aggs + (size_t)(tl * 16 + r) * 64 + lane);
+        }
+        for (int j = 0; j < c; ++j) {
+            f32x16 cur[TPWL];
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    hin[i][r] = __builtin_fmaf(Ej, hin[i][r], shared_load(src + (size_t)(tl * 16 + r) * 64 + lane));
+            for (int i = 0; i < TPWL; ++i) cur[i] = nx[i];
+            const float e = en;
+            const int jn = min(j + 1, c - 1);
+            const float *src = aggs + (size_t)jn * AGG;
+            en = shared_load(src + N * PC);
+#pragma unroll
+            for (int i = 0; i < TPWL; ++i) {
+                const int tl = snt + NTL * (jpart + LW * i);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) nx[i][r] = shared_load(src + (size_t)(tl * 16 + r) * 64 + lane);
             }
+#pragma unroll
+            for (int i = 0; i < TPWL; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) hin[i][r] = j == 0 ? cur[i][r] : __builtin_fmaf(e, hin[i][r], cur[i][r]);
         }
     }
     // ---- the final state, from the last chunk (nothing reads h0 after chunk 0 has) ----
