@@ -223,6 +223,42 @@ def test_prefill_single_launch_configs(N, Bt):
     assert ey <= TOL[synth.BF16] and es <= TOL[synth.BF16]
 
 
+@pytest.mark.parametrize("want_y", [True, False], ids=["y", "state_only"])
+def test_single_launch_continue(want_y):
+    """Prefill, verify, commit, then a several-chunk prefill that continues from the
+    committed state, all through the single launch (chunk 0 starts from the cache's state,
+    the later chunks fold it through the published ones), with y or the state alone."""
+    from speculative_decode_amd import _lib
+    Bt, H, P, N, G = 2, 8, 128, 128, 2
+    L1, K, L2 = 600, 4, 1000
+    rng = np.random.default_rng(4400 + want_y)
+    layer, tok = make_layer_and_tokens(rng, Bt, L1 + K + L2, H, P, N, G, synth.BF16)
+    a = synth.slice_tokens(tok, 0, Bt, 0, L1)
+    d = synth.slice_tokens(tok, 0, Bt, L1, L1 + K)
+    c = synth.slice_tokens(tok, 0, Bt, L1 + K, L1 + K + L2)
+    cache = SSMCache(Bt, H, P, N, G, K, synth.BF16)
+    for n in (L1, L2):
+        assert _lib.lib().mil_ssm_prefill_kernels(ctypes.byref(cache.desc), Bt, n, 256) == \
+            1 << _lib.TRACE["prefill_scan"]
+    A, D = dev_layer(layer)
+    print(f"single-launch continue, y={want_y}", flush=True)
+    cache.prefill(*dev_tokens(a), A, D, chunk=256)
+    dx, dB, dC, ddt = dev_tokens(d)
+    cache.verify(dx, dB, dC, ddt, A, D)
+    j = np.array([3, 1], dtype=np.int32)
+    cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt)
+    y2 = cache.prefill(*dev_tokens(c), A, D, chunk=256, cont=True, want_y=want_y)
+    torch.cuda.synchronize()
+    assert cache.status() == -1
+    _, h1 = oracle.prefill(a.x.f64, a.B.f64, a.C.f64, a.dt.f64, layer.A.f64, layer.D.f64)
+    h1 = oracle.commit(h1, d.x.f64, d.B.f64, d.dt.f64, layer.A.f64, layer.D.f64, j)
+    ry, rs = oracle.prefill(c.x.f64, c.B.f64, c.C.f64, c.dt.f64, layer.A.f64, layer.D.f64, h0=h1)
+    if want_y:
+        assert y_err(sync_np(y2), ry) <= TOL[synth.BF16]
+    assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
+    assert cache.pos().cpu().tolist() == [L1 + int(j[0]) + L2, L1 + int(j[1]) + L2]
+
+
 # --------------------------------------------------------------------------- verify / commit
 
 def test_tiny_f32_protocol_against_oracle():
