@@ -31,6 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));  // 16 bytes that arrays keep in registers
 
 constexpr int kT = 32;  // MFMA tile edge and decay tile (tokens)
 
@@ -411,25 +412,29 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
     const bool active = I * kT < len;
     const int t = I * kT + l32;  // this lane's output row as an A/B operand index
 
-    // C rows of this wave's tile (the B operand of Z and the A operand of C h_in), first,
-    // so that their latency overlaps the staging below
-    bf16x8 cf[NK];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-        cf[kk] = (active && t < len)
-                     ? *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + t) * G + g) * N + kk * 16 + hf * 8)
-                     : bf16x8{};
+    // the carried state of this chunk ([p][n] groups of 8 hi + 8 lo bf16)
+    const bool has_hin = p.cont || c > 0;
+    const uint4 *hin = reinterpret_cast<const uint4 *>(p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N +
+                                                       (size_t)pc0 * N);
+    constexpr int HV = PC * N * 4 / 16;  // 16-byte pieces of this slab's rows
+    constexpr int HPT = (HV + 511) / 512;
+    constexpr bool kPrefetch = HPT <= 8;  // larger states are read at the LDS write instead
+    // the light waves' registers cover the whole state only when NT * HPT pieces do (512 threads)
+    const bool pre = kPrefetch && NT * HPT >= HV;
 
-    // every global load of the staging is issued before the first LDS write
-    const float dv = tid < Q && tid < len ? bf2f(p.dt[(tok0 + tid) * H + h]) : 0.f;  // NT = 2Q >= Q
+    // ---- staging.  Every load is unconditional (rows past the chunk end clamped, their
+    // values zeroed after), so no branch makes the compiler wait for one load before the
+    // next.  Issue order: dt, B and X, which the LDS writes below wait for, then the C rows
+    // of this wave's tile (the B operand of Z and the A operand of C h_in), which are needed
+    // only after the staging. ----
+    const float dv0 = bf2f(p.dt[(tok0 + min(tid, len - 1)) * H + h]);  // NT = 2Q >= Q
     constexpr int BI = N / 16;  // B pieces per thread: Q*N/8 pieces over NT = 2Q threads
     uint4 vb[BI];
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
         const int it = tid + j * NT;
         const int sr = it / (N / 8), ng = it % (N / 8);
-        vb[j] = sr < len ? *reinterpret_cast<const uint4 *>(p.B + ((tok0 + sr) * G + g) * N + ng * 8)
-                         : make_uint4(0, 0, 0, 0);
+        vb[j] = *reinterpret_cast<const uint4 *>(p.B + ((tok0 + min(sr, len - 1)) * G + g) * N + ng * 8);
     }
     constexpr int XI = (PC + 63) / 64;  // X items (4 tokens x 8 columns) per thread
     uint4 vx[XI][4];
@@ -440,11 +445,32 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int sr = sq * 4 + r;
-            vx[j][r] = (it < (Q / 4) * (PC / 8) && sr < len)
-                           ? *reinterpret_cast<const uint4 *>(p.x + ((tok0 + sr) * H + h) * P + pc0 + pg * 8)
-                           : make_uint4(0, 0, 0, 0);
+            vx[j][r] = *reinterpret_cast<const uint4 *>(p.x + ((tok0 + min(sr, len - 1)) * H + h) * P + pc0 +
+                                                         min(pg, PC / 8 - 1) * 8);
         }
     }
+    asm volatile("" ::: "memory");  // the C rows and the carried state after the others
+    bf16x8 cf[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+        cf[kk] = *reinterpret_cast<const bf16x8 *>(p.C + ((tok0 + min(t, len - 1)) * G + g) * N + kk * 16 + hf * 8);
+    asm volatile("" ::: "memory");
+    const float dv = tid < len ? dv0 : 0.f;
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int sr = (tid + j * NT) / (N / 8);
+        if (sr >= len) vb[j] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+        const int sq = (tid + j * NT) % (Q / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (sq * 4 + r >= len) vx[j][r] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+        if (!(active && t < len)) cf[kk] = bf16x8{};
     if (tid < Q) {
         sDt[tid] = dv;
         sDtA[tid] = dv * Ah;  // zero past the chunk end
@@ -470,38 +496,26 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
     __syncthreads();
     chunk_factors(sDtA, len, sR, sSuf, sTot, tid, NT);
     const int ntile = (len + kT - 1) / kT;
+    // the tile totals in registers (two LDS reads), summed in ascending tile order as a
+    // sequential loop would; totals past the last tile are never selected
+    const float4 tq0 = *reinterpret_cast<const float4 *>(sTot), tq1 = *reinterpret_cast<const float4 *>(sTot + 4);
+    const float tv[8] = {tq0.x, tq0.y, tq0.z, tq0.w, tq1.x, tq1.y, tq1.z, tq1.w};
     for (int s = tid; s < len; s += NT) {
         sColf[s] = sDt[s] * __expf(sSuf[s]);  // dt_s * decay(s, end of s's tile)
+        const int ti = s / kT;
         float m = sR[s];
-        for (int q = 0; q < s / kT; ++q) m += sTot[q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = q < ti ? m + tv[q] : m;
         sEin[s] = __expf(m);                  // decay from the chunk start through s
     }
     if (tid < 64) {
         const int Ii = tid / 8, J = tid % 8;
         float m = 0.f;
-        for (int q = J + 1; q < Ii; ++q) m += sTot[q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = (q > J && q < Ii) ? m + tv[q] : m;
         sMid[tid] = (J < Ii && Ii < ntile) ? __expf(m) : 0.f;  // whole tiles strictly between J and Ii
     }
     __syncthreads();
-
-    // the carried state of this chunk ([p][n] groups of 8 hi + 8 lo bf16), fetched into
-    // registers now and parked in LDS once the intra-chunk products are done
-    const bool has_hin = p.cont || c > 0;
-    const uint4 *hin = reinterpret_cast<const uint4 *>(p.ws + (((size_t)seq * p.nch + c) * H + h) * (size_t)P * N +
-                                                       (size_t)pc0 * N);
-    constexpr int HV = PC * N * 4 / 16;  // 16-byte pieces of this slab's rows
-    constexpr int HPT = (HV + 511) / 512;
-    constexpr bool kPrefetch = HPT <= 8;  // larger states are read at the LDS write instead
-    // the prefetch covers the whole state only when NT * HPT pieces do (512 threads)
-    const bool pre = kPrefetch && NT * HPT >= HV;
-    uint4 hpre[kPrefetch ? HPT : 1];
-    if (pre && has_hin) {
-#pragma unroll
-        for (int i = 0; i < HPT; ++i) {
-            const int v = tid + i * NT;
-            hpre[i] = v < HV ? hin[v] : make_uint4(0, 0, 0, 0);
-        }
-    }
 
     f32x16 acc[PT];
 #pragma unroll
@@ -566,14 +580,26 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
     }
+    // the light waves (the short causal rows, done first) fetch the carried state while
+    // the others finish their rows, and park it in LDS once every wave is done with B and X^T
+    constexpr int HPL = 2 * HPT;  // pieces per light thread
+    const bool lightw = wave < nt / 2;
+    i32x4v hpre[kPrefetch ? HPL : 1];
+    if (kPrefetch && has_hin && lightw) {
+#pragma unroll
+        for (int i = 0; i < HPL; ++i)
+            hpre[i] = *reinterpret_cast<const i32x4v *>(hin + min(tid + i * (NT / 2), HV - 1));
+    }
     if (has_hin) {
         __syncthreads();  // every wave is done with B and X^T
         // N/4 pieces of 16 B per row p of the state
         if (pre) {
+            if (lightw) {
 #pragma unroll
-            for (int i = 0; i < (kPrefetch ? HPT : 1); ++i) {
-                const int v = tid + i * NT;
-                if (v < HV) *reinterpret_cast<uint4 *>(sH + (v / (N / 4)) * HS + (v % (N / 4)) * 8) = hpre[i];
+                for (int i = 0; i < (kPrefetch ? HPL : 1); ++i) {
+                    const int v = tid + i * (NT / 2);
+                    if (v < HV) *reinterpret_cast<i32x4v *>(sH + (v / (N / 4)) * HS + (v % (N / 4)) * 8) = hpre[i];
+                }
             }
         } else {
             for (int v = tid; v < HV; v += NT)
