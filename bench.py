@@ -39,6 +39,7 @@ F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
 KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept", "project", "prefill_scan"]
 PREFILL_KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "prefill_scan"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.json")
 
 
 # the sources each kernel family is compiled from (besides the shared headers): a stored
@@ -412,7 +413,8 @@ def run_gpu(args, w):
             work["accept"] = accept_work(w, Bt, K)
         if w.d_model:
             work["project"] = project_work(w, Bt * K)
-    return dict(R=R, kind=kind, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant,
+    jmean = float(jall.mean()) if kind in ("full", "verify") else 0.0
+    return dict(R=R, kind=kind, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant, jmean=jmean,
                 dom_ms=dom_ms, ktime=ktime, work=work, device=torch.cuda.get_device_name(dev), eager_ms=eager_ms)
 
 
@@ -554,6 +556,27 @@ def traffic(fetch_db, write_db, workload, copy_mib):
     return out
 
 
+def mfma_counters(db, workload):
+    """Issued matrix-core work per launch of each kernel family from a rocprofv3 --pmc run
+    of SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA flops / 512) and MfmaUtil (rocprofv3's
+    derived busy percentage of the matrix cores over the dispatch)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    acc = {}
+    for name, cname, v in con.execute("select kernel_name, counter_name, value from counters_collection"):
+        f = _family(name)
+        if f in FAMILY_SOURCES:
+            acc.setdefault(f, {}).setdefault(cname, []).append(v)
+    out = {}
+    for f, c in acc.items():
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c or "MfmaUtil" not in c:
+            continue
+        out[f"{f}/{workload}"] = {"issued_bf16_flops": float(np.mean(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"])) * 512,
+                                  "mfma_busy_frac": float(np.mean(c["MfmaUtil"])) / 100.0,
+                                  "source_sha": source_hash(f)}
+    return out
+
+
 # --------------------------------------------------------------------------- main
 
 def main():
@@ -571,12 +594,23 @@ def main():
                     help="after the run, time a plain elementwise copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 --kernel-trace databases and exit")
+    ap.add_argument("--mfma", metavar="DB",
+                    help="turn a SQ_INSTS_VALU_MFMA_MOPS_BF16 / MfmaUtil --pmc database into "
+                         "profiles/mfma.json entries for --workload, then exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn FETCH_SIZE / WRITE_SIZE --pmc databases (run with --copy-mib) into "
                          "profiles/traffic.json entries for --workload, then exit")
     args = ap.parse_args()
     if args.summarize:
         print(summarize(args.summarize))
+        return
+    if args.mfma:
+        t = mfma_counters(args.mfma, args.workload)
+        old = json.load(open(MFMA_FILE)) if os.path.exists(MFMA_FILE) else {}
+        old.update(t)
+        with open(MFMA_FILE, "w") as fh:
+            json.dump(old, fh, indent=1, sort_keys=True)
+        print(json.dumps(t, indent=1))
         return
     if args.traffic:
         if not args.copy_mib:
@@ -638,6 +672,19 @@ def main():
                 roof["traffic"] = ent["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             pass
+    # issued matrix-core work (counters): the hi / lo splits issue about twice the
+    # algorithmic flops of the products they feed
+    roof["issued_mfma_tflops"] = None
+    roof["mfma_busy_frac"] = None
+    if os.path.exists(MFMA_FILE):
+        try:
+            ent = json.load(open(MFMA_FILE)).get(f"{dom}/{args.workload}")
+            if ent and ent.get("source_sha") == source_hash(dom):
+                roof["issued_mfma_tflops"] = ent["issued_bf16_flops"] / t / 1e12
+                roof["issued_mfma_frac_bf16"] = roof["issued_mfma_tflops"] / BF16_PEAK_TFLOPS
+                roof["mfma_busy_frac"] = ent["mfma_busy_frac"]
+        except (OSError, ValueError, KeyError):
+            pass
     # measured ceilings and the fraction of the attainable roofline: the larger of the
     # byte time and the flop time at the published peaks, over the kernel's time
     copy_gbs, gemm_tflops = measured_peaks()
@@ -691,6 +738,7 @@ def main():
         vb, _ = g["work"]["verify"]
         out["hbm_gbs"] = vb / (g["ktime"]["verify"] * 1e-3) / 1e9
         out["verify_commit_ms"] = g["vc_ms"]
+        out["accepted_tokens_per_s"] = Bt * g["jmean"] / (g["vc_ms"] * 1e-3)
         if g["eager_ms"] is not None:
             out["eager_step_ms"] = g["eager_ms"]
             out["eager_tokens_per_s"] = Bt * K / (g["eager_ms"] * 1e-3)
