@@ -706,6 +706,17 @@ constexpr bool scan_split_tokens(int N, int PC) {
     return scan_base_lds(kScanQ, N, PC) + scan_xchg_bytes(N, PC) <= kLdsMax;
 }
 
+// The published chunk states are moved 16 bytes per lane with the same cache bypass
+// (sc1) that the relaxed agent-scope atomics above use, four registers at a time.  A tile's
+// floats are laid out [register / 4][lane][register % 4].
+constexpr int kCoherentPolicy = 16;  // sc1
+__device__ __forceinline__ void shared_store4(__amdgpu_buffer_rsrc_t r, int boff, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4v, v), r, boff, 0, kCoherentPolicy);
+}
+__device__ __forceinline__ f32x4 shared_load4(__amdgpu_buffer_rsrc_t r, int boff) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, boff, 0, kCoherentPolicy));
+}
+
 template <int N, int PC>
 __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     extern __shared__ __align__(16) char lds[];
@@ -947,8 +958,10 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     // stores, then counts itself in LDS; the fourth raises the flag. ----
     const int slot = p.slot0 + seq;
     int32_t *flags = p.scan + (((size_t)slot * H + h) * kScanSlabs + slab) * kScanChunks;
-    const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: state in register order, then E_c
+    const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: state tiles (see shared_store4), then E_c
     float *aggs = p.chain + (((size_t)seq * H + h) * nps + slab) * (size_t)p.nch * AGG;
+    const __amdgpu_buffer_rsrc_t agr = __builtin_amdgcn_make_buffer_rsrc(aggs, (short)0,
+                                                                         (int)(p.nch * AGG * 4), 0x00020000);
     float *cache = p.state + (size_t)(seq * H + h) * p.head_stride;
     const bool has_hin = p.cont || c > 0;
     const bool last = c == p.nch - 1;
@@ -976,9 +989,12 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                 for (int i = 0; i < TPWL; ++i) {
                     const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float v = c == 0 ? __builtin_fmaf(Ec, hin[i][r], sacc[i][r]) : sacc[i][r];
-                        shared_store(dst + (size_t)(tl * 16 + r) * 64 + lane, v);
+                    for (int q = 0; q < 4; ++q) {
+                        f32x4 v;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            v[u] = c == 0 ? __builtin_fmaf(Ec, hin[i][4 * q + u], sacc[i][4 * q + u]) : sacc[i][4 * q + u];
+                        shared_store4(agr, (int)(((size_t)c * AGG + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
                     }
                 }
             }
@@ -1067,6 +1083,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                 break;
             }
         }
+        asm volatile("" ::: "memory");  // the published states are read after the flags
         // chunk by chunk, every owned tile at once, with the next chunk's loads (clamped to
         // the last one, so that no branch makes the compiler wait for all loads) in flight
         // while this one is folded in
@@ -1076,7 +1093,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         for (int i = 0; i < TPWL; ++i) {
             const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) nx[i][r] = shared_load(aggs + (size_t)(tl * 16 + r) * 64 + lane);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = shared_load4(agr, (int)(((size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) nx[i][4 * q + u] = v[u];
+            }
         }
         for (int j = 0; j < c; ++j) {
             f32x16 cur[TPWL];
@@ -1090,7 +1111,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             for (int i = 0; i < TPWL; ++i) {
                 const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) nx[i][r] = shared_load(src + (size_t)(tl * 16 + r) * 64 + lane);
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = shared_load4(agr, (int)(((size_t)jn * AGG + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) nx[i][4 * q + u] = v[u];
+                }
             }
 #pragma unroll
             for (int i = 0; i < TPWL; ++i)
