@@ -10,20 +10,21 @@
 // and fp32 accumulation.
 //
 // Work decomposition: a workgroup (4 waves) owns BM token rows x 128 output columns of one
-// block (a column tile never straddles two blocks) and a slice of the d inputs.  Wave w
-// owns 32 columns; its lanes stream those weight rows from HBM straight into registers
-// (each weight element is read by one lane of one workgroup), kDepth blocks of 64 inputs
-// ahead of the products.  The u rows go through LDS, shared by the 4 waves.  For few token rows (a decode round) the d inputs
+// block (a column tile never straddles two blocks) and a slice of the d inputs.  Blocks of
+// 64 inputs of the 128 weight rows and the BM u rows are loaded kDepth blocks ahead of the
+// products, each wave reading whole 128-byte rows (eight rows per load instruction, so the
+// vector memory path handles a quarter of the cache lines it would if each lane streamed
+// its own weight row), and staged into one of two LDS buffers right before their
+// products; wave w then takes the B operands of its 32 columns from LDS.  Each weight
+// element is read once per row tile.  For few token rows (a decode round) the d inputs
 // are split over S workgroups so that every CU streams weights; each writes fp32 partial
 // sums and a second kernel adds the S partials in a fixed order, so the result does not
 // depend on scheduling.
 //
-// MFMA operands: for input block kb, lane (l32, hf) holds inputs kb*64 + 32hf + [0, 32)
-// of its weight row as four 8-element groups; step j (0..3) pairs group j of the weight
-// row (B operand, column l32) with the same 8 inputs of token row l32 (A operand, from
-// LDS).  Any assignment of inputs to k-slots works as long as both operands use it.
-// The u rows of a block are loaded with that block's weights (kDepth blocks ahead) and
-// staged into one of two LDS buffers right before its products.
+// MFMA operands: for input block kb, lane (l32, hf) takes inputs kb*64 + 32hf + [0, 32)
+// of weight row l32 of its wave as four 8-element groups; step j (0..3) pairs group j of
+// the weight row (B operand, column l32) with the same 8 inputs of token row l32 (A
+// operand).  Any assignment of inputs to k-slots works as long as both operands use it.
 #include <algorithm>
 
 #include "ssm_internal.h"
@@ -54,10 +55,8 @@ struct ProjParams {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
-// Weight loads use the default cache policy: a lane's four loads of one block touch the
-// same 128-byte lines, which the later three find in the vector L1 (with the non-temporal
-// policy they were fetched again, measured 1.3-1.5x slower).  16-byte values are kept as
-// ext_vector_type: arrays of them stay in registers.
+// Weight loads use the default cache policy.  16-byte values are kept as ext_vector_type:
+// arrays of them stay in registers.
 __device__ __forceinline__ i32x4v wload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
@@ -80,7 +79,9 @@ template <int BM, bool EXACT>
 __global__ __launch_bounds__(256) void project_gemm(const ProjParams p) {
     constexpr int MI = BM / 32;         // 32-row MFMA tiles per wave
     constexpr int UQ = BM * 8 / 256;    // 16-byte pieces of a u block per thread
+    constexpr int WQ = kBN * 8 / 256;   // 16-byte pieces of a weight block per thread
     __shared__ __align__(16) __bf16 sU[2][BM][kUS];
+    __shared__ __align__(16) __bf16 sW[2][kBN][kUS];
 
     const int ntiles = p.tile0[4];
     const int mt = blockIdx.x % ((p.T + BM - 1) / BM);
@@ -92,13 +93,20 @@ __global__ __launch_bounds__(256) void project_gemm(const ProjParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
     const int d = p.d, nkb = p.nkb, k0 = split * nkb * kKB;
 
-    // this lane's weight row (clamped inside the block; columns past it are never stored)
+    // this lane's output column (columns past the block are never stored)
     const int n = col0 + wave * 32 + l32;
-    const int nr = min(n, p.cols[b] - 1);
     const __amdgpu_buffer_rsrc_t wr = rsrc(p.w[b], (uint32_t)((size_t)p.cols[b] * d * 2));
-    const int wvoff = (nr * d + k0 + 32 * hf) * 2;
 
-    // u pieces: row = piece / 8, 16-byte column = piece % 8 (rows past T clamped)
+    // weight and u pieces: row = piece / 8, 16-byte column = piece % 8, so the 64 lanes of
+    // a wave read eight whole 128-byte rows of a block (weight rows past the block and u
+    // rows past T clamped)
+    int woff[WQ];
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) {
+        const int q = tid + 256 * i;
+        const int r = min(col0 + q / 8, p.cols[b] - 1);
+        woff[i] = (r * d + k0 + (q % 8) * 8) * 2;
+    }
     size_t uoff[UQ];
 #pragma unroll
     for (int i = 0; i < UQ; ++i) {
@@ -107,12 +115,12 @@ __global__ __launch_bounds__(256) void project_gemm(const ProjParams p) {
         uoff[i] = (size_t)r * d + k0 + (q % 8) * 8;
     }
 
-    // A ring of kDepth input blocks in flight: each slot holds this lane's weight pieces
-    // and this thread's u pieces of one block, loaded together.  Loads complete in issue
-    // order, so waiting for the oldest slot leaves the other kDepth - 1 in flight.  Four
-    // named slots (constant indices only, so they stay in registers).
+    // A ring of kDepth input blocks in flight: each slot holds this thread's weight and u
+    // pieces of one block, loaded together.  Loads complete in issue order, so waiting for
+    // the oldest slot leaves the other kDepth - 1 in flight.  Four named slots (constant
+    // indices only, so they stay in registers).
     struct Slot {
-        i32x4v w[4], u[UQ];
+        i32x4v w[WQ], u[UQ];
     };
     Slot s0, s1, s2, s3;
     // (the empty asm statements are compiler-only barriers that keep the blocks' loads in
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(256) void project_gemm(const ProjParams p) {
     auto fetch = [&](Slot &sl, int kb) {
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sl.w[j] = wload(wr, wvoff, kb * kKB * 2 + j * 16);
+        for (int i = 0; i < WQ; ++i) sl.w[i] = wload(wr, woff[i], kb * kKB * 2);
 #pragma unroll
         for (int i = 0; i < UQ; ++i) sl.u[i] = *reinterpret_cast<const i32x4v *>(p.u + uoff[i] + kb * kKB);
         asm volatile("" ::: "memory");
@@ -134,11 +142,16 @@ __global__ __launch_bounds__(256) void project_gemm(const ProjParams p) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) acc[i] = f32x16{};
 
-    // one input block: its u pieces into LDS buffer kb & 1 (last read two blocks ago, before
-    // the previous barrier), barrier, products, then the slot is refilled with block
-    // kb + kDepth (clamped: a repeat read of the last block hits L2 and is never used)
+    // one input block: its weight and u pieces into LDS buffer kb & 1 (last read two blocks
+    // ago, before the previous barrier), barrier, products, then the slot is refilled with
+    // block kb + kDepth (clamped: a repeat read of the last block hits L2 and is never used)
     auto step = [&](Slot &sl, int kb) {
         const int buf = kb & 1;
+#pragma unroll
+        for (int i = 0; i < WQ; ++i) {
+            const int q = tid + 256 * i;
+            *reinterpret_cast<i32x4v *>(&sW[buf][q / 8][(q % 8) * 8]) = sl.w[i];
+        }
 #pragma unroll
         for (int i = 0; i < UQ; ++i) {
             const int q = tid + 256 * i;
@@ -147,7 +160,7 @@ __global__ __launch_bounds__(256) void project_gemm(const ProjParams p) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bf16x8 bw = as_bf16x8(sl.w[j]);
+            const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(&sW[buf][wave * 32 + l32][32 * hf + 8 * j]);
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sU[buf][32 * i + l32][32 * hf + 8 * j]);
