@@ -527,6 +527,15 @@ def summarize(dbs):
     return "\n".join(lines)
 
 
+def per_call(per_kernel):
+    """One call's value of a kernel family from per-dispatch counter values grouped by
+    kernel: each kernel's mean, counted as often per call as it was launched relative to
+    the family's most launched kernel (a projection launches its product and its
+    reduction once each; kernels launched only while setting up count zero times)."""
+    cmax = max(len(v) for v in per_kernel.values())
+    return float(sum(np.mean(v) * round(len(v) / cmax) for v in per_kernel.values()))
+
+
 def traffic(fetch_db, write_db, workload, copy_mib):
     """HBM bytes per launch of each kernel family from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for a plain elementwise copy of
@@ -540,8 +549,8 @@ def traffic(fetch_db, write_db, workload, copy_mib):
                                    (counter,)):
             f = _family(name)
             if f:
-                acc.setdefault(f, []).append(v * 1024.0)
-        return {k: float(np.mean(v)) for k, v in acc.items()}
+                acc.setdefault(f, {}).setdefault(name, []).append(v * 1024.0)
+        return {k: per_call(per) for k, per in acc.items()}
 
     fe = per_family(fetch_db, "FETCH_SIZE")
     wr = per_family(write_db, "WRITE_SIZE")
@@ -566,13 +575,13 @@ def mfma_counters(db, workload):
     for name, cname, v in con.execute("select kernel_name, counter_name, value from counters_collection"):
         f = _family(name)
         if f in FAMILY_SOURCES:
-            acc.setdefault(f, {}).setdefault(cname, []).append(v)
+            acc.setdefault(f, {}).setdefault(cname, {}).setdefault(name, []).append(v)
     out = {}
     for f, c in acc.items():
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c or "MfmaUtil" not in c:
             continue
-        out[f"{f}/{workload}"] = {"issued_bf16_flops": float(np.mean(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"])) * 512,
-                                  "mfma_busy_frac": float(np.mean(c["MfmaUtil"])) / 100.0,
+        out[f"{f}/{workload}"] = {"issued_bf16_flops": per_call(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512,
+                                  "mfma_busy_frac": float(np.mean([x for v in c["MfmaUtil"].values() for x in v])) / 100.0,
                                   "source_sha": source_hash(f)}
     return out
 

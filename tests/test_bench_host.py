@@ -81,6 +81,25 @@ def test_traffic_is_scaled_by_the_copy(tmp_path):
     assert e["source_sha"] == bench.source_hash("verify")
 
 
+def test_traffic_sums_the_kernels_of_a_family(tmp_path):
+    # a projection launches its product and its reduction once each: their bytes add up
+    copy = "void at::native::vectorized_elementwise_kernel<4>"
+    gemm = "void mil::(anonymous namespace)::project_gemm<64, true>(mil::ProjParams)"
+    red = "mil::(anonymous namespace)::project_reduce(mil::ProjParams)"
+    setup = "void mil::(anonymous namespace)::ssm_verify_kernel<unsigned short, 4>(mil::VerifyParams)"
+    step = "void mil::(anonymous namespace)::ssm_verify_kernel<unsigned short, 8>(mil::VerifyParams)"
+    _db(tmp_path / "f.db", [(copy, "FETCH_SIZE", 1024.0), (gemm, "FETCH_SIZE", 100.0), (gemm, "FETCH_SIZE", 300.0),
+                            (red, "FETCH_SIZE", 10.0), (red, "FETCH_SIZE", 30.0),
+                            (setup, "FETCH_SIZE", 7.0)] + [(step, "FETCH_SIZE", 50.0)] * 8)
+    _db(tmp_path / "w.db", [(copy, "WRITE_SIZE", 1024.0), (gemm, "WRITE_SIZE", 4.0), (red, "WRITE_SIZE", 2.0),
+                            (step, "WRITE_SIZE", 5.0)])
+    t = bench.traffic(str(tmp_path / "f.db"), str(tmp_path / "w.db"), "wl", 1)
+    assert t["project/wl"]["fetch_bytes"] == pytest.approx((200.0 + 20.0) * 1024)
+    assert t["project/wl"]["write_bytes"] == pytest.approx((4.0 + 2.0) * 1024)
+    # a kernel launched once while setting up, beside eight launches in the steps, counts zero times
+    assert t["verify/wl"]["fetch_bytes"] == pytest.approx(50.0 * 1024)
+
+
 def test_mfma_counters(tmp_path):
     k = "void mil::(anonymous namespace)::chunk_scan_mfma<128, 64>(mil::MParams)"
     _db(tmp_path / "m.db", [(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1000.0), (k, "MfmaUtil", 10.0),
