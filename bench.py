@@ -500,7 +500,7 @@ KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
     "prefill_scan": "chunk_scan_",
     "verify": "ssm_verify_kernel", "commit": ("_commit_kernel", "_commit_tree_kernel"), "accept": "greedy_argmax",
     "project": "project_",
-    "copy": "elementwise",
+    "copy": "MulFunctor",  # the calibration copy: torch.mul(src, 1.0, out=dst)
 }
 
 

@@ -65,15 +65,16 @@ def _db(path, rows):
 
 
 def test_traffic_is_scaled_by_the_copy(tmp_path):
-    copy = "void at::native::vectorized_elementwise_kernel<4>"
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float> > >"
     ver = "void mil::ssm_verify_kernel<unsigned short, 8>"
     mib = 256
     # counters in KiB per dispatch: the copy reads mib MiB but its fetch counter says a third
+    other = "void at::native::vectorized_elementwise_kernel<4, at::native::bfloat16_copy_kernel_cuda>"
     _db(tmp_path / "f.db", [(copy, "FETCH_SIZE", mib * 1024 / 3), (ver, "FETCH_SIZE", 1000.0),
-                            (ver, "FETCH_SIZE", 1200.0)])
+                            (ver, "FETCH_SIZE", 1200.0), (other, "FETCH_SIZE", 5.0), (other, "FETCH_SIZE", 5.0)])
     _db(tmp_path / "w.db", [(copy, "WRITE_SIZE", mib * 1024), (ver, "WRITE_SIZE", 500.0)])
     t = bench.traffic(str(tmp_path / "f.db"), str(tmp_path / "w.db"), "wl", mib)
-    assert t["_calibration"]["fetch_scale"] == pytest.approx(3.0)
+    assert t["_calibration"]["fetch_scale"] == pytest.approx(3.0)  # other elementwise kernels do not count
     assert t["_calibration"]["write_scale"] == pytest.approx(1.0)
     e = t["verify/wl"]
     assert e["fetch_bytes"] == pytest.approx(1100.0 * 1024 * 3)
@@ -83,7 +84,7 @@ def test_traffic_is_scaled_by_the_copy(tmp_path):
 
 def test_traffic_sums_the_kernels_of_a_family(tmp_path):
     # a projection launches its product and its reduction once each: their bytes add up
-    copy = "void at::native::vectorized_elementwise_kernel<4>"
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float> > >"
     gemm = "void mil::(anonymous namespace)::project_gemm<64, true>(mil::ProjParams)"
     red = "mil::(anonymous namespace)::project_reduce(mil::ProjParams)"
     setup = "void mil::(anonymous namespace)::ssm_verify_kernel<unsigned short, 4>(mil::VerifyParams)"
