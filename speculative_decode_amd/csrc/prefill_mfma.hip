@@ -768,17 +768,18 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         const int sr = it / (N / 8), ng = it % (N / 8);
         vb[j] = *reinterpret_cast<const uint4 *>(p.B + ((tok0 + min(sr, len - 1)) * G + g) * N + ng * 8);
     }
+    // X items: 4 tokens x 8 columns, the column group fastest, so that one load
+    // instruction of a wave reads whole rows of the slab (8 tokens x PC / 8 groups)
     constexpr int XI = (PC + 63) / 64;
     uint4 vx[XI][4];
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
         const int it = tid + j * NT;
-        const int pg = it / (Q / 4), sq = it % (Q / 4);
+        const int pg = it % (PC / 8), sq = it / (PC / 8);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int sr = sq * 4 + r;
-            vx[j][r] = *reinterpret_cast<const uint4 *>(p.x + ((tok0 + min(sr, len - 1)) * H + h) * P + pc0 +
-                                                         min(pg, PC / 8 - 1) * 8);
+            vx[j][r] = *reinterpret_cast<const uint4 *>(p.x + ((tok0 + min(sr, len - 1)) * H + h) * P + pc0 + pg * 8);
         }
     }
     asm volatile("" ::: "memory");  // keep the C loads after the others in issue order
@@ -795,7 +796,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     }
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
-        const int sq = (tid + j * NT) % (Q / 4);
+        const int sq = (tid + j * NT) / (PC / 8);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (sq * 4 + r >= len) vx[j][r] = make_uint4(0, 0, 0, 0);
@@ -818,7 +819,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     for (int j = 0; j < XI; ++j) {
         const int it = tid + j * NT;
         if (it >= (Q / 4) * (PC / 8)) break;
-        const int pg = it / (Q / 4), sq = it % (Q / 4);
+        const int pg = it % (PC / 8), sq = it / (PC / 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             *reinterpret_cast<uint2 *>(sXT + (pg * 8 + i) * XS + sq * 4) =
