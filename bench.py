@@ -11,7 +11,10 @@ Printed JSON line:
   value                verified tokens/s = batch*K / (verify + commit time per step)
   prefill_tokens_per_s batch*L / (prefill time per step)
   hbm_gbs              verify's algorithmic bytes / verify kernel time
-  ms_per_step          whole step (prefill + verify + commit), HIP events
+  ms_per_step          whole step (prefill + verify + commit), HIP events; the steps are
+                       queued behind a spin kernel so that they run back to back and the
+                       events time the device, not the Python launch loop
+  host_us_per_step     the host's launch time per step (Python + C ABI calls)
   roofline             for the kernel with the largest time per step (HIP events around
                        its launches, recorded by the library's trace hook), against the
                        published peaks and against ceilings measured in the same run (a
@@ -152,6 +155,68 @@ def project_work(w, T):
     return cols * w.d_model * 2 + T * w.d_model * 2 + T * cols * 2 + w.H * 4, 2 * T * cols * w.d_model
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: recording it
+    skips the system-scope release (an L2 writeback and invalidate) that a default event
+    performs, which on this GPU adds about 2.5 us inside an interval and disturbs the
+    kernel after it.  Timestamps are read only after a device synchronize.  Calls go to
+    the HIP runtime already loaded in the process (torch's), so the handle is valid for
+    the library's trace hook as well."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            cls._hip = ctypes.CDLL(path)
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._h = ctypes.c_void_p()
+        if self.hip().hipEventCreateWithFlags(ctypes.byref(self._h), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    @property
+    def cuda_event(self):
+        return self._h.value
+
+    def record(self):
+        import ctypes
+        import torch
+        if self.hip().hipEventRecord(self._h, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        if self.hip().hipEventElapsedTime(ctypes.byref(ms), self._h, end._h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
+def sleep_cycles_per_s():
+    """Rate of the clock that torch.cuda._sleep counts, measured with events."""
+    import torch
+    a, b = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    a.record()
+    torch.cuda._sleep(4_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return 4_000_000 / (a.elapsed_time(b) * 1e-3)
+
+
 def run_gpu(args, w):
     """Times `args.steps` steps.  Step kinds: "full" = prefill + verify + commit on a fresh
     slot; "verify" = verify + commit on prefilled caches (every layer for the hybrid
@@ -269,8 +334,6 @@ def run_gpu(args, w):
         if kind in ("full", "prefill"):
             x, B, C, dt = st["pre"]
             st["caches"][0].prefill(x, B, C, dt, *AD[0], y=st["y"], chunk=w.chunk, ws=st["ws"])
-        if mark:
-            evs["mid"][s].record()
         if kind in ("full", "verify"):
             for li, c in enumerate(st["caches"]):
                 dx, dB, dC, ddt = st["drf"][li]
@@ -321,18 +384,31 @@ def run_gpu(args, w):
         kernels = kernels + ["accept"]
     if w.d_model:
         kernels = kernels + ["project"]
-    n_ev = max(args.steps, args.warmup, len(kernels) * 4)
-    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for k in ("beg", "mid", "end", "ta", "tb")}
-    for e in evs["ta"] + evs["tb"]:
-        e.record()  # creates the underlying hipEvent so that its handle can be passed down
+    n_ev = max(args.steps, len(kernels) * 4)
+    evs = {k: [TimingEvent() for _ in range(n_ev)] for k in ("ta", "tb")}
+    e0, e1 = TimingEvent(), TimingEvent()
     torch.cuda.synchronize()
 
-    # warmup, then one pass per kernel to find the one with the largest time per launch
+    # warmup (which also gives the host's launch time per step), then one pass per kernel
+    # to find the one with the largest time per launch.  The Python launch loop can be
+    # slower than the device (a short step is a few calls of tens of microseconds of host
+    # work each), and every event interval would then include the device idling for the
+    # host; so before each measured pass the device is held by a spin kernel long enough
+    # for the host to queue the whole pass, and the events measure the device alone.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for s in range(args.warmup):
         step(s)
+    host_step = (time.perf_counter() - t0) / max(args.warmup, 1)
     torch.cuda.synchronize()
+    cps = sleep_cycles_per_s()
+
+    def hold(nsteps):
+        torch.cuda._sleep(int((1.5 * host_step * nsteps + 2e-3) * cps))
+
     ktime = {}
     for i, name in enumerate(kernels):
+        hold(4)
         for rep in range(4):
             s = i * 4 + rep
             set_trace(s, name)
@@ -348,12 +424,13 @@ def run_gpu(args, w):
         # rotating set's whole step (every layer's verify + commit) captured once and
         # replayed; the dominant kernel's time per launch is the traced one found above
         torch.cuda.synchronize()
+        hold(args.steps)
+        e0.record()
         for s in range(args.steps):
-            evs["beg"][s].record()
             step(s, mark=False)
-            evs["end"][s].record()
+        e1.record()
         torch.cuda.synchronize()
-        eager_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+        eager_ms = e0.elapsed_time(e1) / args.steps
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         graphs = []
@@ -366,33 +443,60 @@ def run_gpu(args, w):
         for s in range(args.warmup):
             graphs[s % R].replay()
         torch.cuda.synchronize()
+        hold(args.steps)
         t0 = time.perf_counter()
+        e0.record()
         for s in range(args.steps):
-            evs["beg"][s].record()
             graphs[s % R].replay()
-            evs["end"][s].record()
+        e1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        step_ms = vc_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
+        wall = host_launch = time.perf_counter() - t0
+        step_ms = vc_ms = e0.elapsed_time(e1) / args.steps
         pre_ms = 0.0
         dom_ms = ktime[dominant]
     else:
-        # timed region: K steps, the dominant kernel traced on every step
+        # The timed region: K whole steps back to back between two events, queued behind
+        # the hold as above (`host_us_per_step` reports the host's own launch rate).  Even
+        # a fence-free event costs the device ~2 us of dispatch, so none is recorded
+        # inside the steps here.
         torch.cuda.synchronize()
+        hold(args.steps)
         t0 = time.perf_counter()
+        e0.record()
         for s in range(args.steps):
-            set_trace(s, dominant)
-            evs["beg"][s].record()
-            step(s)
-            evs["end"][s].record()
+            step(s, mark=False)
+        e1.record()
+        host_launch = time.perf_counter() - t0
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        step_ms = e0.elapsed_time(e1) / args.steps
+        # The dominant kernel's time per launch: the same K steps again, with events right
+        # around that kernel's launches (recorded by the library's trace hook on the
+        # stream the kernel runs on).
+        hold(args.steps)
+        for s in range(args.steps):
+            set_trace(s, dominant)
+            step(s)
+        torch.cuda.synchronize()
         for s in range(args.steps):
             set_trace(s, None)
-        pre_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["mid"][s]) for s in range(args.steps)]))
-        vc_ms = float(np.mean([evs["mid"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
-        step_ms = float(np.mean([evs["beg"][s].elapsed_time(evs["end"][s]) for s in range(args.steps)]))
         dom_ms = float(np.mean([evs["ta"][s].elapsed_time(evs["tb"][s]) for s in range(args.steps)]))
+        if kind == "full":
+            # The prefill alone, K launches back to back between two events; verify +
+            # commit take the rest of the step.
+            hold(args.steps)
+            e0.record()
+            for s in range(args.steps):
+                st = sets[s % R]
+                st["caches"][0].prefill(*st["pre"], *AD[0], y=st["y"], chunk=w.chunk, ws=st["ws"])
+            e1.record()
+            torch.cuda.synchronize()
+            pre_ms = e0.elapsed_time(e1) / args.steps
+            vc_ms = step_ms - pre_ms
+        elif kind == "prefill":
+            pre_ms, vc_ms = step_ms, 0.0
+        else:
+            pre_ms, vc_ms = 0.0, step_ms
 
     # algorithmic work per launch of each kernel
     work = {}
@@ -414,7 +518,7 @@ def run_gpu(args, w):
         if w.d_model:
             work["project"] = project_work(w, Bt * K)
     jmean = float(jall.mean()) if kind in ("full", "verify") else 0.0
-    return dict(R=R, kind=kind, wall=wall, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant, jmean=jmean,
+    return dict(R=R, kind=kind, wall=wall, host_us=host_launch / args.steps * 1e6, pre_ms=pre_ms, vc_ms=vc_ms, step_ms=step_ms, dominant=dominant, jmean=jmean,
                 dom_ms=dom_ms, ktime=ktime, work=work, device=torch.cuda.get_device_name(dev), eager_ms=eager_ms)
 
 
@@ -754,7 +858,8 @@ def main():
         if kind == "full":
             out["prefill_tokens_per_s"] = Bt * L / (g["pre_ms"] * 1e-3)
             out["prefill_ms"] = g["pre_ms"]
-    out.update({"roofline": roof, "kernels": kern, "wall_s_timed": g["wall"], "device": g["device"],
+    out.update({"roofline": roof, "kernels": kern, "wall_s_timed": g["wall"], "host_us_per_step": g["host_us"],
+                "device": g["device"],
                 "source_sha": source_hash()})
     out["cpu_baseline"] = None if args.no_cpu_baseline or kind != "full" else run_cpu_baseline(w)
     print(json.dumps(out))

@@ -352,6 +352,16 @@ __global__ __launch_bounds__(256) void state_pass_pn(const MParams p) {
 // Y += M X for one 32-column tile J: the A operands (hi, lo) hold M[t][s] with k-slot
 // (hf, v) <-> s = 32J + 16ks + 8(v/4) + 4hf + v%4, so the B operand reads X^T row p at
 // the same s: two groups of four consecutive tokens.  xr points at X^T[l32][32J + 4hf].
+// One 32-token tile of B as the A operand of Z = B_J C_I^T: row l%32 of the tile, the NK
+// k-steps of 16 state columns (lane half hf takes 8 of each).  Read all at once so that
+// the reads' LDS latencies overlap instead of each waiting before its product.
+template <int NK>
+__device__ __forceinline__ void load_btile(bf16x8 *bq, const bf16 *sB, int J, int l32, int hf, int BS) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+        bq[kk] = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
+}
+
 template <int PT>
 __device__ __forceinline__ void accumulate_mx(f32x16 *acc, const bf16x8 *ah, const bf16x8 *al, const bf16 *xr,
                                               int XS) {
@@ -524,13 +534,21 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
         // rows t >= len are computed but never stored (MFMA rows do not mix)
         const float et = __expf(sR[min(t, Q - 1)]);
         // off-diagonal tiles J < I: every s < t, so no mask; decay = colf(s) * mid(I,J) * e^{R_t}
-        for (int J = 0; J < I; ++J) {
-            f32x16 z = f32x16{};
+        // software pipeline over the tiles J = 0..I: the matrix cores form tile J + 1's
+        // Z (its B rows read from LDS a tile earlier still) while the vector units mask
+        // tile J's, so neither waits for the other within the wave
+        bf16x8 bq[NK];
+        load_btile<NK>(bq, sB, 0, l32, hf, BS);
+        f32x16 zn = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
-                z = mfma(bfr, cf[kk], z);
-            }
+        for (int kk = 0; kk < NK; ++kk) zn = mfma(bq[kk], cf[kk], zn);
+        load_btile<NK>(bq, sB, min(1, I), l32, hf, BS);
+        for (int J = 0; J < I; ++J) {
+            const f32x16 z = zn;
+            zn = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) zn = mfma(bq[kk], cf[kk], zn);
+            load_btile<NK>(bq, sB, min(J + 2, I), l32, hf, BS);
             const float rowf = sMid[I * 8 + J] * et;
             bf16x8 ah[2], al[2];
 #pragma unroll
@@ -552,12 +570,7 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
         // diagonal tile J = I: causal mask, decay exp(R_t - R_s), dt_s, and D on s = t
         {
             const int J = I;
-            f32x16 z = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
-                z = mfma(bfr, cf[kk], z);
-            }
+            const f32x16 z = zn;
             const float Rt = sR[min(t, Q - 1)];
             bf16x8 ah[2], al[2];
 #pragma unroll
@@ -1015,13 +1028,21 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     for (int i = 0; i < PT; ++i) acc[i] = f32x16{};
     if (active && want_y) {
         const float et = __expf(sR[min(t, Q - 1)]);
-        for (int J = 0; J < I; ++J) {
-            f32x16 z = f32x16{};
+        // software pipeline over the tiles J = 0..I: the matrix cores form tile J + 1's
+        // Z (its B rows read from LDS a tile earlier still) while the vector units mask
+        // tile J's, so neither waits for the other within the wave
+        bf16x8 bq[NK];
+        load_btile<NK>(bq, sB, 0, l32, hf, BS);
+        f32x16 zn = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
-                z = mfma(bfr, cf[kk], z);
-            }
+        for (int kk = 0; kk < NK; ++kk) zn = mfma(bq[kk], cf[kk], zn);
+        load_btile<NK>(bq, sB, min(1, I), l32, hf, BS);
+        for (int J = 0; J < I; ++J) {
+            const f32x16 z = zn;
+            zn = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) zn = mfma(bq[kk], cf[kk], zn);
+            load_btile<NK>(bq, sB, min(J + 2, I), l32, hf, BS);
             const float rowf = sMid[I * 8 + J] * et;
             bf16x8 ah[2], al[2];
 #pragma unroll
@@ -1041,12 +1062,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
         {
             const int J = I;
-            f32x16 z = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
-                z = mfma(bfr, cf[kk], z);
-            }
+            const f32x16 z = zn;
             const float Rt = sR[min(t, Q - 1)];
             bf16x8 ah[2], al[2];
 #pragma unroll
