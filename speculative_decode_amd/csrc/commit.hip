@@ -41,12 +41,34 @@ __device__ __forceinline__ void copy_row(char *dst, const char *src, int bytes) 
 // k = 0 workgroup also does the slot's bookkeeping.  A rejected value (j outside 0..K)
 // is reported in err[b] and leaves pos and the pending rows alone; pending becomes 0
 // because the verify that preceded this commit has already folded the previous rows.
-template <typename V>
+// The row is read into registers before j is known, so that the two reads overlap
+// instead of the copy waiting for j first (a row past j is read and dropped); rows
+// longer than kCommitRegs vectors per thread copy their remainder afterwards.
+constexpr int kCommitRegs = 4;
+typedef int i32x4v __attribute__((ext_vector_type(4)));  // 16 bytes that arrays keep in registers
+template <typename V> struct RegVec { typedef V type; };
+template <> struct RegVec<uint4> { typedef i32x4v type; };
+
+template <typename VM>
 __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
-    const int k = blockIdx.x, b = blockIdx.y;
+    typedef typename RegVec<VM>::type V;
+    const int k = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, nt = blockDim.x;
+    const size_t src = (size_t)b * p.K + k, dst = (size_t)b * p.k_max + k;
+    const V *xs = reinterpret_cast<const V *>(p.x + src * p.x_row);
+    const V *bs = reinterpret_cast<const V *>(p.B + src * p.B_row);
+    const uint16_t *ds = reinterpret_cast<const uint16_t *>(p.dt + src * p.dt_row);
+    const int nx = p.x_row / (int)sizeof(V), nb = p.B_row / (int)sizeof(V), nd = p.dt_row / 2;
+    // every index clamped into the row (rows are never empty), so no load waits on a branch
+    V vx[kCommitRegs], vb[kCommitRegs];
+#pragma unroll
+    for (int i = 0; i < kCommitRegs; ++i) {
+        vx[i] = xs[min(tid + i * nt, nx - 1)];
+        vb[i] = bs[min(tid + i * nt, nb - 1)];
+    }
+    const uint16_t vd = ds[min(tid, nd - 1)];
     const int j = p.accepted[b];
     const bool ok = j >= 0 && j <= p.K;
-    if (k == 0 && threadIdx.x == 0) {
+    if (k == 0 && tid == 0) {
         if (ok) {
             p.pending[b] = j;
             p.pos[b] += j;
@@ -56,14 +78,19 @@ __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
         }
     }
     if (!ok || k >= j) return;
-    const size_t src = (size_t)b * p.K + k, dst = (size_t)b * p.k_max + k;
-    copy_row<V>(p.px + dst * p.x_row, p.x + src * p.x_row, p.x_row);
-    copy_row<V>(p.pB + dst * p.B_row, p.B + src * p.B_row, p.B_row);
+    V *xd = reinterpret_cast<V *>(p.px + dst * p.x_row);
+    V *bd = reinterpret_cast<V *>(p.pB + dst * p.B_row);
+    uint16_t *dd = reinterpret_cast<uint16_t *>(p.pdt + dst * p.dt_row);
+#pragma unroll
+    for (int i = 0; i < kCommitRegs; ++i) {
+        if (tid + i * nt < nx) xd[tid + i * nt] = vx[i];
+        if (tid + i * nt < nb) bd[tid + i * nt] = vb[i];
+    }
+    for (int e = tid + kCommitRegs * nt; e < nx; e += nt) xd[e] = xs[e];
+    for (int e = tid + kCommitRegs * nt; e < nb; e += nt) bd[e] = bs[e];
     // dt rows (H elements) need not be a whole number of vectors
-    const char *ds = p.dt + src * p.dt_row;
-    char *dd = p.pdt + dst * p.dt_row;
-    for (int i = threadIdx.x; i < p.dt_row / 2; i += blockDim.x)
-        reinterpret_cast<uint16_t *>(dd)[i] = reinterpret_cast<const uint16_t *>(ds)[i];
+    if (tid < nd) dd[tid] = vd;
+    for (int e = tid + nt; e < nd; e += nt) dd[e] = ds[e];
 }
 
 // ------------------------------------------------------------------ tree drafts
