@@ -53,10 +53,32 @@ __device__ __forceinline__ uint2 column4(const uint4 &v0, const uint4 &v1, const
     return w;
 }
 
-// hi = nearest bf16 of v, lo = nearest bf16 of the remainder
-__device__ __forceinline__ void split(float v, bf16 &hi, bf16 &lo) {
-    hi = static_cast<bf16>(v);
-    lo = static_cast<bf16>(v - static_cast<float>(hi));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// hi = nearest bf16 of each of a and b, lo = nearest bf16 of each remainder, each part as
+// one packed word (a in the low half): one packed conversion per word, the remainders
+// taken from the packed hi word's halves.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a - ha, b - hb}, bf16x2));
+}
+// A lane's 16 accumulator values (register r) split into the hi and lo A operands of two
+// k-steps: register r goes to k-step r / 8, slot r % 8.
+__device__ __forceinline__ void split16(const f32x16 &v, bf16x8 *ah, bf16x8 *al) {
+    i32x4v h[2], l[2];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        uint32_t hw, lw;
+        split2(v[r], v[r + 1], hw, lw);
+        h[r / 8][(r % 8) / 2] = (int)hw;
+        l[r / 8][(r % 8) / 2] = (int)lw;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        ah[k] = __builtin_bit_cast(bf16x8, h[k]);
+        al[k] = __builtin_bit_cast(bf16x8, l[k]);
+    }
 }
 
 struct MParams {
@@ -220,18 +242,17 @@ __global__ __launch_bounds__(256) void chunk_state_mfma(const MParams p) {
                 const int ng = it / (kSB / 4), sq = it % (kSB / 4);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    bf16x4 hi, lo;
+                    float v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const uint32_t wd = word_of(vw[j][r], i >> 1);
-                        const float bb = __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
-                        bf16 x1, x2;
-                        split(wv[j][r] * bb, x1, x2);
-                        hi[r] = x1;
-                        lo[r] = x2;
+                        v[r] = wv[j][r] * __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
                     }
-                    *reinterpret_cast<bf16x4 *>(sWh + (ng * 8 + i) * kSBS + sq * 4) = hi;
-                    *reinterpret_cast<bf16x4 *>(sWl + (ng * 8 + i) * kSBS + sq * 4) = lo;
+                    uint2 hi, lo;
+                    split2(v[0], v[1], hi.x, lo.x);
+                    split2(v[2], v[3], hi.y, lo.y);
+                    *reinterpret_cast<uint2 *>(sWh + (ng * 8 + i) * kSBS + sq * 4) = hi;
+                    *reinterpret_cast<uint2 *>(sWl + (ng * 8 + i) * kSBS + sq * 4) = lo;
                 }
             }
         }
@@ -323,16 +344,13 @@ __global__ __launch_bounds__(256) void state_pass_pn(const MParams p) {
             if (cb + u < p.nch) {
                 const size_t ch = ((size_t)seq * p.nch + cb + u) * p.H + h;
                 float *slot = p.ws + ch * NP + (size_t)pcol * N + n0;
-                bf16x8 hi, lo;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    bf16 a, b;
-                    split(hv[i], a, b);
-                    hi[i] = a;
-                    lo[i] = b;
-                }
-                *reinterpret_cast<bf16x8 *>(slot) = hi;
-                *reinterpret_cast<bf16x8 *>(slot + 4) = lo;
+                uint4 hi, lo;
+                split2(hv[0], hv[1], hi.x, lo.x);
+                split2(hv[2], hv[3], hi.y, lo.y);
+                split2(hv[4], hv[5], hi.z, lo.z);
+                split2(hv[6], hv[7], hi.w, lo.w);
+                *reinterpret_cast<uint4 *>(slot) = hi;
+                *reinterpret_cast<uint4 *>(slot + 4) = lo;
                 const float e = __expf(tt[u]);
                 const float sc[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w, s1[u].x, s1[u].y, s1[u].z, s1[u].w};
 #pragma unroll
@@ -550,21 +568,17 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
             for (int kk = 0; kk < NK; ++kk) zn = mfma(bq[kk], cf[kk], zn);
             load_btile<NK>(bq, sB, min(J + 2, I), l32, hf, BS);
             const float rowf = sMid[I * 8 + J] * et;
-            bf16x8 ah[2], al[2];
+            f32x16 mv;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 // registers 4q..4q+3 hold s = 32J + 8q + 4hf + (0..3)
                 const float4 cf4 = *reinterpret_cast<const float4 *>(sColf + J * kT + 8 * q + 4 * hf);
                 const float cv[4] = {cf4.x, cf4.y, cf4.z, cf4.w};
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * q + u;
-                    bf16 a, b;
-                    split(z[r] * cv[u] * rowf, a, b);
-                    ah[r / 8][r % 8] = a;
-                    al[r / 8][r % 8] = b;
-                }
+                for (int u = 0; u < 4; ++u) mv[4 * q + u] = z[4 * q + u] * cv[u] * rowf;
             }
+            bf16x8 ah[2], al[2];
+            split16(mv, ah, al);
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
         // diagonal tile J = I: causal mask, decay exp(R_t - R_s), dt_s, and D on s = t
@@ -572,7 +586,7 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
             const int J = I;
             const f32x16 z = zn;
             const float Rt = sR[min(t, Q - 1)];
-            bf16x8 ah[2], al[2];
+            f32x16 mv;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 r4 = *reinterpret_cast<const float4 *>(sR + J * kT + 8 * q + 4 * hf);
@@ -584,12 +598,11 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
                     const int sl = 8 * q + 4 * hf + u;  // s - 32J
                     float m = z[r] * dv[u] * __expf(Rt - rv[u]);
                     m = sl < l32 ? m : (sl == l32 ? m + Dh : 0.f);
-                    bf16 a, b;
-                    split(m, a, b);
-                    ah[r / 8][r % 8] = a;
-                    al[r / 8][r % 8] = b;
+                    mv[r] = m;
                 }
             }
+            bf16x8 ah[2], al[2];
+            split16(mv, ah, al);
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
     }
@@ -905,20 +918,16 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             for (int kk = 0; kk < 2; ++kk)
                 tb = mfma(*reinterpret_cast<const bf16x8 *>(sB + (s0 + l32) * BS + snt * kT + kk * 16 + 8 * hf), eye[kk],
                           tb);
-            bf16x8 ah[2], al[2];
+            f32x16 mv;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 w4 = *reinterpret_cast<const float4 *>(sWst + s0 + 8 * q + 4 * hf);
                 const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-                for (int u2 = 0; u2 < 4; ++u2) {
-                    const int r = 4 * q + u2;
-                    bf16 a1, b1;
-                    split(tb[r] * wv[u2], a1, b1);
-                    ah[r / 8][r % 8] = a1;
-                    al[r / 8][r % 8] = b1;
-                }
+                for (int u2 = 0; u2 < 4; ++u2) mv[4 * q + u2] = tb[4 * q + u2] * wv[u2];
             }
+            bf16x8 ah[2], al[2];
+            split16(mv, ah, al);
             accumulate_mx<PT>(part, ah, al, sXT + l32 * XS + s0 + 4 * hf, XS);
         }
     }
@@ -1044,27 +1053,24 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             for (int kk = 0; kk < NK; ++kk) zn = mfma(bq[kk], cf[kk], zn);
             load_btile<NK>(bq, sB, min(J + 2, I), l32, hf, BS);
             const float rowf = sMid[I * 8 + J] * et;
-            bf16x8 ah[2], al[2];
+            f32x16 mv;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                // registers 4q..4q+3 hold s = 32J + 8q + 4hf + (0..3)
                 const float4 cf4 = *reinterpret_cast<const float4 *>(sColf + J * kT + 8 * q + 4 * hf);
                 const float cv[4] = {cf4.x, cf4.y, cf4.z, cf4.w};
 #pragma unroll
-                for (int u2 = 0; u2 < 4; ++u2) {
-                    const int r = 4 * q + u2;
-                    bf16 a1, b1;
-                    split(z[r] * cv[u2] * rowf, a1, b1);
-                    ah[r / 8][r % 8] = a1;
-                    al[r / 8][r % 8] = b1;
-                }
+                for (int u2 = 0; u2 < 4; ++u2) mv[4 * q + u2] = z[4 * q + u2] * cv[u2] * rowf;
             }
+            bf16x8 ah[2], al[2];
+            split16(mv, ah, al);
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
         {
             const int J = I;
             const f32x16 z = zn;
             const float Rt = sR[min(t, Q - 1)];
-            bf16x8 ah[2], al[2];
+            f32x16 mv;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 r4 = *reinterpret_cast<const float4 *>(sR + J * kT + 8 * q + 4 * hf);
@@ -1076,12 +1082,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                     const int sl = 8 * q + 4 * hf + u2;
                     float m = z[r] * dv4[u2] * __expf(Rt - rv[u2]);
                     m = sl < l32 ? m : (sl == l32 ? m + Dh : 0.f);
-                    bf16 a1, b1;
-                    split(m, a1, b1);
-                    ah[r / 8][r % 8] = a1;
-                    al[r / 8][r % 8] = b1;
+                    mv[r] = m;
                 }
             }
+            bf16x8 ah[2], al[2];
+            split16(mv, ah, al);
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
     }
@@ -1178,16 +1183,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int grp = snt * 4 + q;  // n group of 8: 8 hi then 8 lo
-                    bf16x4 hi4, lo4;
-#pragma unroll
-                    for (int u2 = 0; u2 < 4; ++u2) {
-                        bf16 a1, b1;
-                        split(hin[i][4 * q + u2], a1, b1);
-                        hi4[u2] = a1;
-                        lo4[u2] = b1;
-                    }
-                    *reinterpret_cast<bf16x4 *>(row + grp * 16 + 4 * hf) = hi4;
-                    *reinterpret_cast<bf16x4 *>(row + grp * 16 + 8 + 4 * hf) = lo4;
+                    uint2 hi4, lo4;
+                    split2(hin[i][4 * q], hin[i][4 * q + 1], hi4.x, lo4.x);
+                    split2(hin[i][4 * q + 2], hin[i][4 * q + 3], hi4.y, lo4.y);
+                    *reinterpret_cast<uint2 *>(row + grp * 16 + 4 * hf) = hi4;
+                    *reinterpret_cast<uint2 *>(row + grp * 16 + 8 + 4 * hf) = lo4;
                 }
             }
         }
