@@ -660,7 +660,8 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
         }
     }
     if (!active) return;
-    // y rows of this tile (lane: column p, rows t = 32I + 8(r/4) + 4hf + r%4)
+    // y rows of this tile (lane: column p, rows t = 32I + 8(r/4) + 4hf + r%4), stored
+    // non-temporally: nothing here reads them again
     float *yb = p.y + ((tok0 + I * kT) * H + h) * P + pc0 + l32;
     const int ystride = H * P;
 #pragma unroll
@@ -668,7 +669,7 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
         const int tl = 8 * (r / 4) + 4 * hf + (r % 4);
         if (I * kT + tl < len) {
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) yb[tl * ystride + pt * kT] = acc[pt][r];
+            for (int pt = 0; pt < PT; ++pt) __builtin_nontemporal_store(acc[pt][r], yb + tl * ystride + pt * kT);
         }
     }
 }
@@ -1226,6 +1227,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
     }
     if (!active) return;
+    // y rows of this tile, stored non-temporally as in the output phase
     float *yb = p.y + ((tok0 + I * kT) * H + h) * P + pc0 + l32;
     const int ystride = H * P;
 #pragma unroll
@@ -1233,7 +1235,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         const int tl = 8 * (r / 4) + 4 * hf + (r % 4);
         if (I * kT + tl < len) {
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) yb[tl * ystride + pt * kT] = acc[pt][r];
+            for (int pt = 0; pt < PT; ++pt) __builtin_nontemporal_store(acc[pt][r], yb + tl * ystride + pt * kT);
         }
     }
 }
