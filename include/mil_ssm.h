@@ -83,9 +83,13 @@ typedef struct {
  *           length or node), MIL_DEVERR_TREE (a tree link outside -1..k-1) and
  *           MIL_DEVERR_SCAN (a prefill's chunk-to-chunk handoff timed out; the slot's
  *           prefill results are then wrong).
- *   scan    int32 [batch][H][8][8]: single-launch prefill flags (one per chunk of up to 8
- *           chunks, per column slab); mil_ssm_cache_init zeroes them, and each prefill
- *           writes values no other call in the process uses.
+ *   scan    int32 [batch][H][8][12]: single-launch prefill handoff words, one row per
+ *           (slot, head, column slab): 8 chunk flags, then the row's epoch (the flag value
+ *           of the row's last prefill), then padding.  mil_ssm_cache_init zeroes them; a
+ *           prefill raises its flags to epoch + 1 and then stores epoch + 1 as the epoch,
+ *           so the value that marks a call lives in the buffer itself: graph replays and
+ *           byte copies of a cache (mil_ssm_cache_attach) stay correct.  A buffer whose
+ *           rows hold a flag above their epoch is not a cache this library wrote.
  * The logical state of slot b is `state` advanced through its `pending` rows.
  */
 typedef struct {
@@ -194,8 +198,9 @@ int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted,
  * cut at the first rejected one.  The pages do not say what makes a draft "correct"; the
  * reading taken here is greedy verification: draft k of slot b is correct when it equals
  * the verifier's most likely token at that position, the argmax over the vocabulary of
- * logits[b][k][:] (ties go to the lowest token id; a NaN with the sign bit clear counts as
- * the largest value).  accepted[b] = the number of leading correct drafts (0..K).
+ * logits[b][k][:]: among equal values the lowest token id wins, -0 and +0 are one value,
+ * and every NaN (either sign, any payload) ranks above every number, the lowest id first
+ * among NaNs.  accepted[b] = the number of leading correct drafts (0..K).
  *
  * draft_tokens  device int32 [batch][K], token ids the drafts stand for;
  * logits        device [batch][K][vocab], MIL_F32 or MIL_BF16 (logits_dtype, independent

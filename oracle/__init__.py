@@ -129,13 +129,28 @@ def greedy_accept(draft_tokens, logits):
 
     draft_tokens [batch][K] int, logits [batch][K][vocab] (the exact values the GPU gets,
     widened to float64).  Returns (accepted [batch] int32, verifier_tokens [batch][K]
-    int32): the argmax token of every position (the first index among equal maxima, as
-    numpy's argmax takes it) and the number of leading positions whose draft equals it.
+    int32): the argmax token of every position and the number of leading positions whose
+    draft equals it.
+
+    The argmax rule (the pages fix none; this is the reading the GPU kernel follows too):
+      * the largest value wins, and among equal values the lowest token id;
+      * +0 and -0 are the same value (they compare equal);
+      * a NaN, of either sign and any payload, counts as larger than every number, and
+        among NaNs the lowest token id wins.
     """
     drafts = np.asarray(draft_tokens)
     lg = np.asarray(logits, dtype=np.float64)
-    tokens = np.argmax(lg, axis=2).astype(np.int32)
     batch, K = drafts.shape
+    tokens = np.zeros((batch, K), dtype=np.int32)
+    for b in range(batch):
+        for k in range(K):
+            row = lg[b, k]
+            nan = np.flatnonzero(np.isnan(row))
+            if nan.size:
+                tokens[b, k] = nan[0]
+                continue
+            # equal maxima (including -0 and +0) all satisfy row == max; take the first
+            tokens[b, k] = np.flatnonzero(row == np.max(row))[0]
     accepted = np.zeros(batch, dtype=np.int32)
     for b in range(batch):
         j = 0

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
             p.pending[b] = j;
             p.pos[b] += j;
         } else {
-            p.err[b] = MIL_DEVERR_ACCEPT;
+            atomicOr(p.err + b, MIL_DEVERR_ACCEPT);  // keeps bits set by earlier calls
             p.pending[b] = 0;
         }
     }
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void ssm_commit_tree_kernel(const TreeCommitPa
             p.pending[b] = j;
             p.pos[b] += j;
         } else {
-            p.err[b] = sbad;
+            atomicOr(p.err + b, sbad);  // keeps bits set by earlier calls
             p.pending[b] = 0;
         }
     }
@@ -166,11 +166,15 @@ __global__ __launch_bounds__(256) void ssm_commit_tree_kernel(const TreeCommitPa
 // Key = (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index): the largest
 // key is the largest value, ties going to the lowest index, so the result does not depend
 // on how the vocabulary is split or in which order partial maxima meet.  Integer and
-// compare-only work: exact.
+// compare-only work: exact.  The argmax rule: -0 and +0 are one value, and every NaN
+// (either sign, any payload) ranks above every number, the lowest id first among NaNs.
 constexpr int kGreedySplitsMax = 64;
 
-__device__ __forceinline__ uint32_t ordered(float v) {  // monotonic in v
+__device__ __forceinline__ uint32_t ordered(float v) {  // monotonic in v, +-0 and NaNs canonical
     const uint32_t u = __float_as_uint(v);
+    const uint32_t mag = u & 0x7fffffffu;
+    if (mag > 0x7f800000u) return 0xffffffffu;  // any NaN: above +inf (0xff800000)
+    if (mag == 0u) return 0x80000000u;          // -0 keyed as +0
     return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ uint64_t argmax_key(uint32_t o, uint32_t idx) {

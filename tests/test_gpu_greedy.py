@@ -151,3 +151,66 @@ def test_greedy_commit_argument_checks():
     assert call() == L.MIL_OK
     assert c.phase() == L.PHASE_READY
     torch.cuda.synchronize()
+
+
+def special_logits(rng, batch, K, vocab, dtype):
+    """Rows built from bit patterns: every number negative (so that a zero is a maximum),
+    then per row one of: -0 and +0 at two ids (either order), NaNs of both signs and with
+    small payloads at several ids beside a +inf, a lone negative NaN, or nothing special."""
+    if dtype == synth.BF16:
+        neg0, pos0, inf = 0x8000, 0x0000, 0x7F80
+        nans = [0x7FC0, 0xFFC0, 0x7F81, 0xFF81]
+        vals = synth.f32_to_bf16_bits(-(np.abs(rng.standard_normal((batch, K, vocab))) + 0.5).astype(np.float32))
+        bits = vals.astype(np.uint16)
+    else:
+        neg0, pos0, inf = 0x80000000, 0x00000000, 0x7F800000
+        nans = [0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001]
+        bits = (-(np.abs(rng.standard_normal((batch, K, vocab))) + 0.5)).astype(np.float32).view(np.uint32)
+    kinds = []
+    for b in range(batch):
+        for k in range(K):
+            kind = int(rng.integers(0, 4))
+            kinds.append(kind)
+            ids = rng.choice(vocab, size=4, replace=False)
+            if kind == 0:
+                bits[b, k, ids[0]], bits[b, k, ids[1]] = neg0, pos0
+            elif kind == 1:
+                bits[b, k, ids[0]] = inf
+                for i, nb in zip(ids[1:], rng.choice(nans, size=3)):
+                    bits[b, k, i] = nb
+            elif kind == 2:
+                bits[b, k, ids[0]] = nans[1] if rng.random() < 0.5 else nans[3]
+    if dtype == synth.BF16:
+        f64 = synth.bf16_bits_to_f64(bits)
+        store = bits
+    else:
+        store = bits.view(np.float32)
+        f64 = store.astype(np.float64)
+    return synth.Tensor(store, f64, dtype), kinds
+
+
+@pytest.mark.parametrize("ldt", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("vocab", [257, 4099, 128256])
+def test_greedy_signed_zero_and_nan_match_oracle(ldt, vocab):
+    """-0 ties +0 (the lower id wins) and every NaN ranks above every number (the first NaN
+    wins, whatever its sign): argmax tokens and accepted lengths equal the oracle's."""
+    rng = np.random.default_rng(31 + vocab + (ldt == synth.BF16))
+    batch, K = 6, 8
+    shape = (batch, 4, 32, 32, 2)
+    _, _, drafts, (A, D), (cg, _) = two_caches(rng, shape, synth.BF16, K, 8)
+    lg, kinds = special_logits(rng, batch, K, vocab, ldt)
+    assert set(kinds) == {0, 1, 2, 3}
+    _, tok_ref = oracle.greedy_accept(np.zeros((batch, K), dtype=np.int32), lg.f64)
+    planted = np.array([0, K, 3, 5, 1, 7], dtype=np.int32)
+    draft_tok = tok_ref.copy()
+    for b in range(batch):
+        if planted[b] < K:
+            draft_tok[b, planted[b]] = (tok_ref[b, planted[b]] + 1) % vocab
+    j_ref, tok_ref2 = oracle.greedy_accept(draft_tok, lg.f64)
+    assert np.array_equal(j_ref, planted) and np.array_equal(tok_ref2, tok_ref)
+    dx, dB, dC, ddt = dev_tokens(drafts)
+    acc, tok = cg.commit_greedy(torch.from_numpy(draft_tok).cuda(), logits_dev(lg), dx, dB, ddt, A, D,
+                                want_tokens=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), tok_ref)
+    assert np.array_equal(acc.cpu().numpy(), j_ref)

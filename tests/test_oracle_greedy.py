@@ -60,7 +60,33 @@ def check_ties_lowest_index(fn):
     assert t.tolist() == [[3], [3]] and j.tolist() == [1, 0]
 
 
-CHECKS = [check_brute_force, check_planted, check_ties_lowest_index]
+def check_signed_zero_and_nan(fn):
+    """Hand-worked rows for the two cases numbers alone leave open (the rule stated in
+    oracle.greedy_accept): -0 and +0 are one value, so the lower id wins; every NaN,
+    whatever its sign, ranks above every number, and the first NaN wins."""
+    nan, inf = float("nan"), float("inf")
+    rows = [
+        ([-1.0, -0.0, 0.0, -2.0], 1),       # -0 at id 1 ties +0 at id 2
+        ([0.0, -0.0], 0),
+        ([-0.0, 0.0], 0),
+        ([-3.0, -0.0, -0.0, 0.0], 1),
+        ([1.0, -nan, nan, 5.0], 1),         # a negative NaN is a NaN too
+        ([5.0, inf, nan], 2),               # NaN above +inf
+        ([nan, inf], 0),
+        ([-inf, -inf, -inf], 0),
+        ([nan, nan, nan], 0),
+        ([2.0, 7.0, -nan], 2),
+    ]
+    for vals, want in rows:
+        lg = np.array(vals, dtype=np.float64).reshape(1, 1, -1)
+        j, t = fn(np.array([[want]]), lg)
+        assert t.tolist() == [[want]], (vals, t)
+        assert j.tolist() == [1]
+        j, t = fn(np.array([[want + 1]]), lg)
+        assert j.tolist() == [0]
+
+
+CHECKS = [check_brute_force, check_planted, check_ties_lowest_index, check_signed_zero_and_nan]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -68,31 +94,41 @@ def test_greedy_oracle_pin(check):
     check(oracle.greedy_accept)
 
 
+# (description, [(text in the oracle, replacement), ...])
 MUTANTS = [
-    ("ties go to the highest id", "tokens = np.argmax(lg, axis=2).astype(np.int32)",
-     "tokens = (lg.shape[2] - 1 - np.argmax(lg[:, :, ::-1], axis=2)).astype(np.int32)"),
+    ("ties go to the highest id", [("np.flatnonzero(row == np.max(row))[0]", "np.flatnonzero(row == np.max(row))[-1]")]),
     ("every match counted, not the leading run",
-     "        while j < K and drafts[b, j] == tokens[b, j]:\n            j += 1",
-     "        j = int(np.sum(drafts[b] == tokens[b]))"),
-    ("last draft never accepted", "while j < K and drafts", "while j < K - 1 and drafts"),
-    ("draft compared with the next position", "drafts[b, j] == tokens[b, j]",
-     "drafts[b, j] == tokens[b, min(j + 1, K - 1)]"),
-    ("argmin instead of argmax", "np.argmax(lg, axis=2)", "np.argmin(lg, axis=2)"),
+     [("        while j < K and drafts[b, j] == tokens[b, j]:\n            j += 1",
+       "        j = int(np.sum(drafts[b] == tokens[b]))")]),
+    ("last draft never accepted", [("while j < K and drafts", "while j < K - 1 and drafts")]),
+    ("draft compared with the next position", [("drafts[b, j] == tokens[b, j]",
+                                                "drafts[b, j] == tokens[b, min(j + 1, K - 1)]")]),
+    ("argmin instead of argmax", [("np.max(row)", "np.min(row)")]),
+    ("NaN ignored", [("if nan.size:", "if False:"), ("np.max(row)", "np.nanmax(row)")]),
+    ("last NaN wins", [("tokens[b, k] = nan[0]", "tokens[b, k] = nan[-1]")]),
+    ("-0 ranked below +0 (sign bit read as part of the value)",
+     [("np.flatnonzero(row == np.max(row))[0]",
+       "np.argmax(np.where(row == 0, np.copysign(1e-300, row), row))")]),
+    ("a NaN with the sign bit set ranked below every number",
+     [("nan = np.flatnonzero(np.isnan(row))", "nan = np.flatnonzero(np.isnan(row) & ~np.signbit(row))"),
+      ("np.max(row)", "np.max(np.where(np.isnan(row), -np.inf, row))")]),
 ]
 
 
 @pytest.mark.parametrize("i", range(len(MUTANTS)), ids=[m[0] for m in MUTANTS])
 def test_greedy_planted_mistakes_are_caught(i):
-    desc, old, new = MUTANTS[i]
+    desc, edits = MUTANTS[i]
     src = textwrap.dedent(inspect.getsource(oracle.greedy_accept))
-    assert src.count(old) == 1, desc
+    for old, new in edits:
+        assert src.count(old) >= 1, desc
+        src = src.replace(old, new)
     ns = {"np": np}
-    exec(src.replace(old, new), ns)
+    exec(src, ns)
     mutant = ns["greedy_accept"]
     caught = 0
     for check in CHECKS:
         try:
             check(mutant)
-        except AssertionError:
+        except (AssertionError, IndexError, ValueError):
             caught += 1
     assert caught > 0, desc
