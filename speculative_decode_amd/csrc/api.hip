@@ -93,7 +93,7 @@ int mil_ssm_cache_layout(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mi
     L.err_off = off = round_up(off, kAlign);
     off += Bt * 4;
     L.scan_off = off = round_up(off, kAlign);
-    off += Bt * H * kScanSlabs * kScanChunks * 4;
+    off += Bt * H * kScanSlabs * kScanRow * 4;
     L.bytes = round_up(off, kAlign);
     *out = L;
     return MIL_OK;

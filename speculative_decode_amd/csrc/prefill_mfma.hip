@@ -19,7 +19,6 @@
 // output row t (= its column) and 16 source tokens s: exactly an A operand for M X
 // once the k-slot (hf, v) <-> s correspondence is applied to how X is read from LDS.
 #include <algorithm>
-#include <atomic>
 
 #include "ssm_internal.h"
 
@@ -94,8 +93,7 @@ struct MParams {
     int slot0, nseq, batch, cont;
     int PS, nslab;         // phase 1: state rows p per workgroup, slabs per chunk-head
     // single-launch scan
-    int32_t *scan;         // handoff flags [batch][H][kScanSlabs][kScanChunks]
-    int epoch;             // this call's flag value (never reused in the process)
+    int32_t *scan;         // handoff words [batch][H][kScanSlabs][kScanRow]
     int32_t *err;          // [batch] device error words
     float *chain;          // [nseq][H][P/PC][nch][N*PC + 16] published chunk states (register order), E_c
 };
@@ -684,7 +682,13 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
 // through chunks 0..c-1 in order (h <- E_i h + S_i): the operations of a sequential pass in
 // its order, so the result does not depend on timing, and no workgroup waits on a chain
 // of others, only on the publications.  The last chunk writes the final state.  Flags
-// hold a per-call value (never reused in the process), so nothing needs resetting.
+// hold a per-call value that comes from the device: each (slot, head, slab) row keeps the
+// epoch its last call raised its flags to; every workgroup of this call reads it at its
+// start and raises its flag to epoch + 1, and the last chunk stores epoch + 1 as the
+// row's epoch once its wait is over, which is after every workgroup of the row has read
+// the old value (each of them publishes before the last chunk's wait can end).  So no
+// flag left by an earlier call, a graph replay or a byte copy of the cache equals this
+// call's value, and nothing needs resetting.
 // Longer prompts keep the three launches (their per-chunk reads of all earlier chunks
 // would grow with the square of the count).
 //
@@ -781,6 +785,10 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     const int I = wave < nt / 2 ? wave : nt - 1 - (wave - nt / 2);
     const bool active = I * kT < len;
     const int t = I * kT + l32;
+    // this call's flag value: the row's epoch + 1, read before anything else (the last
+    // chunk overwrites the epoch only after every workgroup of the row has published)
+    int32_t *flags = p.scan + (((size_t)(p.slot0 + seq) * H + h) * kScanSlabs + slab) * kScanRow;
+    const int epoch = __builtin_amdgcn_readfirstlane(scan_load(flags + kScanEpoch)) + 1;
 
     // ---- staging: B, X and dt first (the chunk state needs them), then the C rows (only
     // the outputs need them), so that writing B and X to LDS waits for them alone ----
@@ -981,7 +989,6 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     // 1..nch-2 their own S_c, each with its decay E_c.  Each light wave waits for its own
     // stores, then counts itself in LDS; the fourth raises the flag. ----
     const int slot = p.slot0 + seq;
-    int32_t *flags = p.scan + (((size_t)slot * H + h) * kScanSlabs + slab) * kScanChunks;
     const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: state tiles (see shared_store4), then E_c
     float *aggs = p.chain + (((size_t)seq * H + h) * nps + slab) * (size_t)p.nch * AGG;
     const __amdgpu_buffer_rsrc_t agr = __builtin_amdgcn_make_buffer_rsrc(aggs, (short)0,
@@ -1028,7 +1035,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         // this wave has also read its partial tiles: the exchange area is free of it
         if (lane == 0) {
             const int before = atomicAdd(sCnt, 1);
-            if (publish && before == 3) scan_store(flags + c, p.epoch);
+            if (publish && before == 3) scan_store(flags + c, epoch);
         }
     }
     // ---- outputs: intra-chunk products, as in the output phase (only when y is wanted) ----
@@ -1098,7 +1105,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     if (c > 0 && owner) {
         const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
         while (true) {
-            const bool ok = lane >= c || scan_load(flags + lane) == p.epoch;
+            const bool ok = lane >= c || scan_load(flags + lane) == epoch;
             if (__all(ok)) break;
             __builtin_amdgcn_s_sleep(2);
             if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kScanWaitTicks) {
@@ -1106,6 +1113,10 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                 break;
             }
         }
+        // every earlier chunk of the row has published, so has read the old epoch: this
+        // call's value becomes the row's epoch (also after a timeout, so that no flag of
+        // this call is ever above the epoch)
+        if (last && wave == 0 && lane == 0) scan_store(flags + kScanEpoch, epoch);
         asm volatile("" ::: "memory");  // the published states are read after the flags
         // chunk by chunk, every owned tile at once, with the next chunk's loads (clamped to
         // the last one, so that no branch makes the compiler wait for all loads) in flight
@@ -1250,19 +1261,6 @@ size_t state_lds_bytes(int PS, int N) { return (size_t)(PS + 2 * N) * kSBS * 2 +
 
 constexpr int64_t kOutItemsTarget = 256;  // output workgroups wanted (one per compute unit)
 
-// Flag value of one single-launch call: a process-wide counter, so a flag left by any
-// earlier call (the flags are zero when a cache is set up) never equals a later call's.
-int next_scan_epoch() {
-    static std::atomic<int> counter{0};
-    int e = counter.fetch_add(1) + 1;
-    while (e <= 0) {  // after 2^31 calls: start again at 1
-        int expected = e - 1;
-        counter.compare_exchange_strong(expected, 1);
-        e = counter.fetch_add(1) + 1;
-    }
-    return e;
-}
-
 // Column slab width of the output work (and of the single launch): P split until the grid
 // has a workgroup per compute unit.
 int slab_width(int nseq, int nch, int H, int P) {
@@ -1345,7 +1343,6 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     const void *kf = scan_kernel(chunk, p.nch, p.N, spc);
     if (kf) {
         p.scan = cache_scan(c);
-        p.epoch = next_scan_epoch();
         p.err = cache_err(c);
         p.chain = static_cast<float *>(ws);
         hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);

@@ -50,7 +50,11 @@ class SSMCache:
     """Per-layer state cache for `batch` sequence slots (fp32 state [batch][H][N][P],
     head blocks 256-B aligned) plus the pending accepted-token rows and counters."""
 
-    def __init__(self, batch, H, P, N, G, k_max, dtype, device="cuda"):
+    def __init__(self, batch, H, P, N, G, k_max, dtype, device="cuda", attach_to=None):
+        """attach_to: a uint8 device tensor that already holds a cache of this shape (for
+        instance a byte copy of another SSMCache's `buffer`), described with
+        mil_ssm_cache_attach instead of being set up from zeros; it must be 256-byte
+        aligned and at least `layout.bytes` long."""
         self.batch, self.H, self.P, self.N, self.G, self.k_max = batch, H, P, N, G, k_max
         self.dtype_code = _dtype_code(dtype)
         self.torch_dtype = _TORCH[self.dtype_code]
@@ -60,11 +64,20 @@ class SSMCache:
         self.dims = L.Dims(batch, H, P, N, G)
         self.layout = cache_layout(batch, H, P, N, G, k_max, self.dtype_code)
         nbytes = self.layout.bytes
+        self.desc = L.CacheDesc()
+        if attach_to is not None:
+            if attach_to.dtype != torch.uint8 or attach_to.device != self.device or attach_to.numel() < nbytes:
+                raise ValueError(f"attach_to must be a uint8 tensor of at least {nbytes} bytes on {self.device}")
+            self._raw = attach_to
+            self.buffer = attach_to[:nbytes]
+            L.check(L.lib().mil_ssm_cache_attach(ctypes.byref(self.desc), ctypes.byref(self.dims), k_max,
+                                                self.dtype_code, _ptr(self.buffer), nbytes),
+                    "mil_ssm_cache_attach")
+            return
         # over-allocate so that the carved base is 256-B aligned whatever the allocator does
         self._raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
         off = (-self._raw.data_ptr()) % 256
         self.buffer = self._raw[off:off + nbytes]
-        self.desc = L.CacheDesc()
         L.check(L.lib().mil_ssm_cache_init(ctypes.byref(self.desc), ctypes.byref(self.dims), k_max,
                                           self.dtype_code, _ptr(self.buffer), nbytes, _stream(self.device)),
                 "mil_ssm_cache_init")
@@ -90,6 +103,16 @@ class SSMCache:
 
     def err(self) -> torch.Tensor:
         return self._i32(self.layout.err_off)
+
+    def scan_words(self) -> torch.Tensor:
+        """int32 view [batch][H][8][12] of the single-launch prefill's handoff rows (8 chunk
+        flags, the row's epoch, padding)."""
+        off = self.layout.scan_off
+        return self.buffer[off:off + self.batch * self.H * 8 * 12 * 4].view(torch.int32).view(self.batch, self.H, 8, 12)
+
+    def prefill_kernels(self, nseq, L_tokens, chunk=256) -> int:
+        """Bit mask of the traceable kernels a prefill of these sizes launches (mil_ssm_prefill_kernels)."""
+        return int(L.lib().mil_ssm_prefill_kernels(ctypes.byref(self.desc), nseq, L_tokens, chunk))
 
     def phase(self) -> int:
         return L.lib().mil_ssm_cache_phase(ctypes.byref(self.desc))
