@@ -28,3 +28,22 @@ def gpu_available() -> bool:
 def oracle_lib():
     import oracle
     return oracle.load()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the achieved parity errors of this session (tests/gpu_util.py records every
+    comparison) to gpurun_out/parity_errors.json."""
+    mod = sys.modules.get("gpu_util")
+    recs = getattr(mod, "RECORDS", None) if mod else None
+    if not recs:
+        return
+    import json
+    out = os.path.join(ROOT, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    worst = {}
+    for r in recs:
+        w = worst.setdefault(r["test"], {})
+        for k in ("normwise", "elementwise"):
+            w[f"{r['what']}_{k}"] = max(w.get(f"{r['what']}_{k}", 0.0), r[k])
+    with open(os.path.join(out, "parity_errors.json"), "w") as f:
+        json.dump({"records": len(recs), "worst_per_test": worst}, f, indent=1, sort_keys=True)

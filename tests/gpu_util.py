@@ -3,10 +3,18 @@ error metric used against the oracle.
 
 Metric (the reading used throughout): for each (sequence, head) slice, the normwise
 relative error max|gpu - ref| / max|ref|, maximised over slices.  A purely elementwise
-relative error has no bound where ref crosses zero, so it is reported, not judged.
+relative error has no bound where ref crosses zero, so it is reported, not judged: the
+elementwise figure is max |gpu - ref| / |ref| over the elements of a slice whose |ref| is
+at least 1e-2 of that slice's max |ref|, maximised over slices.
 Bounds: 1e-5 for fp32 token inputs, 2e-3 for bf16 token inputs.
+
+Every comparison made through y_err / state_err is recorded (test id, what was compared,
+both figures); the test session writes the records to gpurun_out/parity_errors.json, so a
+GPU run leaves the achieved errors of every parity test behind.
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import torch
@@ -14,6 +22,13 @@ import torch
 from speculative_decode_amd import synth
 
 TOL = {synth.F32: 1e-5, synth.BF16: 2e-3}
+# Beside the bounds above, a regression bound for the layer's own kernels, from the errors
+# they were measured to reach: every bf16 prefill (matrix-core path with hi/lo splits of the
+# fp32-derived operands) and every verify / tree / graph round came to at most 7.3e-6
+# normwise over the whole GPU parity suite; a product missing its lo half lands near 1e-3.
+# Inputs rounded on the way (the projection test's bf16 outputs) keep the bound above only.
+REGRESSION = {synth.F32: 1e-5, synth.BF16: 5e-5}
+BOUND = {dt: min(TOL[dt], REGRESSION[dt]) for dt in TOL}
 
 
 def dev(t: synth.Tensor, device="cuda") -> torch.Tensor:
@@ -30,26 +45,55 @@ def dev_layer(layer: synth.Layer, device="cuda"):
     return dev(layer.A, device), dev(layer.D, device)
 
 
-def slice_err(gpu: np.ndarray, ref: np.ndarray, head_axis: int) -> float:
-    """Max over (sequence, head) slices of max|g - r| / max|r|.  Arrays are
-    [seq][...][H][...] with the head axis given."""
+RECORDS: list[dict] = []
+
+
+def _slices(gpu, ref, head_axis):
     g = np.moveaxis(np.asarray(gpu, dtype=np.float64), head_axis, 1)
     r = np.moveaxis(np.asarray(ref, dtype=np.float64), head_axis, 1)
     S, H = g.shape[0], g.shape[1]
-    g = g.reshape(S, H, -1)
-    r = r.reshape(S, H, -1)
+    return g.reshape(S, H, -1), r.reshape(S, H, -1)
+
+
+def slice_err(gpu: np.ndarray, ref: np.ndarray, head_axis: int) -> float:
+    """Max over (sequence, head) slices of max|g - r| / max|r|.  Arrays are
+    [seq][...][H][...] with the head axis given."""
+    g, r = _slices(gpu, ref, head_axis)
+    if g.size == 0:
+        return 0.0
     num = np.max(np.abs(g - r), axis=2)
     den = np.max(np.abs(r), axis=2)
     den = np.where(den == 0, 1.0, den)
     return float(np.max(num / den))
 
 
+def elementwise_err(gpu: np.ndarray, ref: np.ndarray, head_axis: int) -> float:
+    """Max over slices of max |g - r| / |r| over the elements with |r| >= 1e-2 max|r| of
+    their slice (reported beside the normwise figure, not judged)."""
+    g, r = _slices(gpu, ref, head_axis)
+    if g.size == 0:
+        return 0.0
+    ar = np.abs(r)
+    keep = ar >= 1e-2 * np.max(ar, axis=2, keepdims=True)
+    keep &= ar > 0
+    if not keep.any():
+        return 0.0
+    return float(np.max(np.where(keep, np.abs(g - r) / np.where(keep, ar, 1.0), 0.0)))
+
+
+def _record(kind, gpu, ref, head_axis) -> float:
+    e = slice_err(gpu, ref, head_axis)
+    RECORDS.append({"test": os.environ.get("PYTEST_CURRENT_TEST", "?").rsplit(" ", 1)[0], "what": kind,
+                    "normwise": e, "elementwise": elementwise_err(gpu, ref, head_axis)})
+    return e
+
+
 def y_err(gpu_y, ref_y) -> float:
-    return slice_err(gpu_y, ref_y, head_axis=2)       # y [seq][T][H][P]
+    return _record("y", gpu_y, ref_y, head_axis=2)       # y [seq][T][H][P]
 
 
 def state_err(gpu_s, ref_s) -> float:
-    return slice_err(gpu_s, ref_s, head_axis=1)       # state [seq][H][N][P]
+    return _record("state", gpu_s, ref_s, head_axis=1)   # state [seq][H][N][P]
 
 
 def head_slice(tok: synth.Tokens, layer: synth.Layer, h: int, H: int, G: int):

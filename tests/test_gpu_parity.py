@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (TOL, dev, dev_layer, dev_tokens, head_slice, state_err, y_err)
+from gpu_util import (BOUND, dev, dev_layer, dev_tokens, head_slice, state_err, y_err)
 from speculative_decode_amd import synth
 from speculative_decode_amd.ssm import SSMCache
 
@@ -79,7 +79,7 @@ def test_prefill_matches_oracle(dtype, shape, L, chunk, a_mode):
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
     ey, es = y_err(y, ry), state_err(logical_state(cache), rs)
     print(f"prefill {dtype} L={L} chunk={chunk} A={a_mode}: y {ey:.2e} state {es:.2e}")
-    assert ey <= TOL[dtype] and es <= TOL[dtype]
+    assert ey <= BOUND[dtype] and es <= BOUND[dtype]
     assert cache.pos().cpu().tolist() == [L] * Bt
 
 
@@ -95,8 +95,8 @@ def test_prefill_shapes(shape, dtype, chunk):
     cache = SSMCache(Bt, H, P, N, G, 4, dtype)
     y = sync_np(cache.prefill(*dev_tokens(tok), *dev_layer(layer), chunk=chunk))
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
-    assert y_err(y, ry) <= TOL[dtype]
-    assert state_err(logical_state(cache), rs) <= TOL[dtype]
+    assert y_err(y, ry) <= BOUND[dtype]
+    assert state_err(logical_state(cache), rs) <= BOUND[dtype]
 
 
 def test_prefill_misaligned_inputs_take_the_vector_path():
@@ -113,8 +113,8 @@ def test_prefill_misaligned_inputs_take_the_vector_path():
     assert xm.data_ptr() % 16 != 0
     y = sync_np(cache.prefill(xm, B, C, dt, *dev_layer(layer), chunk=64))
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
-    assert y_err(y, ry) <= TOL[synth.BF16]
-    assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
+    assert y_err(y, ry) <= BOUND[synth.BF16]
+    assert state_err(logical_state(cache), rs) <= BOUND[synth.BF16]
 
 
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
@@ -170,8 +170,8 @@ def test_prefill_continue_after_pending_rows(shape, chunk):
     _, h1 = oracle.prefill(a.x.f64, a.B.f64, a.C.f64, a.dt.f64, layer.A.f64, layer.D.f64)
     h1 = oracle.commit(h1, d.x.f64, d.B.f64, d.dt.f64, layer.A.f64, layer.D.f64, j)
     ry, rs = oracle.prefill(c.x.f64, c.B.f64, c.C.f64, c.dt.f64, layer.A.f64, layer.D.f64, h0=h1)
-    assert y_err(y2, ry) <= TOL[dtype]
-    assert state_err(logical_state(cache), rs) <= TOL[dtype]
+    assert y_err(y2, ry) <= BOUND[dtype]
+    assert state_err(logical_state(cache), rs) <= BOUND[dtype]
     assert cache.pos().cpu().tolist() == [L1 + int(j[0]) + L2, L1 + int(j[1]) + L2]
 
 
@@ -191,8 +191,8 @@ def test_prefill_back_to_back_single_launch(L):
         ys.append(sync_np(cache.prefill(*dev_tokens(one), A, D, slot0=b, chunk=256)))
     assert cache.status() == -1
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
-    assert y_err(np.concatenate(ys), ry) <= TOL[synth.BF16]
-    assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
+    assert y_err(np.concatenate(ys), ry) <= BOUND[synth.BF16]
+    assert state_err(logical_state(cache), rs) <= BOUND[synth.BF16]
 
 
 # The single launch's column slab follows from the number of chunk-heads (P halved until
@@ -220,7 +220,7 @@ def test_prefill_single_launch_configs(N, Bt):
     ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
     ey, es = y_err(y, ry), state_err(logical_state(cache), rs)
     print(f"  y {ey:.2e} state {es:.2e}")
-    assert ey <= TOL[synth.BF16] and es <= TOL[synth.BF16]
+    assert ey <= BOUND[synth.BF16] and es <= BOUND[synth.BF16]
 
 
 @pytest.mark.parametrize("want_y", [True, False], ids=["y", "state_only"])
@@ -254,8 +254,8 @@ def test_single_launch_continue(want_y):
     h1 = oracle.commit(h1, d.x.f64, d.B.f64, d.dt.f64, layer.A.f64, layer.D.f64, j)
     ry, rs = oracle.prefill(c.x.f64, c.B.f64, c.C.f64, c.dt.f64, layer.A.f64, layer.D.f64, h0=h1)
     if want_y:
-        assert y_err(sync_np(y2), ry) <= TOL[synth.BF16]
-    assert state_err(logical_state(cache), rs) <= TOL[synth.BF16]
+        assert y_err(sync_np(y2), ry) <= BOUND[synth.BF16]
+    assert state_err(logical_state(cache), rs) <= BOUND[synth.BF16]
     assert cache.pos().cpu().tolist() == [L1 + int(j[0]) + L2, L1 + int(j[1]) + L2]
 
 
@@ -314,12 +314,12 @@ def test_verify_rounds_against_oracle(dtype, shape, K, k_max):
         dx, dB, dC, ddt = dev_tokens(drf)
         yv = sync_np(cache.verify(dx, dB, dC, ddt, A, D))
         ry = oracle.verify(ref, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, layer.A.f64, layer.D.f64)
-        assert y_err(yv, ry) <= TOL[dtype], r
+        assert y_err(yv, ry) <= BOUND[dtype], r
         cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt, A, D, materialize=(r == 3))
         ref = oracle.commit(ref, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j)
         pos += j
     assert np.array_equal(cache.pos().cpu().numpy(), pos)
-    assert state_err(logical_state(cache), ref) <= TOL[dtype]
+    assert state_err(logical_state(cache), ref) <= BOUND[dtype]
 
 
 def _prefilled_cache(rng, Bt, H, P, N, G, k_max, dtype, L=50):
@@ -413,12 +413,36 @@ def test_bad_accepted_length_sets_error_and_changes_nothing():
     assert cache.err().cpu().tolist() == [1, 1, 0]
     assert cache.pos().cpu().tolist() == [50, 50, 52]
     ref = oracle.commit(ref, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, np.array([0, 0, 2]))
-    assert state_err(logical_state(cache), ref) <= TOL[synth.BF16]
+    assert state_err(logical_state(cache), ref) <= BOUND[synth.BF16]
     assert cache.status(clear=True) == 0
     assert cache.status() == -1
     # the protocol goes on
     cache.verify(dx, dB, dC, ddt, A, D)
     cache.commit(torch.zeros(Bt, dtype=torch.int32, device="cuda"), dx, dB, ddt)
+
+
+@pytest.mark.parametrize("kind", ["commit", "commit_tree"])
+def test_error_bits_accumulate(kind):
+    """err is the OR of every device error a slot has seen: a bad accepted length (or node)
+    adds MIL_DEVERR_ACCEPT to a bit set earlier and erases nothing."""
+    from speculative_decode_amd._lib import MIL_DEVERR_ACCEPT, MIL_DEVERR_SCAN, MIL_DEVERR_TREE
+    rng = np.random.default_rng(83)
+    Bt, H, P, N, G, K = 3, 4, 64, 32, 2, 4
+    layer, pre, cache, A, D = _prefilled_cache(rng, Bt, H, P, N, G, K, synth.BF16)
+    cache.err().copy_(torch.tensor([MIL_DEVERR_SCAN, MIL_DEVERR_TREE, 0], dtype=torch.int32, device="cuda"))
+    drf = synth.draw_tokens(rng, Bt, K, H, P, N, G, synth.BF16)
+    dx, dB, dC, ddt = dev_tokens(drf)
+    bad = np.array([K + 1, 2, -3], dtype=np.int32)  # slot 1 is fine
+    if kind == "commit":
+        cache.verify(dx, dB, dC, ddt, A, D)
+        cache.commit(torch.from_numpy(bad).cuda(), dx, dB, ddt)
+    else:
+        parent = torch.from_numpy(np.tile(np.arange(-1, K - 1, dtype=np.int32), (Bt, 1))).cuda()
+        cache.verify_tree(parent, dx, dB, dC, ddt, A, D)
+        cache.commit_tree(parent, torch.from_numpy(np.array([K, 1, -2], dtype=np.int32)).cuda(), dx, dB, ddt)
+    torch.cuda.synchronize()
+    assert cache.err().cpu().tolist() == [MIL_DEVERR_SCAN | MIL_DEVERR_ACCEPT, MIL_DEVERR_TREE, MIL_DEVERR_ACCEPT]
+    assert cache.pos().cpu().tolist() == [50, 52, 50]
 
 
 def test_protocol_order_errors():

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, dev_layer, dev_tokens, state_err, y_err
+from gpu_util import BOUND, dev_layer, dev_tokens, state_err, y_err
 from speculative_decode_amd import _lib as L
 from speculative_decode_amd import synth
 from speculative_decode_amd.ssm import SSMCache
@@ -64,7 +64,7 @@ def test_mixed_protocol_against_oracle(shape, dtype, K, seed):
     layer = synth.draw_layer(rng, H)
     A, D = dev_layer(layer)
     Af, Df = layer.A.f64, layer.D.f64
-    tol = TOL[dtype]
+    tol = BOUND[dtype]
 
     L0 = int(rng.integers(20, 300))
     pre = synth.draw_tokens(rng, Bt, L0, H, P, N, G, dtype)
