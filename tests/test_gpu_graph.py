@@ -100,3 +100,90 @@ def test_graph_replays_match_eager(greedy):
             assert torch.equal(ye, stat[li]["y"]), (rnd, li)
             assert torch.equal(c.state(), sets[1][li].state()), (rnd, li)
             assert torch.equal(c.pos(), sets[1][li].pos()) and torch.equal(c.pending(), sets[1][li].pending())
+
+
+def test_graph_decode_step_at_hybrid_layer_shape_matches_oracle():
+    """The decode step of the hybrid workload's layer shape (32 sequences, 32 heads,
+    P = 128, N = 256, 8 groups, K = 4, accepted lengths ~ Geometric(0.3) capped at 4) for
+    three layers, captured once and replayed for four rounds.  Each round, two sampled heads
+    of every layer are checked against the oracle: the drafts' y against oracle verify
+    from the oracle's committed state, and the stored state against the oracle's state
+    through the previous round's accepted drafts (this round's verify folded them in);
+    replay == eager stays bit for bit on the whole layer."""
+    import oracle
+    from gpu_util import BOUND, head_slice, state_err, y_err
+
+    rng = np.random.default_rng(5005)
+    layers, Bt, H, P, N, G, K, L0 = 3, 32, 32, 128, 256, 8, 4, 256
+    dtype = synth.BF16
+    lay = [synth.draw_layer(rng, H) for _ in range(layers)]
+    params = [dev_layer(l) for l in lay]
+    pres = [synth.draw_tokens(rng, Bt, L0, H, P, N, G, dtype) for _ in range(layers)]
+    sets = []
+    for _ in range(2):  # [0] eager, [1] graph
+        cs = []
+        for li in range(layers):
+            c = SSMCache(Bt, H, P, N, G, K, dtype)
+            c.prefill(*dev_tokens(pres[li]), *params[li], want_y=False)
+            cs.append(c)
+        sets.append(cs)
+    heads = [[int(h) for h in rng.choice(H, size=2, replace=False)] for _ in range(layers)]
+    ref = {}  # (layer, head) -> oracle committed state [Bt][1][N][P]
+    for li in range(layers):
+        for h in heads[li]:
+            x, B, C, dt, A, D = head_slice(pres[li], lay[li], h, H, G)
+            _, ref[li, h] = oracle.prefill(x, B, C, dt, A, D)
+    torch.cuda.synchronize()
+
+    stat = [dict(x=torch.empty((Bt, K, H, P), dtype=torch.bfloat16, device="cuda"),
+                 B=torch.empty((Bt, K, G, N), dtype=torch.bfloat16, device="cuda"),
+                 C=torch.empty((Bt, K, G, N), dtype=torch.bfloat16, device="cuda"),
+                 dt=torch.empty((Bt, K, H), dtype=torch.bfloat16, device="cuda"),
+                 j=torch.zeros(Bt, dtype=torch.int32, device="cuda"),
+                 y=torch.empty((Bt, K, H, P), dtype=torch.float32, device="cuda")) for _ in range(layers)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for li in range(layers):
+            s = stat[li]
+            sets[1][li].verify(s["x"], s["B"], s["C"], s["dt"], *params[li], y=s["y"])
+            sets[1][li].commit(s["j"], s["x"], s["B"], s["dt"])
+    torch.cuda.synchronize()
+
+    pos = [np.full(Bt, L0) for _ in range(layers)]
+    for rnd in range(4):
+        rounds = []
+        for li in range(layers):
+            drf = synth.draw_tokens(rng, Bt, K, H, P, N, G, dtype)
+            j = synth.draw_accept_geometric(rng, Bt, K)
+            x, B, C, dt = dev_tokens(drf)
+            for key, t in (("x", x), ("B", B), ("C", C), ("dt", dt)):
+                stat[li][key].copy_(t)
+            stat[li]["j"].copy_(torch.from_numpy(j).cuda())
+            rounds.append((drf, j))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li in range(layers):
+            drf, j = rounds[li]
+            yg = stat[li]["y"].cpu().numpy()
+            st = sets[1][li].state().cpu().numpy()
+            for h in heads[li]:
+                x, B, C, dt, A, D = head_slice(drf, lay[li], h, H, G)
+                ry = oracle.verify(ref[li, h], x, B, C, dt, A, D)
+                assert y_err(yg[:, :, h:h + 1], ry) <= BOUND[dtype], (rnd, li, h)
+                # the stored state: this round's verify folded the previous round's rows
+                assert state_err(st[:, h:h + 1].astype(np.float64), ref[li, h]) <= BOUND[dtype], (rnd, li, h)
+                ref[li, h] = oracle.commit(ref[li, h], x, B, dt, A, D, j)
+            assert sets[1][li].pending().cpu().tolist() == j.tolist()
+            pos[li] = pos[li] + j
+            assert sets[1][li].pos().cpu().numpy().tolist() == pos[li].tolist()
+            # the same round eagerly on the twin caches: bit for bit
+            c = sets[0][li]
+            xe, Be, Ce, dte = dev_tokens(drf)
+            ye = c.verify(xe, Be, Ce, dte, *params[li])
+            c.commit(torch.from_numpy(j).cuda(), xe, Be, dte)
+            torch.cuda.synchronize()
+            assert torch.equal(ye, stat[li]["y"]), (rnd, li)
+            assert torch.equal(c.state(), sets[1][li].state()), (rnd, li)
