@@ -221,6 +221,26 @@ int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_
                           const float *A, const float *D, void *ws, size_t ws_bytes,
                           uint32_t flags, mil_stream_t stream);
 
+/*
+ * mil_ssm_commit_greedy for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * results and errors, without ws / ws_bytes: the partial maxima go to a scratch array the
+ * library owns, MIL_GREEDY_NOALLOC_SCRATCH_BYTES in every GPU's memory, held until the
+ * process ends.  Nothing is allocated by this call (its first call on a device looks up
+ * that device's array).  batch * K above MIL_GREEDY_NOALLOC_MAX_ROWS returns
+ * MIL_E_WORKSPACE and enqueues nothing.  Every call on one GPU shares that GPU's array
+ * and leaves its contents behind (nothing in it needs clearing: each call writes every
+ * entry it reads), so calls that may overlap on one GPU (other streams, other threads)
+ * race and must not be made.
+ */
+#define MIL_GREEDY_NOALLOC_MAX_ROWS 512
+#define MIL_GREEDY_NOALLOC_SCRATCH_BYTES (256 * 1024)
+int mil_ssm_commit_greedy_noalloc(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens,
+                                  const void *logits, int32_t vocab, int32_t logits_dtype,
+                                  int32_t *accepted, int32_t *verifier_tokens,
+                                  const void *x, const void *B, const void *dt,
+                                  const float *A, const float *D, uint32_t flags, mil_stream_t stream);
+
 /* ---- Tree drafts ----
  *
  * Speculative decoding with tree-organised candidates (named among the variants in the

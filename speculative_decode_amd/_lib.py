@@ -28,8 +28,9 @@ EXPORTS = [
     "mil_ssm_cache_init", "mil_ssm_cache_attach", "mil_ssm_prefill_workspace_bytes", "mil_ssm_prefill", "mil_ssm_verify",
     "mil_ssm_commit", "mil_ssm_cache_status", "mil_ssm_cache_phase", "mil_ssm_cache_trace",
     "mil_ssm_greedy_workspace_bytes", "mil_ssm_commit_greedy", "mil_ssm_project_workspace_bytes", "mil_ssm_project",
-    "mil_ssm_verify_tree", "mil_ssm_commit_tree", "mil_ssm_prefill_kernels",
+    "mil_ssm_verify_tree", "mil_ssm_commit_tree", "mil_ssm_prefill_kernels", "mil_ssm_commit_greedy_noalloc",
 ]
+MIL_GREEDY_NOALLOC_MAX_ROWS = 512
 TRACE = {"off": 0, "verify": 1, "fold": 2, "commit": 3, "prefill_state": 4, "prefill_pass": 5, "prefill_out": 6,
          "accept": 7, "prefill_scan": 8}
 
@@ -87,6 +88,8 @@ def lib():
         "mil_ssm_greedy_workspace_bytes": ([dims_p, i32, i32], sz),
         "mil_ssm_commit_greedy": ([cache_p, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
                                   ctypes.c_int),
+        "mil_ssm_commit_greedy_noalloc": ([cache_p, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, u32, vp],
+                                          ctypes.c_int),
         "mil_ssm_project_workspace_bytes": ([dims_p, i32, i32], sz),
         "mil_ssm_verify_tree": ([cache_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "mil_ssm_prefill_kernels": ([cache_p, i32, i32, i32], ctypes.c_int),

@@ -286,10 +286,15 @@ size_t mil_ssm_greedy_workspace_bytes(const mil_ssm_dims *d, int32_t K, int32_t 
     return (size_t)greedy_workspace_bytes(d->batch, K);
 }
 
-int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
-                          int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
-                          const void *x, const void *B, const void *dt, const float *A, const float *D, void *ws,
-                          size_t ws_bytes, uint32_t flags, mil_stream_t stream) {
+}  // extern "C"
+
+namespace {
+// mil_ssm_commit_greedy with its workspace given; `noalloc`: the workspace is the
+// library's scratch (checked for size against the batch and K, not against ws_bytes).
+int commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits, int32_t vocab,
+                  int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens, const void *x, const void *B,
+                  const void *dt, const float *A, const float *D, void *ws, size_t ws_bytes, uint32_t flags,
+                  mil_stream_t stream, bool noalloc) {
     CacheImpl *c = impl(cache);
     if (!c) return MIL_E_INVALID;
     if (c->phase != kVerified) return MIL_E_ORDER;
@@ -300,6 +305,11 @@ int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_
     const bool mat = (flags & MIL_COMMIT_MATERIALIZE) != 0;
     if (mat && (!A || !D)) return MIL_E_INVALID;
     const int64_t need = greedy_workspace_bytes(c->dims.batch, K);
+    if (noalloc) {
+        if ((int64_t)c->dims.batch * K > MIL_GREEDY_NOALLOC_MAX_ROWS) return MIL_E_WORKSPACE;
+        if (greedy_noalloc_scratch(&ws) != hipSuccess) return MIL_E_HIP;
+        ws_bytes = MIL_GREEDY_NOALLOC_SCRATCH_BYTES;
+    }
     if (!ws || (int64_t)ws_bytes < need) return MIL_E_WORKSPACE;
     const int eb = elt_bytes(c->dtype);
     if (!aligned(draft_tokens, 4) || !aligned(accepted, 4) || (verifier_tokens && !aligned(verifier_tokens, 4)) ||
@@ -317,6 +327,25 @@ int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_
     c->phase = kReady;
     c->verified_k = 0;
     return MIL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
+                          int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
+                          const void *x, const void *B, const void *dt, const float *A, const float *D, void *ws,
+                          size_t ws_bytes, uint32_t flags, mil_stream_t stream) {
+    return commit_greedy(cache, K, draft_tokens, logits, vocab, logits_dtype, accepted, verifier_tokens, x, B, dt, A,
+                         D, ws, ws_bytes, flags, stream, false);
+}
+
+int mil_ssm_commit_greedy_noalloc(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
+                                  int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
+                                  const void *x, const void *B, const void *dt, const float *A, const float *D,
+                                  uint32_t flags, mil_stream_t stream) {
+    return commit_greedy(cache, K, draft_tokens, logits, vocab, logits_dtype, accepted, verifier_tokens, x, B, dt, A,
+                         D, nullptr, 0, flags, stream, true);
 }
 
 size_t mil_ssm_project_workspace_bytes(const mil_ssm_dims *d, int32_t T, int32_t d_model) {

@@ -8,6 +8,7 @@
 // and sets pending = j, pos += j.  The state itself is not touched here; the next
 // verify (or an immediate fold) applies the pending rows.  Integer work only: exact.
 #include <algorithm>
+#include <mutex>
 
 #include "ssm_internal.h"
 
@@ -391,6 +392,37 @@ int greedy_splits(int batch, int K, int64_t vocab) {
 
 int64_t greedy_workspace_bytes(int batch, int K) {
     return ((int64_t)batch * K * kGreedySplitsMax * 8 + 255) / 256 * 256;
+}
+
+// ---- the greedy commit's scratch for callers that cannot allocate ----
+// One array per GPU, in the library's own device memory (held until the process ends).
+// Host code never passes `scratch` itself to a kernel: its name is a host-side stand-in,
+// not a device address.  The device address is looked up once per device, with that
+// device current, and kept; kernels get that address, as they get a workspace.
+static __device__ __align__(256) uint64_t scratch[MIL_GREEDY_NOALLOC_SCRATCH_BYTES / 8];
+static_assert(MIL_GREEDY_NOALLOC_MAX_ROWS * kGreedySplitsMax * 8 <= MIL_GREEDY_NOALLOC_SCRATCH_BYTES,
+              "the no-alloc scratch holds the partial keys of its largest accepted size");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t greedy_noalloc_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_commit_greedy(const CacheImpl &c, int K, const int32_t *draft, const void *logits, int vocab,

@@ -88,6 +88,9 @@ int64_t greedy_workspace_bytes(int batch, int K);
 hipError_t launch_commit_greedy(const CacheImpl &c, int K, const int32_t *draft, const void *logits, int vocab,
                                 int logits_dtype, int32_t *accepted, int32_t *tokens, const void *x, const void *B,
                                 const void *dt, void *ws, hipStream_t s);
+// Device address of the calling thread's current device's no-alloc greedy scratch
+// (MIL_GREEDY_NOALLOC_SCRATCH_BYTES), looked up on the first call per device.
+hipError_t greedy_noalloc_scratch(void **out);
 
 // Chunked prefill (three phases: chunk states, inter-chunk pass, chunk outputs).  The
 // inter-chunk pass also sets pos[slot] = L (or += L when cont) for the prefilled slots

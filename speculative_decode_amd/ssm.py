@@ -238,10 +238,11 @@ class SSMCache:
         return int(L.lib().mil_ssm_greedy_workspace_bytes(ctypes.byref(self.dims), K, vocab))
 
     def commit_greedy(self, draft_tokens, logits, x, B, dt, A=None, D=None, materialize=False,
-                      want_tokens=False, accepted=None, ws=None):
+                      want_tokens=False, accepted=None, ws=None, noalloc=False):
         """Greedy acceptance on the device, then the commit: draft_tokens [batch][K] int32,
         logits [batch][K][vocab] (float32 or bfloat16).  Returns (accepted [batch] int32,
-        verifier_tokens [batch][K] int32 or None)."""
+        verifier_tokens [batch][K] int32 or None).  noalloc=True calls
+        mil_ssm_commit_greedy_noalloc (the library's own scratch, no workspace; `ws` unused)."""
         K = x.shape[1]
         self._check_tokens("commit_greedy", x, B, dt)
         self._check_shapes("commit_greedy", self.batch, K, x, B, None, dt, A, D, None)
@@ -260,6 +261,14 @@ class SSMCache:
         if accepted is None:
             accepted = torch.empty(self.batch, dtype=torch.int32, device=self.device)
         tokens = torch.empty((self.batch, K), dtype=torch.int32, device=self.device) if want_tokens else None
+        if noalloc:
+            st = L.lib().mil_ssm_commit_greedy_noalloc(ctypes.byref(self.desc), K, _ptr(draft_tokens), _ptr(logits),
+                                                       vocab, ldt, _ptr(accepted), _ptr(tokens), _ptr(x), _ptr(B),
+                                                       _ptr(dt), _ptr(A), _ptr(D),
+                                                       L.MIL_COMMIT_MATERIALIZE if materialize else 0,
+                                                       _stream(self.device))
+            L.check(st, "mil_ssm_commit_greedy_noalloc")
+            return accepted, tokens
         need = self.greedy_workspace_bytes(K, vocab)
         if ws is None:
             ws = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
