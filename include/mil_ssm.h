@@ -83,13 +83,14 @@ typedef struct {
  *           length or node), MIL_DEVERR_TREE (a tree link outside -1..k-1) and
  *           MIL_DEVERR_SCAN (a prefill's chunk-to-chunk handoff timed out; the slot's
  *           prefill results are then wrong).
- *   scan    int32 [batch][H][8][12]: single-launch prefill handoff words, one row per
- *           (slot, head, column slab): 8 chunk flags, then the row's epoch (the flag value
- *           of the row's last prefill), then padding.  mil_ssm_cache_init zeroes them; a
- *           prefill raises its flags to epoch + 1 and then stores epoch + 1 as the epoch,
- *           so the value that marks a call lives in the buffer itself: graph replays and
- *           byte copies of a cache (mil_ssm_cache_attach) stay correct.  A buffer whose
- *           rows hold a flag above their epoch is not a cache this library wrote.
+ *   scan    int32 [batch][H][8][68]: single-launch prefill handoff words, one row per
+ *           (slot, head, column slab): 64 chunk flags, then the row's epoch (that of the
+ *           row's last launch), then padding.  mil_ssm_cache_init zeroes them; a launch
+ *           takes epoch e = the row's epoch + 1, writes its flags as (e << 2) | kind and
+ *           then stores e as the row's epoch, so the value that marks a launch lives in the
+ *           buffer itself: graph replays and byte copies of a cache (mil_ssm_cache_attach)
+ *           stay correct.  A buffer whose rows hold a flag of a later epoch than their own
+ *           is not a cache this library wrote.
  * The logical state of slot b is `state` advanced through its `pending` rows.
  */
 typedef struct {

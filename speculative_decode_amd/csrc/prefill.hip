@@ -279,9 +279,11 @@ int64_t prefill_workspace_bytes(const mil_ssm_dims &d, int nseq, int L, int chun
     const int64_t nch = (L + chunk - 1) / chunk;
     const int64_t states = (int64_t)nseq * nch * d.nheads * d.dstate * d.headdim * 4;
     const int64_t tots = (int64_t)nseq * nch * d.nheads * 4;
-    // the single-launch form publishes each chunk's own state (and its decay, padded to 16
-    // floats per column slab, at most kScanSlabs slabs) instead
-    const int64_t chain = (int64_t)nseq * d.nheads * nch * ((int64_t)d.dstate * d.headdim + 16 * kScanSlabs) * 4;
+    // the single-launch form keeps one record per chunk of a launch (at most kScanChunks):
+    // the chunk's own state and the state after it, plus its decay padded to 16 floats per
+    // column slab (at most kScanSlabs slabs)
+    const int64_t nchl = std::min<int64_t>(nch, kScanChunks);
+    const int64_t chain = (int64_t)nseq * d.nheads * nchl * (2 * (int64_t)d.dstate * d.headdim + 16 * kScanSlabs) * 4;
     return std::max((states + 255) / 256 * 256 + (tots + 255) / 256 * 256, (chain + 255) / 256 * 256);
 }
 

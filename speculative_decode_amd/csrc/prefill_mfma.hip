@@ -94,6 +94,9 @@ struct MParams {
     int PS, nslab;         // phase 1: state rows p per workgroup, slabs per chunk-head
     // single-launch scan
     int32_t *scan;         // handoff words [batch][H][kScanSlabs][kScanRow]
+    int t0;                // single launch: token index of this launch's first chunk
+    int book;              // single launch: this launch sets pos / pending (the last launch of a prefill)
+    int pos_add;           // single launch: the caller's continue flag (pos grows by L, every slot's pending is 0)
     int32_t *err;          // [batch] device error words
     float *chain;          // [nseq][H][P/PC][nch][N*PC + 16] published chunk states (register order), E_c
 };
@@ -710,6 +713,16 @@ __device__ __forceinline__ int scan_load(const int32_t *f) {
 __device__ __forceinline__ void scan_store(int32_t *f, int v) {
     __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Epochs run 1..2^30-1 (then again from 1); a flag is (epoch << 2) | kind.
+constexpr int kFlagAggregate = 1;  // the chunk's own state S_c and decay E_c are published
+constexpr int kFlagInclusive = 2;  // the state after the chunk (the next chunk's h_in) is published
+__device__ __forceinline__ int scan_next_epoch(int e) {
+    const int n = (e + 1) & 0x3fffffff;
+    return n == 0 ? 1 : n;
+}
+__device__ __forceinline__ int scan_flag(int epoch, int kind) {
+    return static_cast<int>((static_cast<uint32_t>(epoch) << 2) | static_cast<uint32_t>(kind));
+}
 __device__ __forceinline__ float shared_load(const float *q) {
     return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -762,7 +775,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     const int h = hs % H, seq = hs / H;
     const int pc0 = slab * PC;
     const int g = h / (H / G);
-    const int c0 = c * Q, len = min(Q, p.L - c0);
+    const int c0 = p.t0 + c * Q, len = min(Q, p.L - c0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
     const int NT = blockDim.x, NW = NT >> 6;
     const int BS = N + 8, XS = Q + 8;
@@ -785,10 +798,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     const int I = wave < nt / 2 ? wave : nt - 1 - (wave - nt / 2);
     const bool active = I * kT < len;
     const int t = I * kT + l32;
-    // this call's flag value: the row's epoch + 1, read before anything else (the last
-    // chunk overwrites the epoch only after every workgroup of the row has published)
+    // this launch's epoch: the row's epoch + 1 (1..2^30-1, so no flag of it is ever zero),
+    // read before anything else (the last chunk overwrites the row's epoch only after
+    // every workgroup of the row has published)
     int32_t *flags = p.scan + (((size_t)(p.slot0 + seq) * H + h) * kScanSlabs + slab) * kScanRow;
-    const int epoch = __builtin_amdgcn_readfirstlane(scan_load(flags + kScanEpoch)) + 1;
+    const int epoch = scan_next_epoch(__builtin_amdgcn_readfirstlane(scan_load(flags + kScanEpoch)));
 
     // ---- staging: B, X and dt first (the chunk state needs them), then the C rows (only
     // the outputs need them), so that writing B and X to LDS waits for them alone ----
@@ -843,7 +857,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         sDt[tid] = dv;
         sDtA[tid] = dv * Ah;
     }
-    if (tid == 0) *reinterpret_cast<int *>(sMid + 64) = 0;  // the light waves' counter
+    if (tid < 2) reinterpret_cast<int *>(sMid + 64)[tid] = 0;  // the light and owning waves' counters
 #pragma unroll
     for (int j = 0; j < BI; ++j) {
         const int it = tid + j * NT;
@@ -985,19 +999,24 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
     }
 
-    // ---- publish: chunk 0 its outgoing state E_0 h0 + S_0 (it alone reads h0), chunks
-    // 1..nch-2 their own S_c, each with its decay E_c.  Each light wave waits for its own
-    // stores, then counts itself in LDS; the fourth raises the flag. ----
+    // ---- publish.  Each chunk's record holds its own contribution S_c with its decay E_c
+    // (the aggregate) and, once known, the state after the chunk (inclusive).  Chunk 0 has
+    // its inclusive state at once, E_0 h0 + S_0 (it alone reads h0); later chunks publish
+    // their aggregate now and their inclusive state after the look-back below.  Each light
+    // wave waits for its own stores, then counts itself in LDS; the fourth raises the flag.
+    // The last chunk publishes nothing: nothing waits for it. ----
     const int slot = p.slot0 + seq;
-    const size_t AGG = (size_t)N * PC + 16;  // floats per published chunk: state tiles (see shared_store4), then E_c
-    float *aggs = p.chain + (((size_t)seq * H + h) * nps + slab) * (size_t)p.nch * AGG;
-    const __amdgpu_buffer_rsrc_t agr = __builtin_amdgcn_make_buffer_rsrc(aggs, (short)0,
-                                                                         (int)(p.nch * AGG * 4), 0x00020000);
+    const size_t REC = 2 * (size_t)N * PC + 16;  // floats per chunk record: S_c tiles, E_c (16), inclusive tiles
+    const size_t INC = (size_t)N * PC + 16;      // offset of the inclusive tiles in a record
+    float *recs = p.chain + (((size_t)seq * H + h) * nps + slab) * (size_t)p.nch * REC;
+    const __amdgpu_buffer_rsrc_t agr = __builtin_amdgcn_make_buffer_rsrc(recs, (short)0,
+                                                                         (int)(p.nch * REC * 4), 0x00020000);
     float *cache = p.state + (size_t)(seq * H + h) * p.head_stride;
     const bool has_hin = p.cont || c > 0;
     const bool last = c == p.nch - 1;
-    const bool publish = !last;
-    int *sCnt = reinterpret_cast<int *>(sMid + 64);
+    int *sCnt = reinterpret_cast<int *>(sMid + 64);  // light waves past the first publication
+    int *sCnt2 = sCnt + 1;                            // owning waves past the inclusive publication
+    constexpr int NOWN = NTL * (PT < LW ? PT : LW);   // owning waves
     f32x16 hin[TPWL];
 #pragma unroll
     for (int i = 0; i < TPWL; ++i) hin[i] = f32x16{};
@@ -1013,8 +1032,8 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
     }
     if (light) {
-        if (publish) {
-            float *dst = aggs + (size_t)c * AGG;
+        if (!last) {
+            const size_t base = (size_t)c * REC + (c == 0 ? INC : 0);
             if (owner) {
 #pragma unroll
                 for (int i = 0; i < TPWL; ++i) {
@@ -1025,17 +1044,18 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
                             v[u] = c == 0 ? __builtin_fmaf(Ec, hin[i][4 * q + u], sacc[i][4 * q + u]) : sacc[i][4 * q + u];
-                        shared_store4(agr, (int)(((size_t)c * AGG + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
+                        shared_store4(agr, (int)((base + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
                     }
                 }
             }
-            if (tid == 0) shared_store(dst + N * PC, Ec);
+            if (c > 0 && tid == 0) shared_store(recs + (size_t)c * REC + (size_t)N * PC, Ec);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
         }
         // this wave has also read its partial tiles: the exchange area is free of it
         if (lane == 0) {
             const int before = atomicAdd(sCnt, 1);
-            if (publish && before == 3) scan_store(flags + c, epoch);
+            if (!last && before == 3)
+                scan_store(flags + c, scan_flag(epoch, c == 0 ? kFlagInclusive : kFlagAggregate));
         }
     }
     // ---- outputs: intra-chunk products, as in the output phase (only when y is wanted) ----
@@ -1098,55 +1118,75 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
         }
     }
-    // ---- the state entering this chunk: chunk 0's outgoing state folded through chunks
-    // 1..c-1 in order, h <- E_i h + S_i: the operations of a sequential pass in its order,
-    // so the result does not depend on which workgroup got where first.  Each owning wave
-    // waits for the c flags at once (lane i polls chunk i). ----
+    // ---- the state entering this chunk (c > 0), by decoupled look-back.  Lane i of each
+    // owning wave watches chunk c-1-i; the wave waits until some chunk j0 < c has published
+    // the state after it (inclusive) and every chunk after j0 has published its own
+    // contribution (aggregate), then reads j0's state and folds the contributions
+    // j0+1..c-1 in order, h <- E_j h + S_j.  Every inclusive record is that same fold in
+    // the same order, back to chunk 0's E_0 h0 + S_0, so h_in is bit for bit the state of
+    // a sequential pass over the chunks, whichever j0 the wait ends at. ----
     if (c > 0 && owner) {
-        const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+        const long long tw0 = (long long)__builtin_amdgcn_s_memrealtime();
+        int j0 = 0;
         while (true) {
-            const bool ok = lane >= c || scan_load(flags + lane) == epoch;
-            if (__all(ok)) break;
+            const int f = lane < c ? scan_load(flags + (c - 1 - lane)) : 0;
+            const bool ready = lane < c && (static_cast<uint32_t>(f) >> 2) == static_cast<uint32_t>(epoch);
+            const uint64_t mi = __ballot(ready && (f & 3) == kFlagInclusive);
+            const uint64_t mr = __ballot(ready);
+            if (mi) {
+                const int d = __builtin_ctzll(mi);            // nearest inclusive: chunk c-1-d
+                const uint64_t need = (1ull << d) - 1;        // chunks c-d..c-1: aggregates at least
+                if ((mr & need) == need) {
+                    j0 = c - 1 - d;
+                    break;
+                }
+            }
             __builtin_amdgcn_s_sleep(2);
-            if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kScanWaitTicks) {
+            if ((long long)__builtin_amdgcn_s_memrealtime() - tw0 > kScanWaitTicks) {
                 if (lane == 0) atomicOr(p.err + slot, MIL_DEVERR_SCAN);
                 break;
             }
         }
         // every earlier chunk of the row has published, so has read the old epoch: this
-        // call's value becomes the row's epoch (also after a timeout, so that no flag of
-        // this call is ever above the epoch)
+        // launch's epoch becomes the row's (also after a timeout, so that no flag of this
+        // launch is ever above the row's epoch)
         if (last && wave == 0 && lane == 0) scan_store(flags + kScanEpoch, epoch);
-        asm volatile("" ::: "memory");  // the published states are read after the flags
-        // chunk by chunk, every owned tile at once, with the next chunk's loads (clamped to
-        // the last one, so that no branch makes the compiler wait for all loads) in flight
-        // while this one is folded in
+        asm volatile("" ::: "memory");  // the records are read after the flags
+        // j0's inclusive tiles, then the aggregates j0+1..c-1, the next one's loads (clamped
+        // to the last, so that no branch makes the compiler wait for every load) in flight
+        // while one is folded in
         f32x16 nx[TPWL];
         float en = 0.f;
+        const int ja = min(j0 + 1, c - 1);
 #pragma unroll
         for (int i = 0; i < TPWL; ++i) {
             const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f32x4 v = shared_load4(agr, (int)(((size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+                const int lo = (q * 64 + lane) * 4 + tl * 1024;
+                const f32x4 v = shared_load4(agr, (int)(((size_t)j0 * REC + INC + lo) * 4));
+                const f32x4 a = shared_load4(agr, (int)(((size_t)ja * REC + lo) * 4));
 #pragma unroll
-                for (int u = 0; u < 4; ++u) nx[i][4 * q + u] = v[u];
+                for (int u = 0; u < 4; ++u) {
+                    hin[i][4 * q + u] = v[u];
+                    nx[i][4 * q + u] = a[u];
+                }
             }
         }
-        for (int j = 0; j < c; ++j) {
+        en = shared_load(recs + (size_t)ja * REC + (size_t)N * PC);
+        for (int j = j0 + 1; j < c; ++j) {
             f32x16 cur[TPWL];
 #pragma unroll
             for (int i = 0; i < TPWL; ++i) cur[i] = nx[i];
             const float e = en;
             const int jn = min(j + 1, c - 1);
-            const float *src = aggs + (size_t)jn * AGG;
-            en = shared_load(src + N * PC);
+            en = shared_load(recs + (size_t)jn * REC + (size_t)N * PC);
 #pragma unroll
             for (int i = 0; i < TPWL; ++i) {
                 const int tl = snt + NTL * (jpart + LW * i);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = shared_load4(agr, (int)(((size_t)jn * AGG + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+                    const f32x4 v = shared_load4(agr, (int)(((size_t)jn * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
 #pragma unroll
                     for (int u = 0; u < 4; ++u) nx[i][4 * q + u] = v[u];
                 }
@@ -1154,7 +1194,30 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 #pragma unroll
             for (int i = 0; i < TPWL; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) hin[i][r] = j == 0 ? cur[i][r] : __builtin_fmaf(e, hin[i][r], cur[i][r]);
+                for (int r = 0; r < 16; ++r) hin[i][r] = __builtin_fmaf(e, hin[i][r], cur[i][r]);
+        }
+        // the state after this chunk, E_c h_in + S_c, for the chunks after it
+        if (!last) {
+#pragma unroll
+            for (int i = 0; i < TPWL; ++i) {
+                const int tl = snt + NTL * (jpart + LW * i);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 v;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v[u] = __builtin_fmaf(Ec, hin[i][4 * q + u], sacc[i][4 * q + u]);
+                    shared_store4(agr, (int)(((size_t)c * REC + INC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (lane == 0) {
+                // the aggregate flag (raised by the fourth light wave) goes up before this one
+                for (int spin = 0; spin < (1 << 20); ++spin) {
+                    if (__hip_atomic_load(sCnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (atomicAdd(sCnt2, 1) == NOWN - 1) scan_store(flags + c, scan_flag(epoch, kFlagInclusive));
+            }
         }
     }
     // ---- the final state, from the last chunk (nothing reads h0 after chunk 0 has) ----
@@ -1170,11 +1233,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
     }
     if (p.y == nullptr) {
-        if (blockIdx.x == 0) {
+        if (p.book && blockIdx.x == 0) {
             for (int i = tid; i < p.batch; i += NT) {
                 const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
-                if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
-                if (mine || p.cont) p.pending[i] = 0;
+                if (mine) p.pos[i] = p.pos_add ? p.pos[i] + p.L : p.L;
+                if (mine || p.pos_add) p.pending[i] = 0;
             }
         }
         return;
@@ -1230,11 +1293,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             }
         }
     }
-    if (blockIdx.x == 0) {  // the slots' bookkeeping, off the start of the critical chunk
+    if (p.book && blockIdx.x == 0) {  // the slots' bookkeeping, off the start of the critical chunk
         for (int i = tid; i < p.batch; i += NT) {
             const bool mine = i >= p.slot0 && i < p.slot0 + p.nseq;
-            if (mine) p.pos[i] = p.cont ? p.pos[i] + p.L : p.L;
-            if (mine || p.cont) p.pending[i] = 0;
+            if (mine) p.pos[i] = p.pos_add ? p.pos[i] + p.L : p.L;
+            if (mine || p.pos_add) p.pending[i] = 0;
         }
     }
     if (!active) return;
@@ -1273,10 +1336,11 @@ int slab_width(int nseq, int nch, int H, int P) {
 // slabs leave no LDS for adding the token parts of the chunk state).
 int scan_slab(int nseq, int nch, int H, int P) { return std::min(slab_width(nseq, nch, H, P), 64); }
 
-// The single-launch kernel for these sizes, or null (its LDS does not fit, a chunk other
-// than 256 tokens, which it is not built for, or more chunks than it keeps flags for).
-const void *scan_kernel(int chunk, int nch, int N, int pc) {
-    if (chunk != 256 || nch > kScanChunks || scan_lds_bytes(chunk, N, pc) > kLdsMax) return nullptr;
+// The single-launch kernel for these sizes, or null (its LDS does not fit, or a chunk other
+// than 256 tokens, which it is not built for).  One launch covers at most kScanChunks
+// chunks; longer prompts take several launches, each continuing from the last.
+const void *scan_kernel(int chunk, int N, int pc) {
+    if (chunk != 256 || scan_lds_bytes(chunk, N, pc) > kLdsMax) return nullptr;
 #define MIL_SCAN_CASE(n, pp) \
     if (N == n && pc == pp) return reinterpret_cast<const void *>(chunk_scan_mfma<n, pp>);
     MIL_SCAN_CASE(64, 32) MIL_SCAN_CASE(64, 64) MIL_SCAN_CASE(128, 32) MIL_SCAN_CASE(128, 64)
@@ -1289,7 +1353,7 @@ const void *scan_kernel(int chunk, int nch, int N, int pc) {
 bool prefill_single_launch(int nseq, int L, int chunk, int H, int P, int N) {
     if (!prefill_mfma_supported(chunk, N, P)) return false;
     const int nch = (L + chunk - 1) / chunk;
-    return scan_kernel(chunk, nch, N, scan_slab(nseq, nch, H, P)) != nullptr;
+    return scan_kernel(chunk, N, scan_slab(nseq, std::min(nch, kScanChunks), H, P)) != nullptr;
 }
 
 // Shapes the matrix-core path covers: bf16 inputs, N and P multiples of 32 up to 256,
@@ -1330,6 +1394,12 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     p.nseq = nseq;
     p.batch = c.dims.batch;
     p.cont = cont ? 1 : 0;
+    p.t0 = 0;
+    p.book = 1;
+    p.pos_add = p.cont;
+    p.scan = nullptr;
+    p.err = nullptr;
+    p.chain = nullptr;
     const int64_t states = (int64_t)nseq * p.nch * p.H * p.N * p.P * 4;
     p.ws = static_cast<float *>(ws);
     p.ws_tot = reinterpret_cast<float *>(static_cast<char *>(ws) + (states + 255) / 256 * 256);
@@ -1338,22 +1408,35 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
 
     const int pc = slab_width(nseq, p.nch, p.H, p.P);
 
-    // one launch for all three phases where its LDS fits (chunks of 256, 8 waves)
-    const int spc = scan_slab(nseq, p.nch, p.H, p.P);
-    const void *kf = scan_kernel(chunk, p.nch, p.N, spc);
-    if (kf) {
+    // one launch for all three phases where its LDS fits (chunks of 256, 8 waves), per run
+    // of at most kScanChunks chunks: each later launch continues from the state the one
+    // before it wrote to the cache, and the last one does the slots' bookkeeping
+    if (scan_kernel(chunk, p.N, scan_slab(nseq, std::min(p.nch, kScanChunks), p.H, p.P))) {
+        const int nch_all = p.nch;
         p.scan = cache_scan(c);
         p.err = cache_err(c);
         p.chain = static_cast<float *>(ws);
-        hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
-        if (e != hipSuccess) return e;
-        void *args[] = {&p};
-        trace_begin(c, MIL_TRACE_PREFILL_SCAN, s);
-        e = hipLaunchKernel(kf, dim3(p.nch * nseq * p.H * (p.P / spc)), dim3(512), args,
-                            scan_lds_bytes(chunk, p.N, spc), s);
-        trace_end(c, MIL_TRACE_PREFILL_SCAN, s);
-        if (e != hipSuccess) return e;
-        return hipGetLastError();
+        p.pos_add = cont ? 1 : 0;
+        for (int c0 = 0; c0 < nch_all; c0 += kScanChunks) {
+            p.nch = std::min(kScanChunks, nch_all - c0);
+            p.t0 = c0 * chunk;
+            p.cont = (cont || c0 > 0) ? 1 : 0;
+            p.book = c0 + p.nch == nch_all ? 1 : 0;
+            const int spc = scan_slab(nseq, p.nch, p.H, p.P);
+            const void *kf = scan_kernel(chunk, p.N, spc);
+            if (!kf) return hipErrorInvalidValue;
+            hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+            if (e != hipSuccess) return e;
+            void *args[] = {&p};
+            trace_begin(c, MIL_TRACE_PREFILL_SCAN, s);
+            e = hipLaunchKernel(kf, dim3(p.nch * nseq * p.H * (p.P / spc)), dim3(512), args,
+                                scan_lds_bytes(chunk, p.N, spc), s);
+            trace_end(c, MIL_TRACE_PREFILL_SCAN, s);
+            if (e != hipSuccess) return e;
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
     const size_t l1 = state_lds_bytes(p.PS, p.N), l3 = out_lds_bytes(chunk, p.N, pc);
     const int tpw = (p.PS / kT) * (p.N / kT) / 4;

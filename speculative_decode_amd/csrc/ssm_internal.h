@@ -45,12 +45,13 @@ inline int32_t *cache_pos(const CacheImpl &c) { return reinterpret_cast<int32_t 
 inline int32_t *cache_pending(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.pending_off); }
 inline int32_t *cache_err(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.err_off); }
 // single-launch prefill handoff words: [slot][head][kScanSlabs][kScanRow], zeroed when the
-// cache is set up.  Per row: kScanChunks chunk flags, then the row's epoch (the value the
-// last call wrote into its flags); a call reads the epoch, raises its flags to epoch + 1
-// and stores epoch + 1 once every flag of the call is up, so the value lives on the device
-// with the cache (graph replays and byte copies of a cache carry it along)
+// cache is set up.  Per row: kScanChunks chunk flags, then the row's epoch (the epoch of
+// the row's last launch, 1..2^30-1).  A launch takes the next epoch e, writes its flags
+// as (e << 2) | kind and stores e as the row's epoch once every flag of the launch is up,
+// so the value that marks a launch lives on the device with the cache (graph replays and
+// byte copies of a cache carry it along)
 constexpr int kScanSlabs = 8;
-constexpr int kScanChunks = 8;  // chunks per prompt the single-launch prefill handles
+constexpr int kScanChunks = 64;  // chunks per launch of the single-launch prefill (longer prompts: more launches)
 constexpr int kScanRow = kScanChunks + 4;  // words per (slot, head, slab) row: flags, epoch, pad
 constexpr int kScanEpoch = kScanChunks;    // index of the epoch word in a row
 inline int32_t *cache_scan(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.scan_off); }

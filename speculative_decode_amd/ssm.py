@@ -104,11 +104,14 @@ class SSMCache:
     def err(self) -> torch.Tensor:
         return self._i32(self.layout.err_off)
 
+    SCAN_ROW, SCAN_EPOCH = 68, 64
+
     def scan_words(self) -> torch.Tensor:
-        """int32 view [batch][H][8][12] of the single-launch prefill's handoff rows (8 chunk
-        flags, the row's epoch, padding)."""
+        """int32 view [batch][H][8][68] of the single-launch prefill's handoff rows: 64 chunk
+        flags ((epoch << 2) | kind), the row's epoch, padding."""
         off = self.layout.scan_off
-        return self.buffer[off:off + self.batch * self.H * 8 * 12 * 4].view(torch.int32).view(self.batch, self.H, 8, 12)
+        n = self.batch * self.H * 8 * self.SCAN_ROW
+        return self.buffer[off:off + 4 * n].view(torch.int32).view(self.batch, self.H, 8, self.SCAN_ROW)
 
     def prefill_kernels(self, nseq, L_tokens, chunk=256) -> int:
         """Bit mask of the traceable kernels a prefill of these sizes launches (mil_ssm_prefill_kernels)."""

@@ -223,6 +223,54 @@ def test_prefill_single_launch_configs(N, Bt):
     assert ey <= BOUND[synth.BF16] and es <= BOUND[synth.BF16]
 
 
+LONG_CASES = [(L, a) for L in (2048, 2100, 4096, 8192) for a in ("zero", "tiny")] + [(16684, "tiny"), (16684, "cfg")]
+
+
+@pytest.mark.parametrize("L,a_mode", LONG_CASES, ids=[f"L{L}_{a}" for L, a in LONG_CASES])
+def test_single_launch_long_prompts(L, a_mode):
+    """Prompts of many chunks through the single launch with decoupled look-back: each
+    chunk publishes its own contribution, then (after looking back to the nearest chunk
+    that has published the state after it) the state after itself.  A = 0 and -1e-3 carry
+    the state across every chunk boundary.  16684 tokens (66 chunks) take two launches of
+    at most 64 chunks, the second continuing from the state the first wrote."""
+    from speculative_decode_amd import _lib
+    Bt, H, P, N, G = (1, 8, 128, 128, 2) if L <= 8192 else (1, 4, 128, 128, 1)
+    rng = np.random.default_rng(4600 + L)
+    layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, synth.BF16, a_mode)
+    cache = SSMCache(Bt, H, P, N, G, 4, synth.BF16)
+    assert cache.prefill_kernels(Bt, L) == 1 << _lib.TRACE["prefill_scan"]
+    A, D = dev_layer(layer)
+    print(f"single-launch prefill L={L} A={a_mode}", flush=True)
+    y = sync_np(cache.prefill(*dev_tokens(tok), A, D, chunk=256))
+    assert cache.status() == -1
+    ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
+    ey, es = y_err(y, ry), state_err(logical_state(cache), rs)
+    print(f"  y {ey:.2e} state {es:.2e}")
+    assert ey <= BOUND[synth.BF16] and es <= BOUND[synth.BF16]
+    assert cache.pos().cpu().tolist() == [L] * Bt
+    launches = -(-((L + 255) // 256) // 64)
+    epochs = cache.scan_words().cpu().numpy()[..., SSMCache.SCAN_EPOCH]
+    assert epochs.any() and set(np.unique(epochs[epochs != 0]).tolist()) <= set(range(1, launches + 1))
+
+
+def test_single_launch_long_prompt_is_bitwise_repeatable():
+    """The look-back may end at different chunks from one run to the next, but the state a
+    chunk receives is always the same fold in the same order: two runs of an 8192-token
+    prefill give the same bits."""
+    Bt, H, P, N, G, L = 1, 8, 128, 128, 2, 8192
+    rng = np.random.default_rng(4700)
+    layer, tok = make_layer_and_tokens(rng, Bt, L, H, P, N, G, synth.BF16, "tiny")
+    A, D = dev_layer(layer)
+    outs = []
+    for _ in range(2):
+        cache = SSMCache(Bt, H, P, N, G, 4, synth.BF16)
+        y = cache.prefill(*dev_tokens(tok), A, D, chunk=256)
+        torch.cuda.synchronize()
+        outs.append((y.cpu(), cache.state().contiguous().cpu()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 @pytest.mark.parametrize("want_y", [True, False], ids=["y", "state_only"])
 def test_single_launch_continue(want_y):
     """Prefill, verify, commit, then a several-chunk prefill that continues from the

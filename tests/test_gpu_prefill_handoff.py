@@ -91,7 +91,7 @@ def test_graph_replayed_prefill_matches_oracle(cont):
         if cont:
             ref_state = rs
     # four calls of one row: its epoch moved by one per replay (plus the eager prefill)
-    epochs = cache.scan_words().cpu().numpy()[..., 8]
+    epochs = cache.scan_words().cpu().numpy()[..., SSMCache.SCAN_EPOCH]
     assert epochs.any() and np.all(epochs[epochs != 0] == 4 + cont)
 
 
@@ -99,9 +99,9 @@ def test_prefill_on_attached_copy_with_flags_from_earlier_calls():
     """A cache that has run prefills is copied byte for byte to another buffer and
     attached: the copy's flags already hold the values of those calls.  Prefills on the copy
     (fresh and continuing) must match the oracle.  Then the same with the copy's rows set
-    to values by hand before a call: flags 1..8 under epoch 8 (a buffer whose calls used
-    other chunk counts), and every flag and epoch at 1000 (a buffer written by a process
-    that had run 1000 prefills)."""
+    to values by hand before a call: flags of epochs 1..8 under epoch 8 (a buffer whose
+    launches used other chunk counts), and every flag and epoch at 1000 (a buffer written
+    by a process that had run 1000 prefills)."""
     rng = np.random.default_rng(616)
     Bt, H, P, N, G = SHAPE
     layer = slow_layer(rng, H)
@@ -119,17 +119,20 @@ def test_prefill_on_attached_copy_with_flags_from_earlier_calls():
     assert copy.prefill_kernels(Bt, L_TOK) == SCAN_BIT
     torch.cuda.synchronize()
     assert np.array_equal(copy.scan_words().cpu().numpy(), src.scan_words().cpu().numpy())
-    epochs = copy.scan_words().cpu().numpy()[..., 8]
+    epochs = copy.scan_words().cpu().numpy()[..., SSMCache.SCAN_EPOCH]
     assert epochs.any() and np.all(epochs[epochs != 0] == 3)
     pos = L_TOK
     for rnd, (preset, cont) in enumerate([(False, True), (False, False), (True, True), (True, False)]):
-        if preset:  # small flags 1..8 under epoch 8, then every word 1000 (1000 earlier calls)
+        if preset:  # flags of epochs 1..8 under epoch 8, then every flag and epoch at 1000
             words = copy.scan_words()
+            E = SSMCache.SCAN_EPOCH
             if cont:
-                words[:, :, :, :8] = torch.arange(1, 9, dtype=torch.int32, device="cuda")
-                words[:, :, :, 8] = 8
+                ep = torch.arange(E, dtype=torch.int32, device="cuda") % 8 + 1
+                words[:, :, :, :E] = ep * 4 + 2  # (epoch << 2) | inclusive
+                words[:, :, :, E] = 8
             else:
-                words[:, :, :, :9] = 1000
+                words[:, :, :, :E] = 1000 * 4 + 2
+                words[:, :, :, E] = 1000
         tok = synth.draw_tokens(rng, Bt, L_TOK, H, P, N, G, synth.BF16)
         y = copy.prefill(*dev_tokens(tok), A, D, cont=cont)
         ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64,

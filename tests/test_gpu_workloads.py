@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import BOUND, dev_layer, dev_tokens, head_slice, slice_err
+from gpu_util import BOUND, dev_layer, dev_tokens, head_slice, slice_err, state_err, y_err
 from speculative_decode_amd import synth
 from speculative_decode_amd.ssm import SSMCache
 
@@ -115,25 +115,30 @@ def test_llama8b_batched_verify():
         assert slice_err(state[:, h:h + 1], st, head_axis=1) <= BOUND[w.dtype]
 
 
-def test_long_prefill_8192():
-    """One 8192-token scan, chunk 256: sampled heads' y and final state."""
+@pytest.mark.parametrize("a_mode", ["cfg", "zero", "tiny"])
+def test_long_prefill_8192(a_mode):
+    """The long-prefill workload (one 8192-token prompt, chunk 256, 32 heads, P = N = 128,
+    8 groups) in the launch the bench times: every head's y and final state against the
+    oracle, with the workload's decays and with A = 0 / -1e-3 on every head (the state
+    then crosses all 32 chunk boundaries)."""
+    from speculative_decode_amd import _lib
     w = synth.WORKLOADS["llama8b_long_prefill"]
     rng = np.random.default_rng(w.seed)
     layer = synth.draw_layer(rng, w.H)
+    if a_mode != "cfg":
+        layer = synth.Layer(synth.quantize(np.full(w.H, 0.0 if a_mode == "zero" else -1e-3), synth.F32), layer.D)
     tok = synth.draw_tokens(rng, w.batch, w.L, w.H, w.P, w.N, w.G, w.dtype)
     cache = SSMCache(w.batch, w.H, w.P, w.N, w.G, 4, w.dtype)
+    assert cache.prefill_kernels(w.batch, w.L, w.chunk) == 1 << _lib.TRACE["prefill_scan"]
     A, D = dev_layer(layer)
     y = cache.prefill(*dev_tokens(tok), A, D, chunk=w.chunk)
     torch.cuda.synchronize()
-    y = y.cpu().numpy()
-    state = cache.state().cpu().numpy()
-    for h in sampled_heads(w.H, w.G):
-        x, B, C, dt, Ah, Dh = head_slice(tok, layer, h, w.H, w.G)
-        ry, rs = oracle.prefill(x, B, C, dt, Ah, Dh)
-        ey = slice_err(y[:, :, h:h + 1], ry, head_axis=2)
-        es = slice_err(state[:, h:h + 1], rs, head_axis=1)
-        print(f"long prefill head {h}: y {ey:.2e} state {es:.2e}")
-        assert ey <= BOUND[w.dtype] and es <= BOUND[w.dtype]
+    assert cache.status() == -1
+    ry, rs = oracle.prefill(tok.x.f64, tok.B.f64, tok.C.f64, tok.dt.f64, layer.A.f64, layer.D.f64)
+    ey = y_err(y.cpu().numpy(), ry)
+    es = state_err(cache.state().cpu().numpy(), rs)
+    print(f"long prefill A={a_mode}: y {ey:.2e} state {es:.2e}")
+    assert ey <= BOUND[w.dtype] and es <= BOUND[w.dtype]
 
 
 def test_hybrid_decode_layer():
