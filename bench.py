@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the SSM layer's hot path on one MI355X.
 
-Default workload (`llama8b_single`): one Llama-3-8B-shaped sequence (32 heads, P = N =
-128, 8 B/C groups, bf16 token inputs, fp32 state).  One step is the whole path once:
-  prefill of a 1024-token prompt (chunk 256)  ->  verify K = 4 drafts  ->  commit j ~ U{0..4}
-on a fresh cache slot; steps rotate through independent caches and inputs whose total
-size exceeds the 256 MB Infinity Cache, so every step reads its inputs from HBM.
+Default workload (`hybrid_decode`): the decode step of a hybrid model's 24 SSM layers for
+32 sequences (32 heads, P = 128, expanded state N = 256, 8 B/C groups, bf16 token inputs,
+fp32 state, 4 GiB of caches in all), each sequence with a 1024-token context prefilled on
+the GPU.  One step is, for every layer, verify K = 4 drafts -> commit j ~ min(Geom(0.3)-1, 4).
+The same line carries the long prefill (`llama8b_long_prefill`: one 8192-token prompt of
+the Llama-3-8B layer shape, chunk 256) under "prefill", with its own roofline over the
+whole prefill and its own CPU baseline.  Inputs and caches rotate so that every step reads
+them from HBM, not the 256 MB Infinity Cache.
 
 Printed JSON line:
-  value                verified tokens/s = batch*K / (verify + commit time per step)
-  prefill_tokens_per_s batch*L / (prefill time per step)
+  value                verified tokens/s = batch*K / (time per step)
   hbm_gbs              verify's algorithmic bytes / verify kernel time
-  ms_per_step          whole step (prefill + verify + commit), HIP events; the steps are
-                       queued behind a spin kernel so that they run back to back and the
-                       events time the device, not the Python launch loop
+  ms_per_step          whole step, HIP events; the steps are queued behind a spin kernel so
+                       that they run back to back and the events time the device, not the
+                       Python launch loop
   host_us_per_step     the host's launch time per step (Python + C ABI calls)
   roofline             for the kernel with the largest time per step (HIP events around
                        its launches, recorded by the library's trace hook), against the
                        published peaks and against ceilings measured in the same run (a
                        512 MiB copy, an 8192^3 bf16 matrix product), with the fraction of
                        the attainable roofline max(bytes/8 TB/s, flops/peak) / time
+  prefill              the long prefill: prefill tokens/s, its roofline over all its
+                       launches (bytes and flops of the whole prefill over the time of one
+                       prefill, prefills back to back), its kernels, its CPU baseline
   cpu_baseline         the CPU oracle on a bounded sample of the same step
+Other workloads: --workload llama8b_single | llama8b_batched | llama8b_long_prefill |
+llama8b_batched_greedy | llama8b_batched_project | llama8b_batched_tree.
 """
 from __future__ import annotations
 
@@ -329,35 +336,63 @@ def run_gpu(args, w):
         torch.cuda.synchronize()
     R = len(sets)
 
+    def verify_part(s, mark=True, project_too=True):
+        st = sets[s % R]
+        for li, c in enumerate(st["caches"]):
+            dx, dB, dC, ddt = st["drf"][li]
+            if st.get("proj") and project_too:
+                # the drafts' x, B, C, dt projected from the input rows into the same buffers
+                pj = st["proj"][li]
+                tr = mark and li == 0 and trace_project[0]
+                if tr:
+                    evs["ta"][s].record()
+                project(pj["u"], *pj["w"], w.H, w.P, w.N, w.G, dt_bias=pj["bias"], out=(dx, dB, dC, ddt),
+                        ws=pj["ws"])
+                if tr:
+                    evs["tb"][s].record()
+            if st.get("tree"):
+                c.verify_tree(st["tree"][li]["par"], dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
+            else:
+                c.verify(dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
+
+    def commit_part(s):
+        st = sets[s % R]
+        for li, c in enumerate(st["caches"]):
+            dx, dB, dC, ddt = st["drf"][li]
+            if st.get("tree"):
+                tr = st["tree"][li]
+                c.commit_tree(tr["par"], tr["node"], dx, dB, ddt)
+            elif st.get("greedy"):
+                gr = st["greedy"][li]
+                c.commit_greedy(gr["dtok"], gr["logits"], dx, dB, ddt, accepted=gr["acc"], ws=gr["ws"])
+            else:
+                c.commit(st["j"][li], dx, dB, ddt)
+
     def step(s, mark=True):
         st = sets[s % R]
         if kind in ("full", "prefill"):
             x, B, C, dt = st["pre"]
             st["caches"][0].prefill(x, B, C, dt, *AD[0], y=st["y"], chunk=w.chunk, ws=st["ws"])
         if kind in ("full", "verify"):
-            for li, c in enumerate(st["caches"]):
-                dx, dB, dC, ddt = st["drf"][li]
-                if st.get("proj"):
-                    # the drafts' x, B, C, dt projected from the input rows into the same buffers
-                    pj = st["proj"][li]
-                    tr = mark and li == 0 and trace_project[0]
-                    if tr:
-                        evs["ta"][s].record()
-                    project(pj["u"], *pj["w"], w.H, w.P, w.N, w.G, dt_bias=pj["bias"], out=(dx, dB, dC, ddt),
-                            ws=pj["ws"])
-                    if tr:
-                        evs["tb"][s].record()
-                if st.get("tree"):
-                    tr = st["tree"][li]
-                    c.verify_tree(tr["par"], dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
-                    c.commit_tree(tr["par"], tr["node"], dx, dB, ddt)
-                    continue
-                c.verify(dx, dB, dC, ddt, *AD[li], y=st["yv"][li])
-                if st.get("greedy"):
-                    gr = st["greedy"][li]
-                    c.commit_greedy(gr["dtok"], gr["logits"], dx, dB, ddt, accepted=gr["acc"], ws=gr["ws"])
-                else:
-                    c.commit(st["j"][li], dx, dB, ddt)
+            # every layer's verify, then every layer's commit: the accepted lengths are known
+            # only once the last layer has run
+            verify_part(s, mark)
+            commit_part(s)
+
+    def verify_pass():
+        """Time per verify launch from launches back to back: the verifies of n whole steps
+        (distinct caches: every layer of n rotating sets) between two events, then their
+        commits.  No event sits between the launches, so no dispatch latency is added."""
+        n = max(1, min(args.steps, R))
+        hold(n)
+        e0.record()
+        for s in range(n):
+            verify_part(s, mark=False, project_too=False)
+        e1.record()
+        for s in range(n):
+            commit_part(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n * nlayers)
 
     trace_project = [False]  # the projection is traced with events on torch's stream, around the call
 
@@ -454,6 +489,8 @@ def run_gpu(args, w):
         step_ms = vc_ms = e0.elapsed_time(e1) / args.steps
         pre_ms = 0.0
         dom_ms = traced_ms = ktime[dominant]
+        if dominant == "verify":
+            dom_ms = verify_pass()
     else:
         # The timed region: K whole steps back to back between two events, queued behind
         # the hold as above (`host_us_per_step` reports the host's own launch rate).  Even
@@ -481,6 +518,8 @@ def run_gpu(args, w):
         for s in range(args.steps):
             set_trace(s, None)
         dom_ms = traced_ms = float(np.mean([evs["ta"][s].elapsed_time(evs["tb"][s]) for s in range(args.steps)]))
+        if kind == "verify" and dominant == "verify":
+            dom_ms = verify_pass()
         if kind == "full":
             # The prefill alone, K launches back to back between two events; verify +
             # commit take the rest of the step.
@@ -508,6 +547,7 @@ def run_gpu(args, w):
         pw = prefill_work(w, w.L)
         work.update({k: (pw[k][0] * Bt, pw[k][1] * Bt) for k in ("prefill_state", "prefill_pass", "prefill_out")})
         work["prefill_scan"] = (pw["all"][0] * Bt, pw["all"][1] * Bt)
+        work["prefill_all"] = work["prefill_scan"]
     if kind in ("full", "verify"):
         # rows pending at a verify: none after a prefill ("full"); else the previous
         # commit's accepted lengths, whose mean is that of the j distribution
@@ -564,14 +604,57 @@ def measured_peaks():
     return copy_gbs, gemm_tflops
 
 
-def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
-    """The oracle, as it stands, on the same step (prefill + verify + commit) of the same
-    shapes, repeated on one seeded sample until about budget_s seconds of CPU work."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def run_cpu_baseline(w, kind, budget_s=10.0, max_steps=200):
+    """The oracle, as it stands, on a bounded sample of the same step, repeated until
+    about budget_s seconds of CPU work.  "full": prefill + verify + commit of the whole
+    step.  "prefill": the whole prefill (one repetition may exceed the budget).  "verify":
+    single layers of the step (verify K drafts + commit of every sequence, from a random
+    fp64 state of the layer's shape; the oracle's cost does not depend on the values),
+    scaled to the step's layer count."""
     import oracle
     from speculative_decode_amd import synth
     rng = np.random.default_rng(w.seed + 77)
     layer = synth.draw_layer(rng, w.H)
     threads = oracle.default_threads()
+    A, D = layer.A.f64, layer.D.f64
+    if kind == "prefill":
+        pre = synth.draw_tokens(rng, w.batch, w.L, w.H, w.P, w.N, w.G, w.dtype)
+        t, reps = 0.0, 0
+        while reps < max_steps and t < budget_s:
+            a = time.perf_counter()
+            oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, A, D, nthreads=threads)
+            t += time.perf_counter() - a
+            reps += 1
+        return dict(value=w.batch * w.L * reps / t, unit="prefill tokens/s", cores=threads, kind="oracle",
+                    cpu=_cpu_model(), sample=f"{reps} whole prefills of {w.batch} x {w.L} tokens, same shapes, "
+                                             f"fp64 oracle, {t:.1f} s")
+    if kind == "verify":
+        state = rng.normal(0.0, 0.1, size=(w.batch, w.H, w.N, w.P))
+        drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
+        j = (synth.draw_accept_geometric(rng, w.batch, w.K) if w.accept == "geometric"
+             else synth.draw_accept_uniform(rng, w.batch, w.K))
+        t, reps = 0.0, 0
+        while reps < max_steps and t < budget_s:
+            a = time.perf_counter()
+            oracle.verify(state, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, A, D, nthreads=threads)
+            oracle.commit(state, drf.x.f64, drf.B.f64, drf.dt.f64, A, D, j, nthreads=threads)
+            t += time.perf_counter() - a
+            reps += 1
+        per_step = t / reps * w.layers
+        return dict(value=w.batch * w.K / per_step, unit="verified tokens/s", cores=threads, kind="oracle",
+                    cpu=_cpu_model(),
+                    sample=f"{reps} single layers (verify {w.K} + commit, {w.batch} sequences) of the "
+                           f"{w.layers}-layer step, fp64 oracle, {t:.1f} s, scaled to {w.layers} layers")
     pre = synth.draw_tokens(rng, w.batch, w.L, w.H, w.P, w.N, w.G, w.dtype)
     drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
     j = synth.draw_accept_uniform(rng, w.batch, w.K)
@@ -579,24 +662,16 @@ def run_cpu_baseline(w, budget_s=10.0, max_steps=200):
     steps = 0
     while steps < max_steps and (t_pre + t_vc) < budget_s:
         a = time.perf_counter()
-        _, h = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64, nthreads=threads)
+        _, h = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, A, D, nthreads=threads)
         b = time.perf_counter()
-        oracle.verify(h, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, layer.A.f64, layer.D.f64, nthreads=threads)
-        oracle.commit(h, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j, nthreads=threads)
+        oracle.verify(h, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, A, D, nthreads=threads)
+        oracle.commit(h, drf.x.f64, drf.B.f64, drf.dt.f64, A, D, j, nthreads=threads)
         c = time.perf_counter()
         t_pre += b - a
         t_vc += c - b
         steps += 1
-    cpu = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
     return dict(value=w.batch * w.K * steps / t_vc, unit="verified tokens/s", cores=threads, kind="oracle",
-                prefill_tokens_per_s=w.batch * w.L * steps / t_pre, cpu=cpu,
+                prefill_tokens_per_s=w.batch * w.L * steps / t_pre, cpu=_cpu_model(),
                 sample=f"{steps} whole steps (prefill {w.L} + verify {w.K} + commit) of the same shapes, "
                        f"fp64 oracle, {t_pre + t_vc:.1f} s")
 
@@ -701,7 +776,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b_single")
+    ap.add_argument("--workload", default="hybrid_decode")
+    ap.add_argument("--prefill-workload", default="llama8b_long_prefill",
+                    help="with a verify workload: also run this prefill workload and report it in the same "
+                         "line under \"prefill\" ('none' to skip)")
     ap.add_argument("--rotate", type=int, default=0, help="independent cache/input sets (0: enough for >320 MB)")
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk length (0: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -752,6 +830,25 @@ def main():
     if args.graph and step_kind(w) != "verify":
         ap.error("--graph applies to the verify workloads (llama8b_batched, llama8b_batched_greedy, "
                  "llama8b_batched_project, llama8b_batched_tree, hybrid_decode)")
+    out = report(args, w, args.workload)
+    if args.prefill_workload != "none" and step_kind(w) == "verify":
+        # the long prefill of the same line: its own roofline over the whole prefill and its
+        # own CPU baseline
+        wp = synth.WORKLOADS[args.prefill_workload]
+        if step_kind(wp) != "prefill":
+            ap.error("--prefill-workload must name a prefill workload (llama8b_long_prefill)")
+        args.graph = False
+        args.copy_mib = 0
+        p = report(args, wp, args.prefill_workload)
+        out["prefill"] = {k: p[k] for k in ("value", "unit", "ms_per_step", "config", "roofline", "kernels",
+                                             "cpu_baseline") if k in p}
+        out["prefill_tokens_per_s"] = p["value"]
+    print(json.dumps(out))
+
+
+def report(args, w, name):
+    """Run one workload on the GPU and build its JSON report (value, roofline, kernels,
+    CPU baseline)."""
     g = run_gpu(args, w)
     kind = g["kind"]
 
@@ -766,41 +863,57 @@ def main():
 
     K, Bt, L = w.K, w.batch, w.L
     dom = g["dominant"]
-    byt, fl = g["work"][dom]
-    t = g["dom_ms"] * 1e-3
+    if kind == "prefill":
+        # the whole prefill (every launch it makes), as one unit: its bytes and flops over
+        # the time of one prefill measured back to back
+        byt, fl = g["work"]["prefill_all"]
+        t = g["pre_ms"] * 1e-3
+    else:
+        byt, fl = g["work"][dom]
+        t = g["dom_ms"] * 1e-3
     bf16 = w.dtype == "bf16"
-    if dom in ("prefill_out", "prefill_state", "prefill_scan") and bf16 and fl / byt > (BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3):
+    if kind == "prefill" or dom in ("prefill_out", "prefill_state", "prefill_scan"):
+        mfma_bound = bf16 and fl / byt > (BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3)
+    else:
+        mfma_bound = False
+    if mfma_bound:
         roof = dict(bound="mfma", achieved=fl / t / 1e12, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
     else:
         roof = dict(bound="hbm", achieved=byt / t / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
-    roof["kernel"] = dom
-    roof["kernel_ms"] = g["dom_ms"]
-    roof["kernel_ms_traced"] = g["traced_ms"]  # events right around its launches (dispatch latency included)
+    roof["kernel"] = "prefill (all launches)" if kind == "prefill" else dom
+    roof["kernel_ms"] = t * 1e3
+    if kind != "prefill":
+        roof["kernel_ms_traced"] = g["traced_ms"]  # events right around its launches (dispatch latency included)
     roof["flops_per_launch"] = fl
     roof["bytes_per_launch"] = byt
     roof["mfma_frac_bf16"] = fl / t / 1e12 / BF16_PEAK_TFLOPS
     roof["hbm_frac"] = byt / t / 1e9 / HBM_PEAK_GBS
+    fams = [k for k in g["ktime"]] if kind == "prefill" else [dom]
     if os.path.exists(TRAFFIC_FILE):
         try:
             tr = json.load(open(TRAFFIC_FILE))
-            ent = tr.get(f"{dom}/{args.workload}")
-            if ent and ent.get("source_sha") == source_hash(dom):
-                roof["traffic"] = ent["bytes_per_launch"]
+            ents = [tr.get(f"{k}/{name}") for k in fams]
+            if all(e and e.get("source_sha") == source_hash(k) for e, k in zip(ents, fams)):
+                roof["traffic"] = sum(e["bytes_per_launch"] for e in ents)
         except (OSError, ValueError, KeyError):
             pass
     # issued matrix-core work (counters): the hi / lo splits issue about twice the
     # algorithmic flops of the products they feed
     roof["issued_mfma_tflops"] = None
     roof["mfma_busy_frac"] = None
-    if os.path.exists(MFMA_FILE):
+    if os.path.exists(MFMA_FILE) and (kind == "prefill" or dom in PREFILL_KERNELS):
         try:
-            ent = json.load(open(MFMA_FILE)).get(f"{dom}/{args.workload}")
-            if ent and ent.get("source_sha") == source_hash(dom):
-                roof["issued_mfma_tflops"] = ent["issued_bf16_flops"] / t / 1e12
+            mf = json.load(open(MFMA_FILE))
+            ents = [mf.get(f"{k}/{name}") for k in fams]
+            if all(e and e.get("source_sha") == source_hash(k) for e, k in zip(ents, fams)):
+                issued = sum(e["issued_bf16_flops"] for e in ents)
+                roof["issued_mfma_tflops"] = issued / t / 1e12
                 roof["issued_mfma_frac_bf16"] = roof["issued_mfma_tflops"] / BF16_PEAK_TFLOPS
-                roof["mfma_busy_frac"] = ent["mfma_busy_frac"]
+                # busy fraction of the whole prefill: each launch's, weighted by its time
+                kt = [g["ktime"][k] for k in fams]
+                roof["mfma_busy_frac"] = float(sum(e["mfma_busy_frac"] * x for e, x in zip(ents, kt)) / sum(kt))
         except (OSError, ValueError, KeyError):
             pass
     # measured ceilings and the fraction of the attainable roofline: the larger of the
@@ -832,6 +945,8 @@ def main():
         cfg["prefill_len"] = L
     if w.ctx_range:
         cfg["context"] = f"U{{{w.ctx_range[0]}..{w.ctx_range[1]}}} per sequence"
+    elif kind == "verify":
+        cfg["context"] = f"{w.L} tokens per sequence, prefilled on the GPU"
     cfg["launch"] = "HIP graph per round (capture once, replay)" if g["eager_ms"] is not None else "eager"
     out = {
         "metric": "verified tokens/s + HBM GB/s (K-step SSM verify); prefill scan tokens/s",
@@ -866,8 +981,8 @@ def main():
     out.update({"roofline": roof, "kernels": kern, "wall_s_timed": g["wall"], "host_us_per_step": g["host_us"],
                 "device": g["device"],
                 "source_sha": source_hash()})
-    out["cpu_baseline"] = None if args.no_cpu_baseline or kind != "full" else run_cpu_baseline(w)
-    print(json.dumps(out))
+    out["cpu_baseline"] = None if args.no_cpu_baseline else run_cpu_baseline(w, kind)
+    return out
 
 
 if __name__ == "__main__":

@@ -73,6 +73,12 @@ __device__ __forceinline__ void buf_store4(float4 v, __amdgpu_buffer_rsrc_t r, i
     __builtin_amdgcn_raw_buffer_store_b128(t, r, voff, soff, kStreamStorePolicy);
 }
 
+// A workgroup barrier for LDS traffic only: this wave's LDS accesses are complete
+// (lgkmcnt(0)) when it arrives, while its global loads and stores stay in flight.
+// __syncthreads() would also wait for those (vmcnt(0)), which here would hold the state's
+// write-back, or the readout behind the state loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // The single state step that folds one accepted token into a stored state element:
 //   h <- abar * h + B[n] * (dt * x[p]).
 // Every path that writes a state through accepted tokens (verify's fold, commit's
@@ -280,6 +286,8 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     const T *dsrc = K > 0 ? dDt + (size_t)(b * K + max(min(tid, K - 1), 0)) * H + h : pDt + prow;
     const float pdt = ld(pDt, prow);
     const float ddt = ld(dsrc, 0);
+    // draft tid's parent link, read before the state so that staging it waits for nothing else
+    const int par = p.parent ? p.parent[(size_t)b * K + max(min(tid, K - 1), 0)] : tid - 1;
 
     // the state rows: 16-byte buffer loads, one read per element
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.state + (size_t)(b * H + h) * p.head_stride, N * P * 4);
@@ -319,10 +327,10 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     if (tid < K) {
         sDdt[tid] = ddt;
         sDA[tid] = expf(ddt * Ah);
-        sPar[tid] = p.parent ? p.parent[(size_t)b * K + tid] : tid - 1;
+        sPar[tid] = par;
     }
 
-    __syncthreads();
+    lds_barrier();  // the staged rows are visible; the state loads may still be in flight
 
     // ---- per-draft scalars: alpha_k and w_{k,s}, eight lanes per (k, s) pair, over each
     // draft's root path (all of 0..k for a chain) ----
@@ -334,18 +342,32 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
             if ((pm >> i) & 1u) a *= sDA[i];
         sAlpha[tid] = a;
     }
-    for (int base = 0; base < K * K * 8; base += NT) {
+    // LP lanes per (k, s) pair (one pass for K <= 8 in a 512-thread workgroup), each taking
+    // 4 consecutive n of every 4 LP (16-byte LDS reads) into four interleaved partial sums
+    // (short rounding chains), then a butterfly over the LP lanes.  LP depends on N alone,
+    // so a dot product is formed the same way whatever K is (a tree node's output stays
+    // bit-identical to a flat verify of its path).
+    const int LP = N >= 32 ? 8 : N / 4;
+    const int lgLP = __builtin_ctz(LP);
+    for (int base = 0; base < K * K * LP; base += NT) {
         const int i = base + tid;
-        const int pair = i >> 3, part = i & 7;
+        const int pair = i >> lgLP, part = i & (LP - 1);
         const int k = pair / max(K, 1), s = pair - k * K;
         const uint32_t pm = pair < K * K ? path_mask(sPar, k, bad) : 0u;
         const bool live = pair < K * K && s <= k && ((pm >> s) & 1u);
-        float dot = 0.f;
+        float d4[4] = {0.f, 0.f, 0.f, 0.f};
         if (live)
-            for (int n = part; n < N; n += 8) dot = __builtin_fmaf(sDC[k * N + n], sDB[s * N + n], dot);
-        dot += __shfl_xor(dot, 1);
-        dot += __shfl_xor(dot, 2);
-        dot += __shfl_xor(dot, 4);
+            for (int n = 4 * part, c = 0; n < N; n += 4 * LP, ++c) {
+                const float4 cv = *reinterpret_cast<const float4 *>(sDC + k * N + n);
+                const float4 bv = *reinterpret_cast<const float4 *>(sDB + s * N + n);
+                float &a = d4[c & 3];
+                a = __builtin_fmaf(cv.x, bv.x, a);
+                a = __builtin_fmaf(cv.y, bv.y, a);
+                a = __builtin_fmaf(cv.z, bv.z, a);
+                a = __builtin_fmaf(cv.w, bv.w, a);
+            }
+        float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+        for (int d = 1; d < LP; d <<= 1) dot += __shfl_xor(dot, d);
         if (part == 0 && pair < K * K) {
             float w = 0.f;
             if (live) {
@@ -375,16 +397,17 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
             hv[i].w = state_step(a, hv[i].w, bn, u.w);
         }
     }
-    // The rows are written back (once, when m > 0) only after the readout below has
-    // used them: memory operations complete in issue order, and a readout placed after
-    // the stores would wait for them to drain.
-    if (K == 0) {  // fold only: no outputs
-        if (m > 0) {
+    // The folded rows go back at once (when m > 0): nothing after this point waits on
+    // global memory (the barrier below waits for LDS only), so the write-back drains while
+    // the readout runs.  Every load has arrived by now (the rows are in registers; with
+    // m = 0 the readout needs them next); waiting for them here leaves no load that a
+    // later wait, which on this GPU also counts stores, could be for.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), lgkmcnt and expcnt untouched
+    if (m > 0) {
 #pragma unroll
-            for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
-        }
-        return;
+        for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
     }
+    if (K == 0) return;  // fold only: no outputs
 
     // ---- C_k . h0 over this lane's rows, then over the wave's row groups ----
     for (int k = 0; k < K; ++k) {
@@ -406,11 +429,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
         }
         if (rsub == 0) *reinterpret_cast<float4 *>(sRed + (wave * K + k) * Pc + 4 * c4) = acc;
     }
-    if (m > 0) {
-#pragma unroll
-        for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
-    }
-    __syncthreads();
+    lds_barrier();
 
     // ---- outputs: waves summed in order, then the closed-form draft terms ----
     for (int i = tid; i < K * LPR; i += NT) {
