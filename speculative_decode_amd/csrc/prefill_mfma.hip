@@ -381,6 +381,31 @@ __device__ __forceinline__ void load_btile(bf16x8 *bq, const bf16 *sB, int J, in
         bq[kk] = *reinterpret_cast<const bf16x8 *>(sB + (J * kT + l32) * BS + kk * 16 + hf * 8);
 }
 
+// The B operands of Y += M X for one 32-token tile J (see accumulate_mx), read ahead.
+template <int PT>
+__device__ __forceinline__ void load_x(bf16x8 (*xv)[2], const bf16 *xr, int XS) {
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+        const bf16 *row = xr + pt * kT * XS;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(row + ks * 16);
+            const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(row + ks * 16 + 8);
+            xv[pt][ks] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
+    }
+}
+template <int PT>
+__device__ __forceinline__ void mx_products(f32x16 *acc, const bf16x8 *ah, const bf16x8 *al, bf16x8 (*xv)[2]) {
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            acc[pt] = mfma(ah[ks], xv[pt][ks], acc[pt]);
+            acc[pt] = mfma(al[ks], xv[pt][ks], acc[pt]);
+        }
+}
+
 template <int PT>
 __device__ __forceinline__ void accumulate_mx(f32x16 *acc, const bf16x8 *ah, const bf16x8 *al, const bf16 *xr,
                                               int XS) {
@@ -932,26 +957,53 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int v = 0; v < 8; ++v) eye[kk][v] = static_cast<bf16>(16 * kk + 8 * hf + v == l32 ? 1.f : 0.f);
-        const int bpp = (Q / kT) / SP;
-        const int blk1 = min((len + kT - 1) / kT, (jpart + 1) * bpp);
-        for (int blk = jpart * bpp; blk < blk1; ++blk) {
-            const int s0 = blk * kT;
-            f32x16 tb = f32x16{};
+        // every block of the part, unrolled and without a branch; blocks past a short
+        // chunk's end add exact zeros (their B rows, X columns and weights were zeroed when
+        // staged).  Software pipeline: a block's LDS operands are read two blocks ahead and
+        // its identity products issued one block ahead, so that neither the LDS latency
+        // nor the products' latency is waited for where the values are used.
+        constexpr int BPP = (kScanQ / kT) / SP;
+        struct Ops {
+            bf16x8 bo[2];       // B rows of the block (A operand of the identity products)
+            float4 wq[4];       // w_s of the lane's 16 tokens
+            bf16x8 xv[PT][2];   // X operands of the block's products
+        };
+        auto fetch = [&](int b, Ops &o) {
+            const int s0 = (jpart * BPP + b) * kT;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                tb = mfma(*reinterpret_cast<const bf16x8 *>(sB + (s0 + l32) * BS + snt * kT + kk * 16 + 8 * hf), eye[kk],
-                          tb);
+                o.bo[kk] = *reinterpret_cast<const bf16x8 *>(sB + (s0 + l32) * BS + snt * kT + kk * 16 + 8 * hf);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o.wq[q] = *reinterpret_cast<const float4 *>(sWst + s0 + 8 * q + 4 * hf);
+            load_x<PT>(o.xv, sXT + l32 * XS + s0 + 4 * hf, XS);
+        };
+        auto ident = [&](const Ops &o) {
+            f32x16 tb = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) tb = mfma(o.bo[kk], eye[kk], tb);
+            return tb;
+        };
+        Ops o0, o1;
+        fetch(0, o0);
+        if (BPP > 1) fetch(1, o1);
+        f32x16 tb = ident(o0);
+#pragma unroll
+        for (int b = 0; b < BPP; ++b) {
+            const f32x16 tbn = b + 1 < BPP ? ident(o1) : f32x16{};
             f32x16 mv;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 w4 = *reinterpret_cast<const float4 *>(sWst + s0 + 8 * q + 4 * hf);
-                const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+                const float wv[4] = {o0.wq[q].x, o0.wq[q].y, o0.wq[q].z, o0.wq[q].w};
 #pragma unroll
                 for (int u2 = 0; u2 < 4; ++u2) mv[4 * q + u2] = tb[4 * q + u2] * wv[u2];
             }
             bf16x8 ah[2], al[2];
             split16(mv, ah, al);
-            accumulate_mx<PT>(part, ah, al, sXT + l32 * XS + s0 + 4 * hf, XS);
+            mx_products<PT>(part, ah, al, o0.xv);
+            o0 = o1;
+            if (b + 2 < BPP) fetch(b + 2, o1);
+            __builtin_amdgcn_sched_barrier(0);
+            tb = tbn;
         }
     }
     // ---- the chunk's state tiles belong to the four light waves (w < 4: the waves with
@@ -1077,22 +1129,37 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         for (int J = 0; J < I; ++J) {
             const f32x16 z = zn;
             zn = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) zn = mfma(bq[kk], cf[kk], zn);
-            load_btile<NK>(bq, sB, min(J + 2, I), l32, hf, BS);
             const float rowf = sMid[I * 8 + J] * et;
-            f32x16 mv;
+            // tile J's column factors (registers 4q..4q+3 hold s = 32J + 8q + 4hf + (0..3))
+            // and its X operands, read ahead
+            float cv[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                // registers 4q..4q+3 hold s = 32J + 8q + 4hf + (0..3)
                 const float4 cf4 = *reinterpret_cast<const float4 *>(sColf + J * kT + 8 * q + 4 * hf);
-                const float cv[4] = {cf4.x, cf4.y, cf4.z, cf4.w};
-#pragma unroll
-                for (int u2 = 0; u2 < 4; ++u2) mv[4 * q + u2] = z[4 * q + u2] * cv[u2] * rowf;
+                cv[4 * q] = cf4.x, cv[4 * q + 1] = cf4.y, cv[4 * q + 2] = cf4.z, cv[4 * q + 3] = cf4.w;
             }
-            bf16x8 ah[2], al[2];
-            split16(mv, ah, al);
-            accumulate_mx<PT>(acc, ah, al, sXT + l32 * XS + J * kT + 4 * hf, XS);
+            bf16x8 xv[PT][2];
+            load_x<PT>(xv, sXT + l32 * XS + J * kT + 4 * hf, XS);
+            // the matrix cores form tile J + 1's Z one k-step at a time while the vector
+            // units mask and split tile J's values, a few per k-step (the order is pinned,
+            // so neither unit waits for the other's whole tile)
+            i32x4v hw[2], lw[2];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                zn = mfma(bq[kk], cf[kk], zn);
+#pragma unroll
+                for (int v = kk * 16 / NK; v < (kk + 1) * 16 / NK; v += 2) {
+                    uint32_t hh, ll;
+                    split2(z[v] * cv[v] * rowf, z[v + 1] * cv[v + 1] * rowf, hh, ll);
+                    hw[v / 8][(v % 8) / 2] = (int)hh;
+                    lw[v / 8][(v % 8) / 2] = (int)ll;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            load_btile<NK>(bq, sB, min(J + 2, I), l32, hf, BS);
+            const bf16x8 ah[2] = {__builtin_bit_cast(bf16x8, hw[0]), __builtin_bit_cast(bf16x8, hw[1])};
+            const bf16x8 al[2] = {__builtin_bit_cast(bf16x8, lw[0]), __builtin_bit_cast(bf16x8, lw[1])};
+            mx_products<PT>(acc, ah, al, xv);
         }
         {
             const int J = I;
