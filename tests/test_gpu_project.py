@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, dev, dev_layer, y_err
+from gpu_util import BOUND, TOL, dev, dev_layer, y_err
 from speculative_decode_amd import _lib as L
 from speculative_decode_amd import synth
 from speculative_decode_amd.ssm import SSMCache, project, project_workspace_bytes
@@ -126,10 +126,12 @@ def test_project_is_deterministic_and_bias_optional():
 
 
 def test_project_feeds_verify():
-    """Projections straight into verify: the GPU chain (project, verify) against the
-    oracle's chain (project in float64, rounded to bf16 as the device stores it, then
-    verify).  A bf16 rounding taken the other way on a boundary moves y far less than the
-    bf16 tolerance."""
+    """Projections straight into verify: the GPU chain (project, prefill, verify) against
+    the oracle's prefill and verify on exactly the tokens the device projected (the layer's
+    bound), and against the oracle's whole chain (project in float64, rounded to bf16 as
+    the device stores it, then prefill and verify): there a product summed in fp32 may round
+    to the neighbouring bf16 value on a boundary, which moves y by up to ~1e-3 of its scale,
+    so that comparison takes the stated bf16 tolerance."""
     Bt, K, H, P, N, G, d = 4, 4, 32, 128, 128, 8, 1024
     rng = np.random.default_rng(3400)
     layer = synth.draw_layer(rng, H)
@@ -145,9 +147,21 @@ def test_project_feeds_verify():
         return x, B, C, dt
 
     cache = SSMCache(Bt, H, P, N, G, 8, synth.BF16)
-    cache.prefill(*gpu_tokens(ctx, 32), A, D, chunk=64)
-    y = cache.verify(*gpu_tokens(drafts, K), A, D)
+    ctx_dev = gpu_tokens(ctx, 32)
+    drf_dev = gpu_tokens(drafts, K)
+    cache.prefill(*ctx_dev, A, D, chunk=64)
+    y = cache.verify(*drf_dev, A, D)
     torch.cuda.synchronize()
+
+    # the oracle on exactly the tokens the device projected: the layer's own bound
+    def as_f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    _, h_dev = oracle.prefill(*(as_f64(t) for t in ctx_dev), layer.A.f64, layer.D.f64)
+    y_same = oracle.verify(h_dev, *(as_f64(t) for t in drf_dev), layer.A.f64, layer.D.f64)
+    err_same = y_err(y.cpu().numpy(), y_same)
+    print(f"verify on the projected tokens: y err {err_same:.3e}", flush=True)
+    assert err_same <= BOUND[synth.BF16]
 
     def ref_tokens(pr, T):
         x, B, C, dt = reference(pr)
