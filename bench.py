@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
+kRounds = 8  # accepted-length draws a multi-layer step rotates through
 KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept", "project", "prefill_scan"]
 PREFILL_KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "prefill_scan"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -234,7 +235,7 @@ def run_gpu(args, w):
 
     from speculative_decode_amd import _lib as L
     from speculative_decode_amd import synth
-    from speculative_decode_amd.ssm import SSMCache, project, project_workspace_bytes
+    from speculative_decode_amd.ssm import SSMCache, commit_layers, project, project_workspace_bytes
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -298,12 +299,24 @@ def run_gpu(args, w):
         torch.cuda.synchronize()
         for r in range(R):
             caches, drfs, js, jns, yvs, greedy, proj, trees = [], [], [], [], [], [], [], []
+            # a round accepts the same drafts in every layer (the verifier decides from the
+            # last layer's output), so a multi-layer step uses one j for all its layers; the
+            # steps rotate through kRounds such draws (each verify folds the rows the step
+            # before accepted)
+            j_round, j_rounds = None, []
+            if nlayers > 1:
+                j_rounds = [(synth.draw_accept_geometric(rng, Bt, K) if w.accept == "geometric"
+                             else synth.draw_accept_uniform(rng, Bt, K)) for _ in range(kRounds)]
+                j_round = j_rounds[0]
             for li in range(nlayers):
                 c = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
                 c.buffer.copy_(proto.buffer)
                 drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
-                j = (synth.draw_accept_geometric(rng, Bt, K) if w.accept == "geometric"
-                     else synth.draw_accept_uniform(rng, Bt, K))
+                if j_round is not None:
+                    j = j_round
+                else:
+                    j = (synth.draw_accept_geometric(rng, Bt, K) if w.accept == "geometric"
+                         else synth.draw_accept_uniform(rng, Bt, K))
                 if w.tree:
                     # a random tree per sequence and one accepted node; j = its path length
                     par = synth.draw_tree(rng, Bt, K, w.tree)
@@ -331,7 +344,10 @@ def run_gpu(args, w):
                 js.append(torch.from_numpy(j).to(dev))
                 jns.append(j)
                 yvs.append(torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev))
-            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy, proj=proj, tree=trees))
+            if j_rounds:
+                jns = j_rounds  # the draws the steps use
+            sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy, proj=proj, tree=trees,
+                             jr=[torch.from_numpy(jr).to(dev) for jr in j_rounds]))
         del proto
         torch.cuda.synchronize()
     R = len(sets)
@@ -357,6 +373,12 @@ def run_gpu(args, w):
 
     def commit_part(s):
         st = sets[s % R]
+        if nlayers > 1 and not st.get("tree") and not st.get("greedy"):
+            # every layer's commit of the round in one call (one launch per 32 layers)
+            d = st["drf"]
+            jr = st["jr"][(s // R) % len(st["jr"])]
+            commit_layers(st["caches"], jr, [t[0] for t in d], [t[1] for t in d], [t[3] for t in d])
+            return
         for li, c in enumerate(st["caches"]):
             dx, dB, dC, ddt = st["drf"][li]
             if st.get("tree"):
@@ -382,17 +404,28 @@ def run_gpu(args, w):
     def verify_pass():
         """Time per verify launch from launches back to back: the verifies of n whole steps
         (distinct caches: every layer of n rotating sets) between two events, then their
-        commits.  No event sits between the launches, so no dispatch latency is added."""
+        commits.  No event sits between the launches, so no dispatch latency is added.  A
+        multi-layer step rotates through kRounds accepted-length draws: a priming pass
+        commits the last draw, then kRounds timed passes fold each draw once (each commits
+        the next), and their times are averaged."""
         n = max(1, min(args.steps, R))
-        hold(n)
-        e0.record()
-        for s in range(n):
-            verify_part(s, mark=False, project_too=False)
-        e1.record()
-        for s in range(n):
-            commit_part(s)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (n * nlayers)
+        rounds = kRounds if nlayers > 1 else 1
+
+        def one(first):
+            hold(n)
+            e0.record()
+            for s in range(n):
+                verify_part(first + s, mark=False, project_too=False)
+            e1.record()
+            for s in range(n):
+                commit_part(first + s)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        if rounds > 1:
+            one((rounds - 1) * R)  # priming: leaves the last draw pending
+        tot = sum(one(r * R) for r in range(rounds))
+        return tot / (rounds * n * nlayers)
 
     trace_project = [False]  # the projection is traced with events on torch's stream, around the call
 
@@ -557,6 +590,9 @@ def run_gpu(args, w):
         else:
             work["verify"] = verify_work(w, Bt, K, float(jall.mean()), float((jall > 0).mean()))
         work["commit"] = commit_work(w, [float(jall.mean())] * Bt)
+        if nlayers > 1 and not w.tree and w.accept != "greedy":
+            # one commit launch covers every layer of the round
+            work["commit"] = (work["commit"][0] * nlayers, 0)
         if w.accept == "greedy":
             work["accept"] = accept_work(w, Bt, K)
         if w.d_model:
@@ -681,7 +717,8 @@ def run_cpu_baseline(w, kind, budget_s=10.0, max_steps=200):
 KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
     "prefill_state": "chunk_state_", "prefill_pass": "state_pass", "prefill_out": "chunk_out_",
     "prefill_scan": "chunk_scan_",
-    "verify": "ssm_verify_kernel", "commit": ("_commit_kernel", "_commit_tree_kernel"), "accept": "greedy_argmax",
+    "verify": "ssm_verify_kernel", "commit": ("_commit_kernel", "_commit_tree_kernel", "_commit_layers_kernel"),
+    "accept": "greedy_argmax",
     "project": "project_",
     "copy": "MulFunctor",  # the calibration copy: torch.mul(src, 1.0, out=dst)
 }

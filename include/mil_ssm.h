@@ -193,6 +193,29 @@ int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted,
                    const float *A, const float *D, uint32_t flags, mil_stream_t stream);
 
 /*
+ * The commit of one decoding round for several layers at once.  In a round every layer
+ * verifies the same K drafts and the verifier decides from the last layer's output how
+ * many are accepted, so each layer's cache takes the same accepted lengths (QbitAI
+ * article, speculative-decoding walkthrough: the Mamba layers keep the accepted tokens
+ * and go back to the last accepted one).  Equivalent to mil_ssm_commit(caches[l], K,
+ * accepted, x[l], B[l], dt[l], NULL, NULL, 0, stream) for l = 0 .. n-1 (deferred fold, the
+ * same copies and bookkeeping, bit for bit), issued as one launch per
+ * MIL_COMMIT_LAYERS_MAX layers.
+ * caches: host array of n descriptors (1 <= n); x, B, dt: host arrays of n device pointers,
+ * layer l's draft buffers as given to its verify; accepted: device int32 [batch], 0..K.
+ * Every cache must have the same batch, heads, head dim, state size, groups, dtype and
+ * k_max, be VERIFIED with this K, and appear once.  Nothing is launched and no cache
+ * changes phase when any check fails: MIL_E_INVALID (null pointers, n < 1, a repeated
+ * cache, shapes, dtypes or K that differ), MIL_E_ORDER (a cache not VERIFIED), MIL_E_ALIGN.
+ * An accepted[b] outside 0..K sets err[b] = MIL_DEVERR_ACCEPT in every cache and leaves
+ * slot b's logical state and pos unchanged, as mil_ssm_commit does.
+ */
+#define MIL_COMMIT_LAYERS_MAX 32
+int mil_ssm_commit_layers(mil_ssm_cache *const *caches, int32_t n, int32_t K, const int32_t *accepted,
+                          const void *const *x, const void *const *B, const void *const *dt,
+                          mil_stream_t stream);
+
+/*
  * Greedy acceptance on the device, fused into the commit.
  * QbitAI article "Llama 3+Mamba 强强联手", speculative-decoding walkthrough: the verifier
  * checks the K drafted tokens in order, the accepted ones are kept and the sequence is

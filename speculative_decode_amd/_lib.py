@@ -29,7 +29,9 @@ EXPORTS = [
     "mil_ssm_commit", "mil_ssm_cache_status", "mil_ssm_cache_phase", "mil_ssm_cache_trace",
     "mil_ssm_greedy_workspace_bytes", "mil_ssm_commit_greedy", "mil_ssm_project_workspace_bytes", "mil_ssm_project",
     "mil_ssm_verify_tree", "mil_ssm_commit_tree", "mil_ssm_prefill_kernels", "mil_ssm_commit_greedy_noalloc",
+    "mil_ssm_commit_layers",
 ]
+MIL_COMMIT_LAYERS_MAX = 32
 MIL_GREEDY_NOALLOC_MAX_ROWS = 512
 TRACE = {"off": 0, "verify": 1, "fold": 2, "commit": 3, "prefill_state": 4, "prefill_pass": 5, "prefill_out": 6,
          "accept": 7, "prefill_scan": 8}
@@ -94,6 +96,8 @@ def lib():
         "mil_ssm_verify_tree": ([cache_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "mil_ssm_prefill_kernels": ([cache_p, i32, i32, i32], ctypes.c_int),
         "mil_ssm_commit_tree": ([cache_p, i32, vp, vp, vp, vp, vp, vp, vp, u32, vp], ctypes.c_int),
+        "mil_ssm_commit_layers": ([ctypes.POINTER(cache_p), i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                   ctypes.POINTER(vp), vp], ctypes.c_int),
         "mil_ssm_project": ([dims_p, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
                             ctypes.c_int),
     }

@@ -2,6 +2,8 @@
 // kernel launchers.  Every check runs before any work is enqueued.
 #include <string.h>
 
+#include <vector>
+
 #include "ssm_internal.h"
 
 using namespace mil;
@@ -233,6 +235,42 @@ int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, con
     if (e != hipSuccess) return MIL_E_HIP;
     c->phase = kReady;
     c->verified_k = 0;
+    return MIL_OK;
+}
+
+int mil_ssm_commit_layers(mil_ssm_cache *const *caches, int32_t n, int32_t K, const int32_t *accepted,
+                          const void *const *x, const void *const *B, const void *const *dt,
+                          mil_stream_t stream) {
+    if (!caches || n < 1 || !accepted || !x || !B || !dt) return MIL_E_INVALID;
+    std::vector<CacheImpl *> cs((size_t)n);
+    for (int l = 0; l < n; ++l) {
+        cs[l] = impl(caches[l]);
+        if (!cs[l] || !x[l] || !B[l] || !dt[l]) return MIL_E_INVALID;
+        for (int q = 0; q < l; ++q)
+            if (cs[q] == cs[l]) return MIL_E_INVALID;  // each cache once
+    }
+    const CacheImpl &c0 = *cs[0];
+    for (int l = 0; l < n; ++l) {
+        const CacheImpl &c = *cs[l];
+        if (c.dims.batch != c0.dims.batch || c.dims.nheads != c0.dims.nheads || c.dims.headdim != c0.dims.headdim ||
+            c.dims.dstate != c0.dims.dstate || c.dims.ngroups != c0.dims.ngroups || c.dtype != c0.dtype ||
+            c.k_max != c0.k_max)
+            return MIL_E_INVALID;
+    }
+    for (int l = 0; l < n; ++l)
+        if (cs[l]->phase != kVerified) return MIL_E_ORDER;
+    for (int l = 0; l < n; ++l)
+        if (K != cs[l]->verified_k) return MIL_E_INVALID;
+    const int eb = elt_bytes(c0.dtype);
+    if (!aligned(accepted, 4)) return MIL_E_ALIGN;
+    for (int l = 0; l < n; ++l)
+        if (!aligned(x[l], 4) || !aligned(B[l], 4) || !aligned(dt[l], eb)) return MIL_E_ALIGN;
+    const hipError_t e = launch_commit_layers(cs.data(), n, K, accepted, x, B, dt, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return MIL_E_HIP;
+    for (int l = 0; l < n; ++l) {
+        cs[l]->phase = kReady;
+        cs[l]->verified_k = 0;
+    }
     return MIL_OK;
 }
 

@@ -51,9 +51,9 @@ template <typename V> struct RegVec { typedef V type; };
 template <> struct RegVec<uint4> { typedef i32x4v type; };
 
 template <typename VM>
-__global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
+__device__ __forceinline__ void commit_rows(const CommitParams &p, const int k, const int b) {
     typedef typename RegVec<VM>::type V;
-    const int k = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, nt = blockDim.x;
+    const int tid = threadIdx.x, nt = blockDim.x;
     const size_t src = (size_t)b * p.K + k, dst = (size_t)b * p.k_max + k;
     const V *xs = reinterpret_cast<const V *>(p.x + src * p.x_row);
     const V *bs = reinterpret_cast<const V *>(p.B + src * p.B_row);
@@ -92,6 +92,41 @@ __global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
     // dt rows (H elements) need not be a whole number of vectors
     if (tid < nd) dd[tid] = vd;
     for (int e = tid + nt; e < nd; e += nt) dd[e] = ds[e];
+}
+
+template <typename VM>
+__global__ __launch_bounds__(256) void ssm_commit_kernel(const CommitParams p) {
+    commit_rows<VM>(p, blockIdx.x, blockIdx.y);
+}
+
+// The commit of several layers' caches in one launch, grid (K, batch, layers): layer z's
+// workgroups do exactly what ssm_commit_kernel's do for its cache.  The per-layer pointers
+// travel in the kernel arguments (MIL_COMMIT_LAYERS_MAX layers, under 2.5 KB).
+struct LayerPtrs {
+    const char *x, *B, *dt;
+    char *px, *pB, *pdt;
+    int32_t *pos, *pending, *err;
+};
+struct LayersCommitParams {
+    CommitParams shared;  // accepted, row sizes, K, k_max (the pointers are per layer)
+    LayerPtrs layer[MIL_COMMIT_LAYERS_MAX];
+};
+static_assert(sizeof(LayersCommitParams) <= 4096, "kernel arguments are limited to 4 KB");
+
+template <typename VM>
+__global__ __launch_bounds__(256) void ssm_commit_layers_kernel(const LayersCommitParams lp) {
+    const LayerPtrs &l = lp.layer[blockIdx.z];
+    CommitParams p = lp.shared;
+    p.x = l.x;
+    p.B = l.B;
+    p.dt = l.dt;
+    p.px = l.px;
+    p.pB = l.pB;
+    p.pdt = l.pdt;
+    p.pos = l.pos;
+    p.pending = l.pending;
+    p.err = l.err;
+    commit_rows<VM>(p, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ tree drafts
@@ -365,6 +400,33 @@ hipError_t launch_commit_tree(const CacheImpl &c, int K, const int32_t *parent, 
         hipLaunchKernelGGL(ssm_commit_tree_kernel<uint32_t>, dim3(K, c.dims.batch), dim3(256), 0, s, tp);
     trace_end(c, MIL_TRACE_COMMIT, s);
     return hipGetLastError();
+}
+
+hipError_t launch_commit_layers(const CacheImpl *const *cs, int n, int K, const int32_t *accepted,
+                                const void *const *x, const void *const *B, const void *const *dt, hipStream_t s) {
+    bool v16 = true;
+    for (int l = 0; l < n; ++l)
+        v16 = v16 && ((reinterpret_cast<uintptr_t>(x[l]) | reinterpret_cast<uintptr_t>(B[l])) & 15) == 0;
+    for (int l0 = 0; l0 < n; l0 += MIL_COMMIT_LAYERS_MAX) {
+        const int nl = std::min(n - l0, MIL_COMMIT_LAYERS_MAX);
+        LayersCommitParams lp;
+        lp.shared = commit_params(*cs[l0], K, accepted, nullptr, nullptr, nullptr);
+        for (int l = 0; l < MIL_COMMIT_LAYERS_MAX; ++l) {
+            const int li = l0 + std::min(l, nl - 1);  // unused entries repeat the last layer
+            const CommitParams q = commit_params(*cs[li], K, accepted, x[li], B[li], dt[li]);
+            lp.layer[l] = LayerPtrs{q.x, q.B, q.dt, q.px, q.pB, q.pdt, q.pos, q.pending, q.err};
+        }
+        const CacheImpl &c0 = *cs[l0];
+        trace_begin(c0, MIL_TRACE_COMMIT, s);
+        if (v16)
+            hipLaunchKernelGGL(ssm_commit_layers_kernel<uint4>, dim3(K, c0.dims.batch, nl), dim3(256), 0, s, lp);
+        else
+            hipLaunchKernelGGL(ssm_commit_layers_kernel<uint32_t>, dim3(K, c0.dims.batch, nl), dim3(256), 0, s, lp);
+        trace_end(c0, MIL_TRACE_COMMIT, s);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, const void *x,

@@ -74,6 +74,8 @@ bool verify_supported(int batch, int H, int P, int N, int K, int kmax);
 
 // Check accepted[b] in 0..K, copy the accepted draft rows into the pending area,
 // set pending[b] = accepted[b], pos[b] += accepted[b]; a bad value sets err[b] and pending[b] = 0.
+hipError_t launch_commit_layers(const CacheImpl *const *cs, int n, int K, const int32_t *accepted,
+                                const void *const *x, const void *const *B, const void *const *dt, hipStream_t s);
 hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, const void *x,
                          const void *B, const void *dt, hipStream_t s);
 

@@ -284,6 +284,29 @@ class SSMCache:
         return accepted, tokens
 
 
+def commit_layers(caches, accepted, xs, Bs, dts):
+    """One round's commit for several layers' caches at once: caches[l] keeps the first
+    accepted[b] drafts of slot b from xs[l], Bs[l], dts[l] (the draft buffers given to its
+    verify).  The same as caches[l].commit(accepted, xs[l], Bs[l], dts[l]) for every l, in
+    one launch per MIL_COMMIT_LAYERS_MAX layers."""
+    n = len(caches)
+    if n < 1 or not (len(xs) == len(Bs) == len(dts) == n):
+        raise ValueError("commit_layers: one x, B and dt per cache")
+    c0 = caches[0]
+    K = xs[0].shape[1]
+    for c, x, B, dt in zip(caches, xs, Bs, dts):
+        c._check_tokens("commit_layers", x, B, dt)
+        c._check_shapes("commit_layers", c.batch, K, x, B, None, dt, None, None, None)
+    if accepted.dtype != torch.int32 or accepted.device != c0.device:
+        raise TypeError("accepted must be an int32 tensor on the caches' device")
+    if tuple(accepted.shape) != (c0.batch,) or not accepted.is_contiguous():
+        raise ValueError(f"commit_layers: accepted must have shape ({c0.batch},)")
+    descs = (ctypes.POINTER(L.CacheDesc) * n)(*[ctypes.pointer(c.desc) for c in caches])
+    arr = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])  # noqa: E731
+    st = L.lib().mil_ssm_commit_layers(descs, n, K, _ptr(accepted), arr(xs), arr(Bs), arr(dts), _stream(c0.device))
+    L.check(st, "mil_ssm_commit_layers")
+
+
 def project_workspace_bytes(H, P, N, G, T, d_model) -> int:
     d = L.Dims(1, H, P, N, G)
     return int(L.lib().mil_ssm_project_workspace_bytes(ctypes.byref(d), T, d_model))

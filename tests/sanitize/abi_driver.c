@@ -84,6 +84,21 @@ int main(void)
     EXPECT(mil_ssm_commit_greedy(&c, 4, acc, p, 100, MIL_BF16, (int32_t *)f, NULL, p, p, p, f, f, ws, 4096, 0,
                                  NULL),
            MIL_E_ORDER);
+    /* the multi-layer commit: every check before anything is enqueued */
+    {
+        mil_ssm_cache c2;
+        memset(&c2, 0, sizeof c2);
+        EXPECT(mil_ssm_cache_attach(&c2, &d, 8, MIL_BF16, fake, (size_t)lay.bytes), MIL_OK);
+        mil_ssm_cache *two[2] = {&c, &c2}, *same[2] = {&c, &c};
+        const void *ptrs[2] = {p, p}, *holes[2] = {p, NULL};
+        EXPECT(mil_ssm_commit_layers(NULL, 2, 4, acc, ptrs, ptrs, ptrs, NULL), MIL_E_INVALID);
+        EXPECT(mil_ssm_commit_layers(two, 0, 4, acc, ptrs, ptrs, ptrs, NULL), MIL_E_INVALID);
+        EXPECT(mil_ssm_commit_layers(two, 2, 4, NULL, ptrs, ptrs, ptrs, NULL), MIL_E_INVALID);
+        EXPECT(mil_ssm_commit_layers(two, 2, 4, acc, holes, ptrs, ptrs, NULL), MIL_E_INVALID);
+        EXPECT(mil_ssm_commit_layers(same, 2, 4, acc, ptrs, ptrs, ptrs, NULL), MIL_E_INVALID);
+        EXPECT(mil_ssm_commit_layers(two, 2, 4, acc, ptrs, ptrs, ptrs, NULL), MIL_E_ORDER);
+        EXPECT(mil_ssm_cache_phase(&c2), 1);
+    }
     /* project: shapes and pointers */
     EXPECT(mil_ssm_project(&d, 16, 4000, p, p, p, p, p, NULL, MIL_BF16, f, f, f, f, ws, 1 << 20, NULL),
            MIL_E_UNSUPPORTED);

@@ -280,3 +280,28 @@ def test_tree_call_checks(lib):
     assert verify(parent=P(FAKE + 2)) == L.MIL_E_ALIGN
     assert verify(cache=L.CacheDesc()) == L.MIL_E_INVALID
     assert lib.mil_ssm_cache_phase(ctypes.byref(c)) == L.PHASE_READY
+
+
+def test_commit_layers_checks(lib):
+    """Every check of the multi-layer commit that returns before anything is enqueued."""
+    f = lib.mil_ssm_commit_layers
+    a, b = attached(lib), attached(lib)
+    other = attached(lib, d=dims(batch=4))
+
+    def call(cs, n=None, accepted=P(), ptrs=None):
+        n = len(cs) if n is None else n
+        arr = (ctypes.POINTER(L.CacheDesc) * max(len(cs), 1))(*[ctypes.pointer(c) for c in cs])
+        ptrs = ptrs or [P()] * max(len(cs), 1)
+        vp = (ctypes.c_void_p * len(ptrs))(*ptrs)
+        return f(arr, n, 4, accepted, vp, vp, vp, None)
+
+    assert f(None, 2, 4, P(), None, None, None, None) == L.MIL_E_INVALID
+    assert call([a, b], n=0) == L.MIL_E_INVALID
+    assert call([a, b], accepted=None) == L.MIL_E_INVALID
+    assert call([a, b], ptrs=[P(), None]) == L.MIL_E_INVALID  # a null draft pointer
+    assert call([a, a]) == L.MIL_E_INVALID                    # a cache twice
+    assert call([a, other]) == L.MIL_E_INVALID                # shapes differ
+    assert call([a, L.CacheDesc()]) == L.MIL_E_INVALID        # not a cache
+    assert call([a, b]) == L.MIL_E_ORDER                      # no verify before it
+    for c in (a, b, other):
+        assert lib.mil_ssm_cache_phase(ctypes.byref(c)) == L.PHASE_READY
