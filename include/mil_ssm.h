@@ -20,7 +20,9 @@
  *
  * Conventions for every function below:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates no device memory and keeps no global state.
+ *     allocates no device memory.  Its only global state is the static scratch of
+ *     mil_ssm_commit_greedy_noalloc (one array per GPU) and per-device values it
+ *     looks up once (that array's address, the compute-unit count).
  *   - Token tensors are row-major with the last dimension contiguous:
  *       x  [seq][T][H][P],  B, C [seq][T][G][N],  dt [seq][T][H]   (dtype of the cache)
  *       A, D [H] fp32,  y [seq][T][H][P] fp32.
@@ -33,6 +35,12 @@
  *     MIL_E_HIP.  No function throws or aborts.
  *   - Calls on one cache must be issued from one host thread in order; calls on
  *     different caches are independent and reentrant.
+ *   - Debugging: with MIL_SSM_DEBUG set in the environment (any value but "0"),
+ *     every call that fails prints its name and status on stderr, and every call
+ *     that enqueues work then synchronizes its stream, returns MIL_E_HIP if that
+ *     work failed, and prints each slot whose device error word is set in the
+ *     caches it used (its own status is unchanged).  For debugging only: the
+ *     synchronization serializes the host with the GPU.
  */
 #ifndef MIL_SSM_H
 #define MIL_SSM_H

@@ -1,5 +1,7 @@
 // C ABI entry points: argument and protocol checks, cache carving, dispatch to the
 // kernel launchers.  Every check runs before any work is enqueued.
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -43,6 +45,20 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MIL_OK : MIL_E_HIP; }
 
+// MIL_SSM_DEBUG=1 (any value but "0"): verbose host checks.  A call that fails prints its
+// name and status on stderr; a call that enqueued work then synchronizes its stream,
+// reports a failed launch as MIL_E_HIP, and prints every slot whose device error word is
+// set in the caches it used (the status returned stays the call's own).
+bool debug_on() {
+    static const bool on = [] {
+        const char *e = getenv("MIL_SSM_DEBUG");
+        return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+int debug_after(const char *fn, int st, bool enqueued, mil_stream_t stream, mil_ssm_cache *const *caches, int n);
+
 }  // namespace
 
 extern "C" {
@@ -60,7 +76,7 @@ const char *mil_status_string(int status) {
     }
 }
 
-int mil_ssm_supported(const mil_ssm_dims *dims, int32_t dtype) {
+static int mil_ssm_supported_impl(const mil_ssm_dims *dims, int32_t dtype) {
     int st = check_dims(dims);
     if (st != MIL_OK) return st;
     st = check_dtype(dtype);
@@ -70,7 +86,12 @@ int mil_ssm_supported(const mil_ssm_dims *dims, int32_t dtype) {
     return MIL_OK;
 }
 
-int mil_ssm_cache_layout(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mil_ssm_layout *out) {
+int mil_ssm_supported(const mil_ssm_dims *dims, int32_t dtype) {
+    const int st = mil_ssm_supported_impl(dims, dtype);
+    return debug_after("mil_ssm_supported", st, false, nullptr, nullptr, 0);
+}
+
+static int mil_ssm_cache_layout_impl(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mil_ssm_layout *out) {
     int st = check_dims(d);
     if (st != MIL_OK) return st;
     if ((st = check_dtype(dtype)) != MIL_OK) return st;
@@ -99,6 +120,11 @@ int mil_ssm_cache_layout(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mi
     L.bytes = round_up(off, kAlign);
     *out = L;
     return MIL_OK;
+}
+
+int mil_ssm_cache_layout(const mil_ssm_dims *d, int32_t k_max, int32_t dtype, mil_ssm_layout *out) {
+    const int st = mil_ssm_cache_layout_impl(d, k_max, dtype, out);
+    return debug_after("mil_ssm_cache_layout", st, false, nullptr, nullptr, 0);
 }
 
 size_t mil_ssm_cache_bytes(const mil_ssm_dims *d, int32_t k_max, int32_t dtype) {
@@ -131,7 +157,7 @@ int describe(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t
 }
 }  // namespace
 
-int mil_ssm_cache_attach(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
+static int mil_ssm_cache_attach_impl(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
                          void *dev_buf, size_t bytes) {
     const int st = describe(cache, d, k_max, dtype, dev_buf, bytes);
     if (st != MIL_OK) return st;
@@ -141,7 +167,13 @@ int mil_ssm_cache_attach(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_
     return MIL_OK;
 }
 
-int mil_ssm_cache_init(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
+int mil_ssm_cache_attach(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
+                         void *dev_buf, size_t bytes) {
+    const int st = mil_ssm_cache_attach_impl(cache, d, k_max, dtype, dev_buf, bytes);
+    return debug_after("mil_ssm_cache_attach", st, false, nullptr, nullptr, 0);
+}
+
+static int mil_ssm_cache_init_impl(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
                        void *dev_buf, size_t bytes, mil_stream_t stream) {
     const int st = describe(cache, d, k_max, dtype, dev_buf, bytes);
     if (st != MIL_OK) return st;
@@ -158,13 +190,19 @@ int mil_ssm_cache_init(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_ma
     return MIL_OK;
 }
 
+int mil_ssm_cache_init(mil_ssm_cache *cache, const mil_ssm_dims *d, int32_t k_max, int32_t dtype,
+                       void *dev_buf, size_t bytes, mil_stream_t stream) {
+    const int st = mil_ssm_cache_init_impl(cache, d, k_max, dtype, dev_buf, bytes, stream);
+    return debug_after("mil_ssm_cache_init", st, true, stream, &cache, 1);
+}
+
 size_t mil_ssm_prefill_workspace_bytes(const mil_ssm_dims *d, int32_t nseq, int32_t L, int32_t chunk) {
     if (check_dims(d) != MIL_OK || nseq < 1 || L < 1) return 0;
     if (chunk != 64 && chunk != 128 && chunk != 256) return 0;
     return (size_t)prefill_workspace_bytes(*d, nseq, L, chunk);
 }
 
-int mil_ssm_prefill(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L, int32_t chunk,
+static int mil_ssm_prefill_impl(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L, int32_t chunk,
                     const void *x, const void *B, const void *C, const void *dt, const float *A,
                     const float *D, float *y, void *ws, size_t ws_bytes, uint32_t flags,
                     mil_stream_t stream) {
@@ -193,7 +231,15 @@ int mil_ssm_prefill(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L
     return hip_status(e);
 }
 
-int mil_ssm_verify(mil_ssm_cache *cache, int32_t K, const void *x, const void *B, const void *C,
+int mil_ssm_prefill(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L, int32_t chunk,
+                    const void *x, const void *B, const void *C, const void *dt, const float *A,
+                    const float *D, float *y, void *ws, size_t ws_bytes, uint32_t flags,
+                    mil_stream_t stream) {
+    const int st = mil_ssm_prefill_impl(cache, slot0, nseq, L, chunk, x, B, C, dt, A, D, y, ws, ws_bytes, flags, stream);
+    return debug_after("mil_ssm_prefill", st, true, stream, &cache, 1);
+}
+
+static int mil_ssm_verify_impl(mil_ssm_cache *cache, int32_t K, const void *x, const void *B, const void *C,
                    const void *dt, const float *A, const float *D, float *y, mil_stream_t stream) {
     CacheImpl *c = impl(cache);
     if (!c) return MIL_E_INVALID;
@@ -211,7 +257,13 @@ int mil_ssm_verify(mil_ssm_cache *cache, int32_t K, const void *x, const void *B
     return MIL_OK;
 }
 
-int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, const void *x,
+int mil_ssm_verify(mil_ssm_cache *cache, int32_t K, const void *x, const void *B, const void *C,
+                   const void *dt, const float *A, const float *D, float *y, mil_stream_t stream) {
+    const int st = mil_ssm_verify_impl(cache, K, x, B, C, dt, A, D, y, stream);
+    return debug_after("mil_ssm_verify", st, true, stream, &cache, 1);
+}
+
+static int mil_ssm_commit_impl(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, const void *x,
                    const void *B, const void *dt, const float *A, const float *D, uint32_t flags,
                    mil_stream_t stream) {
     CacheImpl *c = impl(cache);
@@ -238,7 +290,14 @@ int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, con
     return MIL_OK;
 }
 
-int mil_ssm_commit_layers(mil_ssm_cache *const *caches, int32_t n, int32_t K, const int32_t *accepted,
+int mil_ssm_commit(mil_ssm_cache *cache, int32_t K, const int32_t *accepted, const void *x,
+                   const void *B, const void *dt, const float *A, const float *D, uint32_t flags,
+                   mil_stream_t stream) {
+    const int st = mil_ssm_commit_impl(cache, K, accepted, x, B, dt, A, D, flags, stream);
+    return debug_after("mil_ssm_commit", st, true, stream, &cache, 1);
+}
+
+static int mil_ssm_commit_layers_impl(mil_ssm_cache *const *caches, int32_t n, int32_t K, const int32_t *accepted,
                           const void *const *x, const void *const *B, const void *const *dt,
                           mil_stream_t stream) {
     if (!caches || n < 1 || !accepted || !x || !B || !dt) return MIL_E_INVALID;
@@ -274,7 +333,14 @@ int mil_ssm_commit_layers(mil_ssm_cache *const *caches, int32_t n, int32_t K, co
     return MIL_OK;
 }
 
-int mil_ssm_verify_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const void *x, const void *B,
+int mil_ssm_commit_layers(mil_ssm_cache *const *caches, int32_t n, int32_t K, const int32_t *accepted,
+                          const void *const *x, const void *const *B, const void *const *dt,
+                          mil_stream_t stream) {
+    const int st = mil_ssm_commit_layers_impl(caches, n, K, accepted, x, B, dt, stream);
+    return debug_after("mil_ssm_commit_layers", st, true, stream, caches, n);
+}
+
+static int mil_ssm_verify_tree_impl(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const void *x, const void *B,
                         const void *C, const void *dt, const float *A, const float *D, float *y,
                         mil_stream_t stream) {
     CacheImpl *c = impl(cache);
@@ -293,7 +359,14 @@ int mil_ssm_verify_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, 
     return MIL_OK;
 }
 
-int mil_ssm_commit_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const int32_t *accepted_node,
+int mil_ssm_verify_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const void *x, const void *B,
+                        const void *C, const void *dt, const float *A, const float *D, float *y,
+                        mil_stream_t stream) {
+    const int st = mil_ssm_verify_tree_impl(cache, K, parent, x, B, C, dt, A, D, y, stream);
+    return debug_after("mil_ssm_verify_tree", st, true, stream, &cache, 1);
+}
+
+static int mil_ssm_commit_tree_impl(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const int32_t *accepted_node,
                         const void *x, const void *B, const void *dt, const float *A, const float *D,
                         uint32_t flags, mil_stream_t stream) {
     CacheImpl *c = impl(cache);
@@ -317,6 +390,13 @@ int mil_ssm_commit_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, 
     c->phase = kReady;
     c->verified_k = 0;
     return MIL_OK;
+}
+
+int mil_ssm_commit_tree(mil_ssm_cache *cache, int32_t K, const int32_t *parent, const int32_t *accepted_node,
+                        const void *x, const void *B, const void *dt, const float *A, const float *D,
+                        uint32_t flags, mil_stream_t stream) {
+    const int st = mil_ssm_commit_tree_impl(cache, K, parent, accepted_node, x, B, dt, A, D, flags, stream);
+    return debug_after("mil_ssm_commit_tree", st, true, stream, &cache, 1);
 }
 
 size_t mil_ssm_greedy_workspace_bytes(const mil_ssm_dims *d, int32_t K, int32_t vocab) {
@@ -370,7 +450,7 @@ int commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, 
 
 extern "C" {
 
-int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
+static int mil_ssm_commit_greedy_impl(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
                           int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
                           const void *x, const void *B, const void *dt, const float *A, const float *D, void *ws,
                           size_t ws_bytes, uint32_t flags, mil_stream_t stream) {
@@ -378,7 +458,15 @@ int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_
                          D, ws, ws_bytes, flags, stream, false);
 }
 
-int mil_ssm_commit_greedy_noalloc(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
+int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
+                          int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
+                          const void *x, const void *B, const void *dt, const float *A, const float *D, void *ws,
+                          size_t ws_bytes, uint32_t flags, mil_stream_t stream) {
+    const int st = mil_ssm_commit_greedy_impl(cache, K, draft_tokens, logits, vocab, logits_dtype, accepted, verifier_tokens, x, B, dt, A, D, ws, ws_bytes, flags, stream);
+    return debug_after("mil_ssm_commit_greedy", st, true, stream, &cache, 1);
+}
+
+static int mil_ssm_commit_greedy_noalloc_impl(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
                                   int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
                                   const void *x, const void *B, const void *dt, const float *A, const float *D,
                                   uint32_t flags, mil_stream_t stream) {
@@ -386,12 +474,20 @@ int mil_ssm_commit_greedy_noalloc(mil_ssm_cache *cache, int32_t K, const int32_t
                          D, nullptr, 0, flags, stream, true);
 }
 
+int mil_ssm_commit_greedy_noalloc(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens, const void *logits,
+                                  int32_t vocab, int32_t logits_dtype, int32_t *accepted, int32_t *verifier_tokens,
+                                  const void *x, const void *B, const void *dt, const float *A, const float *D,
+                                  uint32_t flags, mil_stream_t stream) {
+    const int st = mil_ssm_commit_greedy_noalloc_impl(cache, K, draft_tokens, logits, vocab, logits_dtype, accepted, verifier_tokens, x, B, dt, A, D, flags, stream);
+    return debug_after("mil_ssm_commit_greedy_noalloc", st, true, stream, &cache, 1);
+}
+
 size_t mil_ssm_project_workspace_bytes(const mil_ssm_dims *d, int32_t T, int32_t d_model) {
     if (check_dims(d) != MIL_OK || !project_supported(*d, T, d_model)) return 0;
     return (size_t)project_workspace_bytes(*d, T, d_model);
 }
 
-int mil_ssm_project(const mil_ssm_dims *d, int32_t T, int32_t d_model, const void *u, const void *w_x,
+static int mil_ssm_project_impl(const mil_ssm_dims *d, int32_t T, int32_t d_model, const void *u, const void *w_x,
                     const void *w_B, const void *w_C, const void *w_dt, const float *dt_bias, int32_t out_dtype,
                     void *x, void *B, void *C, void *dt, void *ws, size_t ws_bytes, mil_stream_t stream) {
     int st = check_dims(d);
@@ -411,6 +507,13 @@ int mil_ssm_project(const mil_ssm_dims *d, int32_t T, int32_t d_model, const voi
     void *out[4] = {x, B, C, dt};
     return hip_status(launch_project(*d, T, d_model, u, w, dt_bias, out_dtype == MIL_BF16, out, ws,
                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mil_ssm_project(const mil_ssm_dims *d, int32_t T, int32_t d_model, const void *u, const void *w_x,
+                    const void *w_B, const void *w_C, const void *w_dt, const float *dt_bias, int32_t out_dtype,
+                    void *x, void *B, void *C, void *dt, void *ws, size_t ws_bytes, mil_stream_t stream) {
+    const int st = mil_ssm_project_impl(d, T, d_model, u, w_x, w_B, w_C, w_dt, dt_bias, out_dtype, x, B, C, dt, ws, ws_bytes, stream);
+    return debug_after("mil_ssm_project", st, true, stream, nullptr, 0);
 }
 
 int mil_ssm_cache_status(const mil_ssm_cache *cache, int32_t *bad_slot, int32_t clear, mil_stream_t stream) {
@@ -455,7 +558,7 @@ int mil_ssm_cache_phase(const mil_ssm_cache *cache) {
     return c ? c->phase : kUninit;
 }
 
-int mil_ssm_cache_trace(mil_ssm_cache *cache, int32_t kernel, void *ev_start, void *ev_stop) {
+static int mil_ssm_cache_trace_impl(mil_ssm_cache *cache, int32_t kernel, void *ev_start, void *ev_stop) {
     CacheImpl *c = impl(cache);
     if (!c || kernel < MIL_TRACE_OFF || kernel > MIL_TRACE_PREFILL_SCAN) return MIL_E_INVALID;
     if (kernel == MIL_TRACE_OFF || !ev_start || !ev_stop) {
@@ -469,4 +572,42 @@ int mil_ssm_cache_trace(mil_ssm_cache *cache, int32_t kernel, void *ev_start, vo
     return MIL_OK;
 }
 
+int mil_ssm_cache_trace(mil_ssm_cache *cache, int32_t kernel, void *ev_start, void *ev_stop) {
+    const int st = mil_ssm_cache_trace_impl(cache, kernel, ev_start, ev_stop);
+    return debug_after("mil_ssm_cache_trace", st, false, nullptr, nullptr, 0);
+}
+
 }  // extern "C"
+
+namespace {
+int debug_after(const char *fn, int st, bool enqueued, mil_stream_t stream, mil_ssm_cache *const *caches, int n) {
+    if (!debug_on()) return st;
+    if (st != MIL_OK) {
+        fprintf(stderr, "mil_ssm debug: %s returned %d (%s)\n", fn, st, mil_status_string(st));
+        return st;
+    }
+    if (!enqueued) return st;
+    hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) {
+        fprintf(stderr, "mil_ssm debug: %s: the enqueued work failed: %s\n", fn, hipGetErrorString(e));
+        return MIL_E_HIP;
+    }
+    for (int l = 0; l < n; ++l) {
+        const CacheImpl *c = impl(caches[l]);
+        if (!c) continue;
+        std::vector<int32_t> err((size_t)c->dims.batch);
+        e = hipMemcpy(err.data(), cache_err(*c), sizeof(int32_t) * err.size(), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) {
+            fprintf(stderr, "mil_ssm debug: %s: reading the error words failed: %s\n", fn, hipGetErrorString(e));
+            return MIL_E_HIP;
+        }
+        for (size_t b = 0; b < err.size(); ++b)
+            if (err[b] != 0)
+                fprintf(stderr, "mil_ssm debug: %s: cache %d slot %zu error word 0x%x (accept %d, tree %d, scan %d)\n",
+                        fn, l, b, (unsigned)err[b], (err[b] & MIL_DEVERR_ACCEPT) != 0, (err[b] & MIL_DEVERR_TREE) != 0,
+                        (err[b] & MIL_DEVERR_SCAN) != 0);
+    }
+    return st;
+}
+}  // namespace

@@ -305,3 +305,29 @@ def test_commit_layers_checks(lib):
     assert call([a, b]) == L.MIL_E_ORDER                      # no verify before it
     for c in (a, b, other):
         assert lib.mil_ssm_cache_phase(ctypes.byref(c)) == L.PHASE_READY
+
+
+def test_debug_mode_reports_failed_calls():
+    """MIL_SSM_DEBUG=1: a failing call names itself and its status on stderr; unset, the
+    library prints nothing."""
+    import os
+    import subprocess
+    import sys
+    prog = (
+        "import ctypes, sys\n"
+        f"sys.path.insert(0, {os.path.dirname(os.path.dirname(os.path.abspath(__file__)))!r})\n"
+        "from speculative_decode_amd import _lib as L\n"
+        "lib = L.lib()\n"
+        "d = L.Dims(2, 32, 128, 128, 8)\n"
+        "c = L.CacheDesc()\n"
+        "st = lib.mil_ssm_verify(ctypes.byref(c), 4, None, None, None, None, None, None, None, None)\n"
+        "print(st)\n"
+    )
+    for env, expect in (({"MIL_SSM_DEBUG": "1"}, True), ({"MIL_SSM_DEBUG": "0"}, False), ({}, False)):
+        e = {k: v for k, v in os.environ.items() if k != "MIL_SSM_DEBUG"}
+        e.update(env)
+        r = subprocess.run([sys.executable, "-c", prog], capture_output=True, text=True, env=e, timeout=120)
+        assert r.returncode == 0, r.stderr
+        assert r.stdout.strip() == str(L.MIL_E_INVALID)
+        said = "mil_ssm debug: mil_ssm_verify returned" in r.stderr
+        assert said == expect, (env, r.stderr)
