@@ -37,7 +37,8 @@
  *     different caches are independent and reentrant.
  *   - Debugging: with MIL_SSM_DEBUG set in the environment (any value but "0"),
  *     every call that fails prints its name and status on stderr, and every call
- *     that enqueues work then synchronizes its stream, returns MIL_E_HIP if that
+ *     that enqueues work (on a stream not being captured into a graph) then
+ *     synchronizes its stream, returns MIL_E_HIP if that
  *     work failed, and prints each slot whose device error word is set in the
  *     caches it used (its own status is unchanged).  For debugging only: the
  *     synchronization serializes the host with the GPU.

@@ -46,9 +46,10 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int hip_status(hipError_t e) { return e == hipSuccess ? MIL_OK : MIL_E_HIP; }
 
 // MIL_SSM_DEBUG=1 (any value but "0"): verbose host checks.  A call that fails prints its
-// name and status on stderr; a call that enqueued work then synchronizes its stream,
-// reports a failed launch as MIL_E_HIP, and prints every slot whose device error word is
-// set in the caches it used (the status returned stays the call's own).
+// name and status on stderr; a call that enqueued work then synchronizes its stream
+// (unless the stream is being captured into a graph), reports a failed launch as
+// MIL_E_HIP, and prints every slot whose device error word is set in the caches it used
+// (the status returned stays the call's own).
 bool debug_on() {
     static const bool on = [] {
         const char *e = getenv("MIL_SSM_DEBUG");
@@ -587,6 +588,12 @@ int debug_after(const char *fn, int st, bool enqueued, mil_stream_t stream, mil_
         return st;
     }
     if (!enqueued) return st;
+    // a stream being captured into a graph cannot be synchronized (that would end the
+    // capture): the work runs only when the graph is launched, so there is nothing to check
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap) == hipSuccess &&
+        cap != hipStreamCaptureStatusNone)
+        return st;
     hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) {
