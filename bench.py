@@ -243,6 +243,7 @@ def run_gpu(args, w):
     rng = np.random.default_rng(w.seed)
     kind = step_kind(w)
     Bt, K = w.batch, w.K
+    kcap = w.kmax or K  # pending rows each cache holds
     nlayers = w.layers
     layers = [synth.draw_layer(rng, w.H) for _ in range(nlayers)]
     AD = [(to_dev(l.A), to_dev(l.D)) for l in layers]
@@ -265,7 +266,8 @@ def run_gpu(args, w):
                              ws=torch.empty(cache.workspace_bytes(Bt, Lp, w.chunk) + 256, dtype=torch.uint8,
                                             device=dev),
                              y=torch.empty((Bt, Lp, w.H, w.P), dtype=torch.float32, device=dev),
-                             yv=[torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev)]))
+                             yv=[torch.empty((Bt, K, w.H, w.P), dtype=torch.float32, device=dev)],
+                             m=np.zeros((1, Bt), np.int64), base=np.zeros((1, Bt), np.int64)))
     elif kind == "prefill":
         Lp = w.L
         nch = (Lp + w.chunk - 1) // w.chunk
@@ -291,7 +293,7 @@ def run_gpu(args, w):
         if w.d_model:
             state_bytes += project_work(w, Bt * K)[0]  # and so are the projection weights
         R = args.rotate or (1 if nlayers > 1 else max(2, min(64, int(np.ceil(320e6 / state_bytes)))))
-        proto = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
+        proto = SSMCache(Bt, w.H, w.P, w.N, w.G, kcap, w.dtype, device=dev)
         for b in range(Bt):
             pre = synth.draw_tokens(rng, 1, int(ctx[b]), w.H, w.P, w.N, w.G, w.dtype)
             proto.prefill(*[to_dev(t) for t in (pre.x, pre.B, pre.C, pre.dt)], *AD[0], slot0=b,
@@ -309,7 +311,7 @@ def run_gpu(args, w):
                              else synth.draw_accept_uniform(rng, Bt, K)) for _ in range(kRounds)]
                 j_round = j_rounds[0]
             for li in range(nlayers):
-                c = SSMCache(Bt, w.H, w.P, w.N, w.G, K, w.dtype, device=dev)
+                c = SSMCache(Bt, w.H, w.P, w.N, w.G, kcap, w.dtype, device=dev)
                 c.buffer.copy_(proto.buffer)
                 drf = synth.draw_tokens(rng, Bt, K, w.H, w.P, w.N, w.G, w.dtype)
                 if j_round is not None:
@@ -347,14 +349,28 @@ def run_gpu(args, w):
             if j_rounds:
                 jns = j_rounds  # the draws the steps use
             sets.append(dict(caches=caches, drf=drfs, j=js, jn=jns, yv=yvs, greedy=greedy, proj=proj, tree=trees,
-                             jr=[torch.from_numpy(jr).to(dev) for jr in j_rounds]))
+                             jr=[torch.from_numpy(jr).to(dev) for jr in j_rounds], jrn=j_rounds,
+                             # host mirror of every layer's pending counts (the caches start
+                             # with none pending) and of where the next commit appends
+                             m=np.zeros((nlayers, Bt), np.int64), base=np.zeros((nlayers, Bt), np.int64)))
         del proto
         torch.cuda.synchronize()
     R = len(sets)
 
+    # rows folded and state write-backs of the verifies issued while recording (the
+    # library's rule, mirrored on the host: write back when pending + K > k_max)
+    vstats = dict(on=False, rows=0, writes=0, slots=0)
+
     def verify_part(s, mark=True, project_too=True):
         st = sets[s % R]
         for li, c in enumerate(st["caches"]):
+            m = st["m"][li]
+            wb = (m > 0) & (m + K > kcap)
+            st["base"][li] = np.where(wb | (m == 0), 0, m)
+            if vstats["on"]:
+                vstats["rows"] += int(m.sum())
+                vstats["writes"] += int(wb.sum())
+                vstats["slots"] += Bt
             dx, dB, dC, ddt = st["drf"][li]
             if st.get("proj") and project_too:
                 # the drafts' x, B, C, dt projected from the input rows into the same buffers
@@ -376,9 +392,12 @@ def run_gpu(args, w):
         if nlayers > 1 and not st.get("tree") and not st.get("greedy"):
             # every layer's commit of the round in one call (one launch per 32 layers)
             d = st["drf"]
-            jr = st["jr"][(s // R) % len(st["jr"])]
-            commit_layers(st["caches"], jr, [t[0] for t in d], [t[1] for t in d], [t[3] for t in d])
+            r = (s // R) % len(st["jr"])
+            commit_layers(st["caches"], st["jr"][r], [t[0] for t in d], [t[1] for t in d], [t[3] for t in d])
+            st["m"][:] = st["base"] + st["jrn"][r][None, :]
             return
+        for li in range(nlayers):
+            st["m"][li] = st["base"][li] + st["jn"][li]
         for li, c in enumerate(st["caches"]):
             dx, dB, dC, ddt = st["drf"][li]
             if st.get("tree"):
@@ -395,6 +414,8 @@ def run_gpu(args, w):
         if kind in ("full", "prefill"):
             x, B, C, dt = st["pre"]
             st["caches"][0].prefill(x, B, C, dt, *AD[0], y=st["y"], chunk=w.chunk, ws=st["ws"])
+            if "m" in st:
+                st["m"][:] = 0  # a fresh prefill leaves nothing pending
         if kind in ("full", "verify"):
             # every layer's verify, then every layer's commit: the accepted lengths are known
             # only once the last layer has run
@@ -424,7 +445,9 @@ def run_gpu(args, w):
 
         if rounds > 1:
             one((rounds - 1) * R)  # priming: leaves the last draw pending
+        vstats.update(on=True, rows=0, writes=0, slots=0)
         tot = sum(one(r * R) for r in range(rounds))
+        vstats["on"] = False
         return tot / (rounds * n * nlayers)
 
     trace_project = [False]  # the projection is traced with events on torch's stream, around the call
@@ -587,6 +610,10 @@ def run_gpu(args, w):
         jall = np.concatenate([jn for st in sets for jn in st["jn"]])
         if kind == "full":
             work["verify"] = verify_work(w, Bt, K, 0.0, 0.0)
+        elif vstats["slots"]:
+            # the verifies the back-to-back pass timed: rows they folded, states they wrote
+            work["verify"] = verify_work(w, Bt, K, vstats["rows"] / vstats["slots"],
+                                         vstats["writes"] / vstats["slots"])
         else:
             work["verify"] = verify_work(w, Bt, K, float(jall.mean()), float((jall > 0).mean()))
         work["commit"] = commit_work(w, [float(jall.mean())] * Bt)
@@ -819,6 +846,8 @@ def main():
                          "line under \"prefill\" ('none' to skip)")
     ap.add_argument("--rotate", type=int, default=0, help="independent cache/input sets (0: enough for >320 MB)")
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk length (0: the workload's)")
+    ap.add_argument("--kmax", type=int, default=0,
+                    help="verify workloads: pending rows each cache holds (0: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="verify workloads: replay each round as a HIP graph (launches included in the time)")
@@ -860,9 +889,9 @@ def main():
         sys.exit(2)
     from speculative_decode_amd import synth
     w = synth.WORKLOADS[args.workload]
-    if args.chunk:
+    if args.chunk or args.kmax:
         import dataclasses
-        w = dataclasses.replace(w, chunk=args.chunk)
+        w = dataclasses.replace(w, chunk=args.chunk or w.chunk, kmax=args.kmax or w.kmax)
     args.steps = max(1, args.steps)
     if args.graph and step_kind(w) != "verify":
         ap.error("--graph applies to the verify workloads (llama8b_batched, llama8b_batched_greedy, "
@@ -978,6 +1007,8 @@ def report(args, w, name):
                                                         "planted for j ~ U{0..K}",
                                               "tree": f"{w.tree} draft tree (parent ~ U{{-1..k-1}}), accepted node "
                                                       "~ U{-1..K-1}, j = its root path's length"}[w.accept]})
+    if kind != "prefill":
+        cfg["pending_rows"] = w.kmax or K  # the caches' k_max: accepted rows they can hold unfolded
     if kind != "verify":
         cfg["prefill_len"] = L
     if w.ctx_range:

@@ -100,7 +100,15 @@ typedef struct {
  *           buffer itself: graph replays and byte copies of a cache (mil_ssm_cache_attach)
  *           stay correct.  A buffer whose rows hold a flag of a later epoch than their own
  *           is not a cache this library wrote.
- * The logical state of slot b is `state` advanced through its `pending` rows.
+ *   append  int32 [batch]: the pend_* row at which the next commit puts its first accepted
+ *           row: 0 when the verify before it wrote the folded state back, else that
+ *           verify's pending count (written by verify, read by commit).
+ * The logical state of slot b is `state` advanced through its `pending` rows.  A verify
+ * folds all of them (in registers) for its outputs, but writes the folded state back only
+ * when the next commit could overflow the pending area (pending + K > k_max; always with
+ * K = 0); otherwise the accepted rows stay pending and the next commit appends to them.
+ * With k_max = K every verify that has pending rows writes the state back; a larger k_max
+ * trades a few more rows folded per verify for fewer state writes.
  */
 typedef struct {
     int64_t bytes;
@@ -108,6 +116,7 @@ typedef struct {
     int64_t pend_x_off, pend_B_off, pend_dt_off;
     int64_t pos_off, pending_off, err_off;
     int64_t scan_off;
+    int64_t append_off;
 } mil_ssm_layout;
 
 #define MIL_DEVERR_ACCEPT 1

@@ -51,7 +51,7 @@ class Dims(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("bytes", "state_off", "state_head_stride", "pend_x_off",
                                               "pend_B_off", "pend_dt_off", "pos_off", "pending_off",
-                                              "err_off", "scan_off")]
+                                              "err_off", "scan_off", "append_off")]
 
 
 class CacheDesc(ctypes.Structure):

@@ -118,6 +118,8 @@ static int mil_ssm_cache_layout_impl(const mil_ssm_dims *d, int32_t k_max, int32
     off += Bt * 4;
     L.scan_off = off = round_up(off, kAlign);
     off += Bt * H * kScanSlabs * kScanRow * 4;
+    L.append_off = off = round_up(off, kAlign);
+    off += Bt * 4;
     L.bytes = round_up(off, kAlign);
     *out = L;
     return MIL_OK;

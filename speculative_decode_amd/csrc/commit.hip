@@ -25,6 +25,7 @@ struct CommitParams {
     const char *x, *B, *dt;           // drafts [batch][K][row]
     char *px, *pB, *pdt;              // pending rows [batch][k_max][row]
     int32_t *pos, *pending, *err;
+    const int32_t *append;            // [batch] first pending row this commit writes (set by the verify)
     int x_row, B_row, dt_row;         // bytes per token row (H*P, G*N, H elements)
     int K, k_max;
 };
@@ -54,7 +55,10 @@ template <typename VM>
 __device__ __forceinline__ void commit_rows(const CommitParams &p, const int k, const int b) {
     typedef typename RegVec<VM>::type V;
     const int tid = threadIdx.x, nt = blockDim.x;
-    const size_t src = (size_t)b * p.K + k, dst = (size_t)b * p.k_max + k;
+    // 0 when the verify wrote the state back, else its pending count (at most k_max - K by
+    // the verify's rule; clamped so that no value in the buffer can place a row outside it)
+    const int base = min(max(p.append[b], 0), p.k_max - p.K);
+    const size_t src = (size_t)b * p.K + k, dst = (size_t)b * p.k_max + base + k;
     const V *xs = reinterpret_cast<const V *>(p.x + src * p.x_row);
     const V *bs = reinterpret_cast<const V *>(p.B + src * p.B_row);
     const uint16_t *ds = reinterpret_cast<const uint16_t *>(p.dt + src * p.dt_row);
@@ -71,11 +75,11 @@ __device__ __forceinline__ void commit_rows(const CommitParams &p, const int k, 
     const bool ok = j >= 0 && j <= p.K;
     if (k == 0 && tid == 0) {
         if (ok) {
-            p.pending[b] = j;
+            p.pending[b] = base + j;
             p.pos[b] += j;
         } else {
             atomicOr(p.err + b, MIL_DEVERR_ACCEPT);  // keeps bits set by earlier calls
-            p.pending[b] = 0;
+            p.pending[b] = base;  // the rows still pending stay
         }
     }
     if (!ok || k >= j) return;
@@ -106,6 +110,7 @@ struct LayerPtrs {
     const char *x, *B, *dt;
     char *px, *pB, *pdt;
     int32_t *pos, *pending, *err;
+    const int32_t *append;
 };
 struct LayersCommitParams {
     CommitParams shared;  // accepted, row sizes, K, k_max (the pointers are per layer)
@@ -126,6 +131,7 @@ __global__ __launch_bounds__(256) void ssm_commit_layers_kernel(const LayersComm
     p.pos = l.pos;
     p.pending = l.pending;
     p.err = l.err;
+    p.append = l.append;
     commit_rows<VM>(p, blockIdx.x, blockIdx.y);
 }
 
@@ -170,17 +176,20 @@ __global__ __launch_bounds__(256) void ssm_commit_tree_kernel(const TreeCommitPa
     }
     __syncthreads();
     const int j = sj;
+    // 0 when the verify wrote the state back, else its pending count (at most k_max - K by
+    // the verify's rule; clamped so that no value in the buffer can place a row outside it)
+    const int base = min(max(p.append[b], 0), p.k_max - p.K);
     if (k == 0 && threadIdx.x == 0) {
         if (!sbad) {
-            p.pending[b] = j;
+            p.pending[b] = base + j;
             p.pos[b] += j;
         } else {
             atomicOr(p.err + b, sbad);  // keeps bits set by earlier calls
-            p.pending[b] = 0;
+            p.pending[b] = base;        // the rows still pending stay
         }
     }
     if (k >= j) return;
-    const size_t src = (size_t)b * p.K + spath[k], dst = (size_t)b * p.k_max + k;
+    const size_t src = (size_t)b * p.K + spath[k], dst = (size_t)b * p.k_max + base + k;
     copy_row<V>(p.px + dst * p.x_row, p.x + src * p.x_row, p.x_row);
     copy_row<V>(p.pB + dst * p.B_row, p.B + src * p.B_row, p.B_row);
     const char *ds = p.dt + src * p.dt_row;
@@ -329,16 +338,19 @@ __global__ __launch_bounds__(256) void greedy_commit_kernel(const GreedyParams g
     }
     __syncthreads();
     const int j = sj;
+    // 0 when the verify wrote the state back, else its pending count (at most k_max - K by
+    // the verify's rule; clamped so that no value in the buffer can place a row outside it)
+    const int base = min(max(p.append[b], 0), p.k_max - p.K);
     if (k == 0) {
         if (threadIdx.x == 0) {
             g.accepted[b] = j;
-            p.pending[b] = j;
+            p.pending[b] = base + j;
             p.pos[b] += j;
         }
         if (g.tokens && threadIdx.x < K) g.tokens[(int64_t)b * K + threadIdx.x] = stok[threadIdx.x];
     }
     if (k >= j) return;
-    const size_t src = (size_t)b * K + k, dst = (size_t)b * p.k_max + k;
+    const size_t src = (size_t)b * K + k, dst = (size_t)b * p.k_max + base + k;
     copy_row<V>(p.px + dst * p.x_row, p.x + src * p.x_row, p.x_row);
     copy_row<V>(p.pB + dst * p.B_row, p.B + src * p.B_row, p.B_row);
     const char *ds = p.dt + src * p.dt_row;
@@ -376,6 +388,7 @@ CommitParams commit_params(const CacheImpl &c, int K, const int32_t *accepted, c
     p.pdt = static_cast<char *>(cache_pend_dt(c));
     p.pos = cache_pos(c);
     p.pending = cache_pending(c);
+    p.append = cache_append(c);
     p.err = cache_err(c);
     p.x_row = c.dims.nheads * c.dims.headdim * e;   // multiples of 32 bytes (P, N >= 16)
     p.B_row = c.dims.ngroups * c.dims.dstate * e;
@@ -414,7 +427,7 @@ hipError_t launch_commit_layers(const CacheImpl *const *cs, int n, int K, const 
         for (int l = 0; l < MIL_COMMIT_LAYERS_MAX; ++l) {
             const int li = l0 + std::min(l, nl - 1);  // unused entries repeat the last layer
             const CommitParams q = commit_params(*cs[li], K, accepted, x[li], B[li], dt[li]);
-            lp.layer[l] = LayerPtrs{q.x, q.B, q.dt, q.px, q.pB, q.pdt, q.pos, q.pending, q.err};
+            lp.layer[l] = LayerPtrs{q.x, q.B, q.dt, q.px, q.pB, q.pdt, q.pos, q.pending, q.err, q.append};
         }
         const CacheImpl &c0 = *cs[l0];
         trace_begin(c0, MIL_TRACE_COMMIT, s);

@@ -55,6 +55,7 @@ constexpr int kScanChunks = 64;  // chunks per launch of the single-launch prefi
 constexpr int kScanRow = kScanChunks + 4;  // words per (slot, head, slab) row: flags, epoch, pad
 constexpr int kScanEpoch = kScanChunks;    // index of the epoch word in a row
 inline int32_t *cache_scan(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.scan_off); }
+inline int32_t *cache_append(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.append_off); }
 inline int elt_bytes(int32_t dtype) { return dtype == MIL_BF16 ? 2 : 4; }
 
 // ---- launchers (each returns the launch's hipError_t) ----

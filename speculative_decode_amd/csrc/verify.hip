@@ -17,6 +17,7 @@ hipError_t launch_verify(const CacheImpl &c, int K, const void *x, const void *B
     vp.pend_B = cache_pend_B(c);
     vp.pend_dt = cache_pend_dt(c);
     vp.pending = cache_pending(c);
+    vp.append = cache_append(c);
     vp.x = x;
     vp.B = B;
     vp.C = C;

@@ -92,6 +92,7 @@ struct VerifyParams {
     int64_t head_stride;  // floats between consecutive (slot, head) blocks
     const void *pend_x, *pend_B, *pend_dt;
     const int32_t *pending;
+    int32_t *append;  // [batch] where the next commit appends: 0 after a write-back, else pending
     const void *x, *B, *C, *dt;
     const float *A, *D;
     float *y;
@@ -227,7 +228,9 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     const int h = blockIdx.x / p.cs, b = blockIdx.y;
     const int col0 = (blockIdx.x - h * p.cs) * Pc;
     const int g = h / (H / G);
-    const int m = __builtin_amdgcn_readfirstlane(p.pending[b]);  // uniform: branches on m stay scalar
+    // uniform, so branches on m stay scalar; clamped to the pending area, so that no value in
+    // the buffer can make the staging read or write outside it
+    const int m = min(max(__builtin_amdgcn_readfirstlane(p.pending[b]), 0), kmax);
     const float Ah = p.A[h], Dh = p.D[h];
 
     const T *pX = static_cast<const T *>(p.pend_x);
@@ -397,8 +400,15 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
             hv[i].w = state_step(a, hv[i].w, bn, u.w);
         }
     }
+    // The folded state goes back to HBM only when the next commit could overflow the
+    // pending area (m + K > k_max; always for a fold alone): otherwise the accepted rows stay
+    // pending (the logical state is unchanged either way, and every later fold runs the
+    // same steps in the same order, so the bits do not depend on when the write happens)
+    // and the commit appends to them.  One thread per slot records where it appends.
+    const bool write_back = m > 0 && (K == 0 || m + K > kmax);
+    if (threadIdx.x == 0 && blockIdx.x == 0) p.append[b] = write_back || m == 0 ? 0 : m;
     if (K == 0) {  // fold only: no outputs
-        if (m > 0) {
+        if (write_back) {
 #pragma unroll
             for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
         }
@@ -431,7 +441,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     // same at 32 x 32 heads, N = 256, K = 4, and 1.5 us faster at 16 x 32 heads, N = 128,
     // K = 8, where every workgroup is resident at once and early stores compete with the
     // other workgroups' state loads.
-    if (m > 0) {
+    if (write_back) {
 #pragma unroll
         for (int i = 0; i < ROWS; ++i) buf_store4(hv[i], srs, voff, i * P * 4);
     }

@@ -101,6 +101,11 @@ class SSMCache:
     def pending(self) -> torch.Tensor:
         return self._i32(self.layout.pending_off)
 
+    def append(self) -> torch.Tensor:
+        """Per slot, the pending row at which the next commit puts its first accepted row
+        (0 when the verify before it wrote the folded state back)."""
+        return self._i32(self.layout.append_off)
+
     def err(self) -> torch.Tensor:
         return self._i32(self.layout.err_off)
 

@@ -238,6 +238,8 @@ class Workload:
     d_model: int = 0         # > 0: the drafts' x, B, C, dt are projected on the device from
                              # layer input rows of this width (the step before the layer)
     tree: str = ""           # draft-tree shape (draw_tree kinds); accept "tree" takes one node
+    kmax: int = 0            # pending rows a cache holds (0: K); above K, accepted rows collect
+                             # over rounds and a verify writes the state back only when full
     seed: int = 1000
 
 
@@ -269,5 +271,5 @@ WORKLOADS = {
                                      dtype=BF16, L=8192, chunk=256, seed=1004),
     # hybrid decode step: 24 SSM layers, batch 32, expanded state N=256
     "hybrid_decode": Workload("hybrid_decode", batch=32, H=32, P=128, N=256, G=8, dtype=BF16,
-                              K=4, L=1024, layers=24, accept="geometric", seed=1005),
+                              K=4, L=1024, layers=24, accept="geometric", kmax=8, seed=1005),
 }

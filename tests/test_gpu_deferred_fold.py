@@ -1,0 +1,114 @@
+"""The deferred state write-back: a cache whose pending area holds more rows than one
+round's drafts (k_max > K) lets accepted rows accumulate, and a verify writes the folded
+state back only when the next commit could overflow the pending area.
+
+Two caches take the same inputs: one with k_max = K (every verify with pending rows writes
+back) and one with k_max = 4K.  Every round's outputs must agree bit for bit and match the
+oracle; the deferring cache's append and pending counts must follow the rule, and its
+stored state must be untouched by a verify that defers; after a final commit with
+MIL_COMMIT_MATERIALIZE both states agree bit for bit and match the oracle.  Chain, tree and
+greedy commits, and a rejected accepted length, all take part.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import BOUND, dev, dev_layer, dev_tokens, state_err, y_err
+from speculative_decode_amd import synth
+from speculative_decode_amd.ssm import SSMCache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from speculative_decode_amd import _lib
+    _lib.lib()
+
+
+def i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+def test_deferred_write_back_matches_eager(dtype):
+    batch, H, P, N, G, K, kmax = 6, 4, 64, 64, 2, 4, 16
+    rng = np.random.default_rng(6200 + (dtype == synth.F32))
+    layer = synth.draw_layer(rng, H)
+    A, D = dev_layer(layer)
+    Af, Df = layer.A.f64, layer.D.f64
+    pre = synth.draw_tokens(rng, batch, 48, H, P, N, G, dtype)
+    eager = SSMCache(batch, H, P, N, G, K, dtype)
+    lazy = SSMCache(batch, H, P, N, G, kmax, dtype)
+    for c in (eager, lazy):
+        c.prefill(*dev_tokens(pre), A, D, chunk=64, want_y=False)
+    h = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, Af, Df)[1]
+    kinds = ["chain"] * 5 + ["tree", "chain", "greedy", "chain", "reject", "chain", "tree", "chain", "greedy"]
+    deferred_rounds = 0
+    for r, kind in enumerate(kinds):
+        print(f"round {r}: {kind}", flush=True)
+        drf = synth.draw_tokens(rng, batch, K, H, P, N, G, dtype)
+        dx, dB, dC, ddt = dev_tokens(drf)
+        m = lazy.pending().cpu().numpy().copy()
+        raw = lazy.state().clone()
+        par = synth.draw_tree(rng, batch, K, "random") if kind == "tree" else None
+        if par is not None:
+            ys = [c.verify_tree(i32(par), dx, dB, dC, ddt, A, D) for c in (eager, lazy)]
+            ry = oracle.verify_tree(h, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, Af, Df, par)
+        else:
+            ys = [c.verify(dx, dB, dC, ddt, A, D) for c in (eager, lazy)]
+            ry = oracle.verify(h, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, Af, Df)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0], ys[1]), r
+        assert y_err(ys[1].cpu().numpy(), ry) <= BOUND[dtype]
+        # the rule: write back only when pending + K could overflow the pending area
+        wb = (m > 0) & (m + K > kmax)
+        assert np.array_equal(lazy.append().cpu().numpy(), np.where(wb | (m == 0), 0, m)), r
+        if not wb.any():
+            assert torch.equal(lazy.state(), raw), r  # nothing written back this round
+            deferred_rounds += int((m > 0).any())
+        if kind == "tree":
+            node = rng.integers(-1, K, size=batch)
+            for c in (eager, lazy):
+                c.commit_tree(i32(par), i32(node), dx, dB, ddt)
+            h, _ = oracle.commit_tree(h, drf.x.f64, drf.B.f64, drf.dt.f64, Af, Df, par, node)
+        elif kind == "greedy":
+            planted = synth.draw_accept_uniform(rng, batch, K)
+            tok, lg = synth.draw_greedy(rng, batch, K, 300, synth.F32, planted)
+            j_ref, _ = oracle.greedy_accept(tok, lg.f64)
+            accs = [c.commit_greedy(i32(tok), dev(lg), dx, dB, ddt)[0] for c in (eager, lazy)]
+            assert np.array_equal(accs[1].cpu().numpy(), j_ref)
+            h = oracle.commit(h, drf.x.f64, drf.B.f64, drf.dt.f64, Af, Df, j_ref)
+        else:
+            j = synth.draw_accept_uniform(rng, batch, K)
+            if kind == "reject":
+                j[1] = K + 1  # rejected: slot 1 keeps its logical state and pending rows
+            for c in (eager, lazy):
+                c.commit(i32(j), dx, dB, ddt)
+            jr = j.copy()
+            jr[(jr < 0) | (jr > K)] = 0
+            h = oracle.commit(h, drf.x.f64, drf.B.f64, drf.dt.f64, Af, Df, jr)
+            if kind == "reject":
+                for c in (eager, lazy):
+                    assert c.status(clear=True) == 1
+        torch.cuda.synchronize()
+        assert torch.equal(eager.pos(), lazy.pos()), r
+        assert int(lazy.pending().max()) <= kmax
+    assert deferred_rounds > 0  # the deferring cache did defer
+    # materialize both: one more verify, then a commit of nothing with the fold forced
+    drf = synth.draw_tokens(rng, batch, K, H, P, N, G, dtype)
+    dx, dB, dC, ddt = dev_tokens(drf)
+    for c in (eager, lazy):
+        c.verify(dx, dB, dC, ddt, A, D)
+        c.commit(i32(np.zeros(batch)), dx, dB, ddt, A, D, materialize=True)
+    torch.cuda.synchronize()
+    assert torch.equal(eager.state(), lazy.state())
+    assert int(lazy.pending().max()) == 0
+    e = state_err(lazy.state().cpu().numpy(), h)
+    print(f"final state err {e:.2e}", flush=True)
+    assert e <= BOUND[dtype]

@@ -120,22 +120,27 @@ def test_long_prefill_8192(a_mode):
 
 
 def test_hybrid_decode_layer():
-    """One layer of the hybrid decode step: batch 32, N=256, K=4, geometric accepted
-    lengths; prior state from a (shortened, 256-token) GPU prefill per sequence; every head
-    of every slot against the oracle, two rounds."""
+    """One layer of the hybrid decode step as the bench runs it: batch 32, N=256, K=4,
+    geometric accepted lengths, caches holding the workload's pending rows (so verifies
+    write the state back only when a commit could overflow them); prior state from a
+    (shortened, 256-token) GPU prefill per sequence; every head of every slot against the
+    oracle over six rounds, then the state after a materializing commit."""
     w = synth.WORKLOADS["hybrid_decode"]
     rng = np.random.default_rng(w.seed)
     layer = synth.draw_layer(rng, w.H)
     Lp = 256
     pre = synth.draw_tokens(rng, w.batch, Lp, w.H, w.P, w.N, w.G, w.dtype)
-    cache = SSMCache(w.batch, w.H, w.P, w.N, w.G, w.K, w.dtype)
+    cache = SSMCache(w.batch, w.H, w.P, w.N, w.G, w.kmax or w.K, w.dtype)
     A, D = dev_layer(layer)
     cache.prefill(*dev_tokens(pre), A, D, chunk=w.chunk, want_y=False)
     st = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, layer.A.f64, layer.D.f64)[1]
-    for r in range(2):
+    deferred = 0
+    for r in range(6):
         drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
         j = synth.draw_accept_geometric(rng, w.batch, w.K)
         dx, dB, dC, ddt = dev_tokens(drf)
+        m = cache.pending().cpu().numpy()
+        deferred += int(((m > 0) & (m + w.K <= (w.kmax or w.K))).sum())
         yv = cache.verify(dx, dB, dC, ddt, A, D)
         torch.cuda.synchronize()
         ry = oracle.verify(st, drf.x.f64, drf.B.f64, drf.C.f64, drf.dt.f64, layer.A.f64, layer.D.f64)
@@ -144,10 +149,15 @@ def test_hybrid_decode_layer():
         assert e <= BOUND[w.dtype]
         st = oracle.commit(st, drf.x.f64, drf.B.f64, drf.dt.f64, layer.A.f64, layer.D.f64, j)
         cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt)
-    # the next verify folds the last accepted rows; its written state against the oracle's
+    print(f"verifies that left their slot's rows pending: {deferred}")
+    if w.kmax > w.K:
+        assert deferred > 0
+    # fold everything still pending and compare the stored state with the oracle's
     drf = synth.draw_tokens(rng, w.batch, w.K, w.H, w.P, w.N, w.G, w.dtype)
-    cache.verify(*dev_tokens(drf), A, D)
+    dx, dB, dC, ddt = dev_tokens(drf)
+    cache.verify(dx, dB, dC, ddt, A, D)
+    cache.commit(torch.from_numpy(np.zeros(w.batch, np.int32)).cuda(), dx, dB, ddt, A, D, materialize=True)
     torch.cuda.synchronize()
     e = state_err(cache.state().cpu().numpy(), st)
-    print(f"hybrid folded state err over all heads {e:.2e}")
+    print(f"hybrid state err over all heads {e:.2e}")
     assert e <= BOUND[w.dtype]
