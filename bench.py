@@ -352,7 +352,8 @@ def run_gpu(args, w):
                              jr=[torch.from_numpy(jr).to(dev) for jr in j_rounds], jrn=j_rounds,
                              # host mirror of every layer's pending counts (the caches start
                              # with none pending) and of where the next commit appends
-                             m=np.zeros((nlayers, Bt), np.int64), base=np.zeros((nlayers, Bt), np.int64)))
+                             m=np.zeros((nlayers, Bt), np.int64), base=np.zeros((nlayers, Bt), np.int64),
+                             round=0))
         del proto
         torch.cuda.synchronize()
     R = len(sets)
@@ -392,7 +393,10 @@ def run_gpu(args, w):
         if nlayers > 1 and not st.get("tree") and not st.get("greedy"):
             # every layer's commit of the round in one call (one launch per 32 layers)
             d = st["drf"]
-            r = (s // R) % len(st["jr"])
+            # the round's draw: one running count per set, so that every pass (warm-up,
+            # timed, traced, back to back) continues the same sequence of pending counts
+            r = st["round"] % len(st["jr"])
+            st["round"] += 1
             commit_layers(st["caches"], st["jr"][r], [t[0] for t in d], [t[1] for t in d], [t[3] for t in d])
             st["m"][:] = st["base"] + st["jrn"][r][None, :]
             return
@@ -424,30 +428,26 @@ def run_gpu(args, w):
 
     def verify_pass():
         """Time per verify launch from launches back to back: the verifies of n whole steps
-        (distinct caches: every layer of n rotating sets) between two events, then their
-        commits.  No event sits between the launches, so no dispatch latency is added.  A
-        multi-layer step rotates through kRounds accepted-length draws: a priming pass
-        commits the last draw, then kRounds timed passes fold each draw once (each commits
-        the next), and their times are averaged."""
+        (distinct caches: every layer of n rotating sets) between two timing events, then
+        their commits.  No event sits between the verify launches, so no dispatch latency is
+        added.  A multi-layer step rotates through kRounds accepted-length draws: one whole
+        cycle of them runs under one hold, step after step as a decode loop would (the
+        commits between the timed spans), and the spans are summed."""
         n = max(1, min(args.steps, R))
         rounds = kRounds if nlayers > 1 else 1
-
-        def one(first):
-            hold(n)
-            e0.record()
-            for s in range(n):
-                verify_part(first + s, mark=False, project_too=False)
-            e1.record()
-            for s in range(n):
-                commit_part(first + s)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1)
-
-        if rounds > 1:
-            one((rounds - 1) * R)  # priming: leaves the last draw pending
+        marks = [(TimingEvent(), TimingEvent()) for _ in range(rounds)]
         vstats.update(on=True, rows=0, writes=0, slots=0)
-        tot = sum(one(r * R) for r in range(rounds))
+        hold(n * rounds)
+        for r in range(rounds):
+            marks[r][0].record()
+            for s in range(n):
+                verify_part(r * R + s, mark=False, project_too=False)
+            marks[r][1].record()
+            for s in range(n):
+                commit_part(r * R + s)
+        torch.cuda.synchronize()
         vstats["on"] = False
+        tot = sum(a.elapsed_time(b) for a, b in marks)
         return tot / (rounds * n * nlayers)
 
     trace_project = [False]  # the projection is traced with events on torch's stream, around the call
@@ -838,8 +838,10 @@ def mfma_counters(db, workload):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # multiples of kRounds: every phase of a multi-layer run covers whole cycles of the
+    # accepted-length draws, so each phase's verifies fold and write the same mix
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="hybrid_decode")
     ap.add_argument("--prefill-workload", default="llama8b_long_prefill",
                     help="with a verify workload: also run this prefill workload and report it in the same "

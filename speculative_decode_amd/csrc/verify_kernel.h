@@ -385,19 +385,25 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
 
     if (bad && p.err) atomicOr(p.err + b, MIL_DEVERR_TREE);
 
-    // ---- fold the m pending rows, token by token ----
-    for (int s = 0; s < m; ++s) {
-        const float a = sRA[s], d = sRdt[s];
-        const float4 xr = *reinterpret_cast<const float4 *>(sRX + s * Pc + 4 * c4);
-        const float4 u = make_float4(d * xr.x, d * xr.y, d * xr.z, d * xr.w);  // dt * x
-        const float *bs = sRB + s * N + n0;
+    // ---- fold the m pending rows, token by token: the lane's first half of the state rows
+    // while the second half may still be arriving, then the second (each element takes the
+    // same steps in the same order either way; batched shape 17.75 -> 17.5 us) ----
+    constexpr int HALF = ROWS > 1 ? ROWS / 2 : 1;
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            const float bn = bs[i];
-            hv[i].x = state_step(a, hv[i].x, bn, u.x);
-            hv[i].y = state_step(a, hv[i].y, bn, u.y);
-            hv[i].z = state_step(a, hv[i].z, bn, u.z);
-            hv[i].w = state_step(a, hv[i].w, bn, u.w);
+    for (int i0 = 0; i0 < ROWS; i0 += HALF) {
+        for (int s = 0; s < m; ++s) {
+            const float a = sRA[s], d = sRdt[s];
+            const float4 xr = *reinterpret_cast<const float4 *>(sRX + s * Pc + 4 * c4);
+            const float4 u = make_float4(d * xr.x, d * xr.y, d * xr.z, d * xr.w);  // dt * x
+            const float *bs = sRB + s * N + n0;
+#pragma unroll
+            for (int i = i0; i < i0 + HALF; ++i) {
+                const float bn = bs[i];
+                hv[i].x = state_step(a, hv[i].x, bn, u.x);
+                hv[i].y = state_step(a, hv[i].y, bn, u.y);
+                hv[i].z = state_step(a, hv[i].z, bn, u.z);
+                hv[i].w = state_step(a, hv[i].w, bn, u.w);
+            }
         }
     }
     // The folded state goes back to HBM only when the next commit could overflow the
