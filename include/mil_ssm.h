@@ -186,8 +186,10 @@ int mil_ssm_prefill(mil_ssm_cache *cache, int32_t slot0, int32_t nseq, int32_t L
  * x, B, C, dt hold the drafts, [batch][K][...]; y [batch][K][H][P] receives, for each
  * draft k, the output the layer gives when drafts 0..k follow the slot's logical state.
  * The logical state is NOT changed (a draft is folded in only by a later commit).
- * Each (slot, head) state block is read from HBM once; pending accepted rows from the
- * previous round are folded in on the way and the result is written back once.
+ * Each (slot, head) state block is read from HBM once; the pending accepted rows are
+ * folded in on the way (in registers), and the folded state is written back once, only if
+ * pending + K > k_max (the next commit could overflow the pending area); otherwise the
+ * rows stay pending and the next commit appends to them (see the cache layout above).
  * Order: READY -> VERIFIED.  A second verify without a commit returns MIL_E_ORDER.
  */
 int mil_ssm_verify(mil_ssm_cache *cache, int32_t K,
@@ -200,8 +202,9 @@ int mil_ssm_verify(mil_ssm_cache *cache, int32_t K,
  * verify (C is not needed).  The logical state of slot b becomes the state after its
  * accepted drafts; pos[b] += accepted[b].  The accepted rows are copied into the cache,
  * so the draft buffers may be reused once this call is enqueued.  By default the rows are
- * folded into `state` by the next verify or prefill; MIL_COMMIT_MATERIALIZE folds them in
- * now (same arithmetic, bit-identical state).  An accepted[b] outside 0..K sets
+ * folded into `state` by a later verify (when it writes the state back) or prefill;
+ * MIL_COMMIT_MATERIALIZE folds every pending row in now (same arithmetic, bit-identical
+ * state).  An accepted[b] outside 0..K sets
  * err[b] = MIL_DEVERR_ACCEPT and leaves slot b's logical state and pos unchanged.
  * A and D are needed only with MIL_COMMIT_MATERIALIZE (may be NULL otherwise).
  * Order: VERIFIED -> READY (MIL_E_ORDER otherwise); K must equal the verified K.
