@@ -35,10 +35,11 @@ def i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
-@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
-def test_deferred_write_back_matches_eager(dtype):
-    batch, H, P, N, G, K, kmax = 6, 4, 64, 64, 2, 4, 16
-    rng = np.random.default_rng(6200 + (dtype == synth.F32))
+@pytest.mark.parametrize("dtype,K,kmax", [(synth.BF16, 4, 16), (synth.F32, 4, 16), (synth.BF16, 1, 3),
+                                          (synth.BF16, 7, 9)])
+def test_deferred_write_back_matches_eager(dtype, K, kmax):
+    batch, H, P, N, G = 6, 4, 64, 64, 2
+    rng = np.random.default_rng(6200 + 10 * K + kmax + (dtype == synth.F32))
     layer = synth.draw_layer(rng, H)
     A, D = dev_layer(layer)
     Af, Df = layer.A.f64, layer.D.f64
@@ -69,9 +70,10 @@ def test_deferred_write_back_matches_eager(dtype):
         # the rule: write back only when pending + K could overflow the pending area
         wb = (m > 0) & (m + K > kmax)
         assert np.array_equal(lazy.append().cpu().numpy(), np.where(wb | (m == 0), 0, m)), r
-        if not wb.any():
-            assert torch.equal(lazy.state(), raw), r  # nothing written back this round
-            deferred_rounds += int((m > 0).any())
+        # a slot whose rows stayed pending keeps its stored state bit for bit
+        keep = torch.from_numpy(~wb).cuda()
+        assert torch.equal(lazy.state()[keep], raw[keep]), r
+        deferred_rounds += int(((m > 0) & ~wb).sum())
         if kind == "tree":
             node = rng.integers(-1, K, size=batch)
             for c in (eager, lazy):
@@ -99,7 +101,7 @@ def test_deferred_write_back_matches_eager(dtype):
         torch.cuda.synchronize()
         assert torch.equal(eager.pos(), lazy.pos()), r
         assert int(lazy.pending().max()) <= kmax
-    assert deferred_rounds > 0  # the deferring cache did defer
+    assert deferred_rounds > 0  # the deferring cache did defer (slot-rounds left pending)
     # materialize both: one more verify, then a commit of nothing with the fold forced
     drf = synth.draw_tokens(rng, batch, K, H, P, N, G, dtype)
     dx, dB, dC, ddt = dev_tokens(drf)
