@@ -48,17 +48,22 @@ def _random_parents(rng, Bt, K):
     return par
 
 
-# (batch, H, P, N, G), token dtype, drafts per round, seed
+# (batch, H, P, N, G), token dtype, drafts per round, pending rows the cache holds, seed;
+# with more pending rows than drafts, accepted rows collect over rounds and a verify
+# writes the state back only when a commit could overflow the pending area
 CASES = [
-    ((3, 4, 64, 64, 2), synth.BF16, 4, 1),
-    ((2, 4, 32, 32, 2), synth.F32, 5, 2),
-    ((1, 32, 128, 128, 8), synth.BF16, 4, 3),
+    ((3, 4, 64, 64, 2), synth.BF16, 4, 4, 1),
+    ((2, 4, 32, 32, 2), synth.F32, 5, 5, 2),
+    ((1, 32, 128, 128, 8), synth.BF16, 4, 4, 3),
+    ((3, 4, 64, 64, 2), synth.BF16, 4, 13, 4),
+    ((2, 4, 32, 32, 2), synth.F32, 5, 16, 5),
 ]
 
 
-@pytest.mark.parametrize("shape,dtype,K,seed", CASES,
-                         ids=[f"{c[0][1]}h_P{c[0][2]}_N{c[0][3]}_{'bf16' if c[1] == synth.BF16 else 'f32'}" for c in CASES])
-def test_mixed_protocol_against_oracle(shape, dtype, K, seed):
+@pytest.mark.parametrize("shape,dtype,K,kmax,seed", CASES,
+                         ids=[f"{c[0][1]}h_P{c[0][2]}_N{c[0][3]}_{'bf16' if c[1] == synth.BF16 else 'f32'}_kmax{c[3]}"
+                              for c in CASES])
+def test_mixed_protocol_against_oracle(shape, dtype, K, kmax, seed):
     Bt, H, P, N, G = shape
     rng = np.random.default_rng(1000 + seed)
     layer = synth.draw_layer(rng, H)
@@ -68,7 +73,7 @@ def test_mixed_protocol_against_oracle(shape, dtype, K, seed):
 
     L0 = int(rng.integers(20, 300))
     pre = synth.draw_tokens(rng, Bt, L0, H, P, N, G, dtype)
-    cache = SSMCache(Bt, H, P, N, G, K, dtype)
+    cache = SSMCache(Bt, H, P, N, G, kmax, dtype)
     y = _np(cache.prefill(*dev_tokens(pre), A, D, chunk=256))
     ry, ref = oracle.prefill(pre.x.f64, pre.B.f64, pre.C.f64, pre.dt.f64, Af, Df)
     assert y_err(y, ry) <= tol
