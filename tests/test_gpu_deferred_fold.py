@@ -114,3 +114,38 @@ def test_deferred_write_back_matches_eager(dtype, K, kmax):
     e = state_err(lazy.state().cpu().numpy(), h)
     print(f"final state err {e:.2e}", flush=True)
     assert e <= BOUND[dtype]
+
+
+def test_snapshot_with_rows_pending_continues_bit_for_bit():
+    """A cache holding accepted rows not yet written back, copied byte for byte and attached
+    as a second cache (a snapshot of the whole resumable context), continues exactly as the
+    original: same outputs and states, bit for bit, over further rounds."""
+    batch, H, P, N, G, K, kmax = 4, 4, 64, 64, 2, 4, 12
+    rng = np.random.default_rng(6300)
+    layer = synth.draw_layer(rng, H)
+    A, D = dev_layer(layer)
+    pre = synth.draw_tokens(rng, batch, 40, H, P, N, G, synth.BF16)
+    orig = SSMCache(batch, H, P, N, G, kmax, synth.BF16)
+    orig.prefill(*dev_tokens(pre), A, D, chunk=64, want_y=False)
+
+    def round_(caches, drf, j):
+        dx, dB, dC, ddt = dev_tokens(drf)
+        ys = [c.verify(dx, dB, dC, ddt, A, D) for c in caches]
+        for c in caches:
+            c.commit(i32(j), dx, dB, ddt)
+        return ys
+
+    for _ in range(3):
+        round_([orig], synth.draw_tokens(rng, batch, K, H, P, N, G, synth.BF16),
+               synth.draw_accept_uniform(rng, batch, K))
+    torch.cuda.synchronize()
+    assert int(orig.pending().max()) > 0  # rows are pending in the snapshot
+    raw = torch.empty_like(orig.buffer)
+    raw.copy_(orig.buffer)
+    copy = SSMCache(batch, H, P, N, G, kmax, synth.BF16, attach_to=raw)
+    for r in range(4):
+        ys = round_([orig, copy], synth.draw_tokens(rng, batch, K, H, P, N, G, synth.BF16),
+                    synth.draw_accept_uniform(rng, batch, K))
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0], ys[1]), r
+        assert torch.equal(orig.buffer, copy.buffer), r
