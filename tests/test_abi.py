@@ -12,6 +12,7 @@ import os
 import re
 
 import pytest
+from hypothesis import given, settings, strategies as st
 
 from speculative_decode_amd import _lib as L
 
@@ -59,15 +60,42 @@ def test_layout_is_head_major_and_aligned(lib, shape, dtype, k_max):
     Bt, H, P, N, G = shape
     e = 2 if dtype == L.MIL_BF16 else 4
     offs = [lay.state_off, lay.pend_x_off, lay.pend_B_off, lay.pend_dt_off, lay.pos_off,
-            lay.pending_off, lay.err_off, lay.scan_off, lay.bytes]
+            lay.pending_off, lay.err_off, lay.scan_off, lay.append_off, lay.bytes]
     assert all(o % 256 == 0 for o in offs)
     assert lay.state_head_stride % 256 == 0 and lay.state_head_stride >= N * P * 4
     assert lay.state_head_stride < N * P * 4 + 256
-    # regions in order, each big enough, no overlap
+    # regions in order, each big enough, no overlap; the prefill handoff words are
+    # [slot][head][8 column slabs][64 chunk flags, the row's epoch, 3 spare words]
     sizes = [Bt * H * lay.state_head_stride, Bt * k_max * H * P * e, Bt * k_max * G * N * e,
-             Bt * k_max * H * e, Bt * 4, Bt * 4, Bt * 4, Bt * H * 8 * 8 * 4]
+             Bt * k_max * H * e, Bt * 4, Bt * 4, Bt * 4, Bt * H * 8 * (64 + 4) * 4, Bt * 4]
     for a, b, sz in zip(offs, offs[1:], sizes):
         assert b - a >= sz
+    assert lib.mil_ssm_cache_bytes(ctypes.byref(d), k_max, dtype) == lay.bytes
+
+
+@settings(max_examples=300, deadline=None)
+@given(batch=st.integers(1, 4096), G=st.sampled_from([1, 2, 4, 8, 16]), rep=st.integers(1, 8),
+       P=st.sampled_from([16, 32, 64, 128, 256]), N=st.sampled_from([16, 32, 64, 128, 256]),
+       k_max=st.integers(1, 16), dtype=st.sampled_from([L.MIL_F32, L.MIL_BF16]))
+def test_layout_regions_over_random_shapes(lib, batch, G, rep, P, N, k_max, dtype):
+    """Any supported shape: every region starts on a 256-B boundary, after the end of the
+    one before it, and the cache size covers the last; the two size queries agree."""
+    H = G * rep
+    d = L.Dims(batch, H, P, N, G)
+    lay = L.Layout()
+    assert lib.mil_ssm_cache_layout(ctypes.byref(d), k_max, dtype, ctypes.byref(lay)) == L.MIL_OK
+    e = 2 if dtype == L.MIL_BF16 else 4
+    regions = [(lay.state_off, batch * H * lay.state_head_stride),
+               (lay.pend_x_off, batch * k_max * H * P * e), (lay.pend_B_off, batch * k_max * G * N * e),
+               (lay.pend_dt_off, batch * k_max * H * e), (lay.pos_off, batch * 4),
+               (lay.pending_off, batch * 4), (lay.err_off, batch * 4),
+               (lay.scan_off, batch * H * 8 * (64 + 4) * 4), (lay.append_off, batch * 4)]
+    end = 0
+    for off, size in regions:
+        assert off % 256 == 0 and off >= end
+        end = off + size
+    assert lay.bytes >= end and lay.bytes % 256 == 0 and lay.bytes - end < 256
+    assert lay.state_head_stride == -(-N * P * 4 // 256) * 256
     assert lib.mil_ssm_cache_bytes(ctypes.byref(d), k_max, dtype) == lay.bytes
 
 
