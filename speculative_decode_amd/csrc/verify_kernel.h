@@ -136,6 +136,19 @@ constexpr int64_t kWavesTarget = 2048;
 inline Shape shape_for(int batch, int H, int P, int N, int K, int kmax) {
     Shape best{0, 0, 0};
     if (P < 16 || P > 256 || (P & (P - 1)) || N < 16 || N > 256 || (N & (N - 1))) return best;
+    // Whole rows in 8-wave workgroups with 9..16 rows per lane (N x P = 32768 floats per
+    // head) where that grid still reaches the waves target, ahead of the column tiles the
+    // loop below would take: at 32 slots, P = 128, N = 256 each workgroup then streams one
+    // contiguous 128 KiB block, and verify took 38.3-38.7 us against 39.8-40.7 us with two
+    // column tiles of 8 rows per lane (16-wave whole-row workgroups: 44.6 us).
+    {
+        const int rg = 8 * (256 / P);  // row groups of an 8-wave workgroup (P/4 lanes per row)
+        const int rows = rg <= N ? N / rg : 0;
+        if (rows > kRowsTarget && rows <= 16 && 8 * 64 <= max_threads(rows) &&
+            verify_lds_floats(N, P, K, kmax, 8) * sizeof(float) <= kVerifyLdsMax &&
+            (int64_t)batch * H * 8 >= kWavesTarget)
+            return Shape{8, rows, 1};
+    }
     for (int64_t target : {kWavesTarget, kWavesTarget / 4}) {
         for (int cs = 1; cs <= 4 && P / cs >= 16; cs *= 2) {
             const int Pc = P / cs, RGW = 256 / Pc;

@@ -344,6 +344,21 @@ def test_tiny_f32_protocol_against_oracle():
 def test_verify_rounds_against_oracle(dtype, shape, K, k_max):
     """Several rounds with ragged accepted lengths per sequence: y of every round and
     pos exactly; the final folded state against the oracle."""
+    verify_rounds(dtype, shape, K, k_max)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("shape,K,k_max", [((8, 32, 128, 256, 8), 4, 8), ((8, 32, 128, 256, 8), 16, 16),
+                                           ((8, 32, 256, 128, 8), 4, 4), ((8, 32, 256, 128, 8), 1, 3)])
+def test_verify_rounds_whole_row_workgroups(dtype, shape, K, k_max):
+    """The launch that gives each 8-wave workgroup a whole (slot, head) block with 16 rows
+    per lane (N x P = 32768 floats per head, at least 256 slot-heads): the same rounds
+    against the oracle, in both orientations of N and P, with deferred and immediate
+    write-back and the most drafts."""
+    verify_rounds(dtype, shape, K, k_max)
+
+
+def verify_rounds(dtype, shape, K, k_max):
     Bt, H, P, N, G = shape
     rng = np.random.default_rng(100 * K + Bt * H + P + N)
     layer, pre = make_layer_and_tokens(rng, Bt, 37, H, P, N, G, dtype)
