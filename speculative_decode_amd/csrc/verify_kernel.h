@@ -241,9 +241,11 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     const int h = blockIdx.x / p.cs, b = blockIdx.y;
     const int col0 = (blockIdx.x - h * p.cs) * Pc;
     const int g = h / (H / G);
-    // uniform, so branches on m stay scalar; clamped to the pending area, so that no value in
-    // the buffer can make the staging read or write outside it
-    const int m = min(max(__builtin_amdgcn_readfirstlane(p.pending[b]), 0), kmax);
+    // The slot's pending count m: loaded here through the vector memory path (it returns in
+    // order with the loads after it, so staging the token rows waits for it too) and used
+    // only once every load is issued, so that no workgroup waits for it before asking for
+    // its rows (a scalar load would be waited on with the kernel's other scalar loads).
+    const int mraw = __hip_atomic_load(p.pending + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float Ah = p.A[h], Dh = p.D[h];
 
     const T *pX = static_cast<const T *>(p.pend_x);
@@ -254,18 +256,23 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     const T *dC = static_cast<const T *>(p.C);
     const T *dDt = static_cast<const T *>(p.dt);
 
-    if (K == 0 && m == 0) return;  // nothing to fold and nothing to read out
+    if (K == 0) {  // a fold alone: nothing to do for a slot without pending rows
+        asm volatile("" ::: "memory");  // keeps this test (and its wait for m) off the K > 0 path
+        if (min(max(__builtin_amdgcn_readfirstlane(mraw), 0), kmax) == 0) return;
+    }
 
     // ---- staging.  The global loads go out in one batch and are waited on once: first
     // the token rows this workgroup needs as 16-byte chunks (pending B, draft B, draft C:
     // N wide; pending x, draft x: this tile's Pc columns), then the dt values, then the
     // state rows.  Loads return in issue order, so writing the token rows to LDS waits
-    // for them alone while the state loads are still in flight. ----
+    // for them alone while the state loads are still in flight.  All k_max pending rows
+    // are loaded whatever m is (the area holds them; rows past m are staged and unused), so
+    // no address waits for m. ----
     constexpr int E = 16 / sizeof(T);       // elements per chunk
     constexpr int CH = ROWS >= 32 ? 1 : 4;  // chunks per thread in the batch
     const int lgN = __builtin_ctz(N / E), lgP = __builtin_ctz(Pc / E);
-    const int e0 = m << lgN, e1 = e0 + (K << lgN), e2 = e1 + (K << lgN);
-    const int e3 = e2 + (m << lgP), e4 = e3 + (K << lgP);
+    const int e0 = kmax << lgN, e1 = e0 + (K << lgN), e2 = e1 + (K << lgN);
+    const int e3 = e2 + (kmax << lgP), e4 = e3 + (K << lgP);
     const bool batched = p.vec && e4 <= CH * NT;  // else: element loops after the state loads
     const int xoff = (int)(sRX - lds);
     uint4 v[CH];
@@ -302,8 +309,13 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     const T *dsrc = K > 0 ? dDt + (size_t)(b * K + max(min(tid, K - 1), 0)) * H + h : pDt + prow;
     const float pdt = ld(pDt, prow);
     const float ddt = ld(dsrc, 0);
-    // draft tid's parent link, read before the state so that staging it waits for nothing else
-    const int par = p.parent ? p.parent[(size_t)b * K + max(min(tid, K - 1), 0)] : tid - 1;
+    // draft tid's parent link, read before the state so that staging it waits for nothing
+    // else.  The load is issued for a chain too (from the slot's pending count: any valid
+    // word) and a chain's link tid - 1 is taken where it is staged.  With a branch around
+    // the load the compiler guarded the link's register against the tree path's load in
+    // flight, and the chain path waited for every load before issuing the state loads.
+    const int *plink = p.parent ? p.parent + (size_t)b * K + max(min(tid, K - 1), 0) : p.pending + b;
+    const int link = *plink;
 
     // the state rows: 16-byte buffer loads, one read per element
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.state + (size_t)(b * H + h) * p.head_stride, N * P * 4);
@@ -311,6 +323,9 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     float4 hv[ROWS];
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) hv[i] = buf_load4(srs, voff, i * P * 4);
+    // uniform, so branches on m stay scalar; clamped to the pending area, so that no value in
+    // the buffer can make the staging or the fold read or write outside it
+    const int m = min(max(__builtin_amdgcn_readfirstlane(mraw), 0), kmax);
 
     if (batched) {
 #pragma unroll
@@ -343,7 +358,7 @@ __global__ __launch_bounds__(max_threads(ROWS)) void ssm_verify_kernel(const Ver
     if (tid < K) {
         sDdt[tid] = ddt;
         sDA[tid] = expf(ddt * Ah);
-        sPar[tid] = par;
+        sPar[tid] = p.parent ? link : tid - 1;
     }
 
     lds_barrier();  // the staged rows are visible; the state loads may still be in flight
