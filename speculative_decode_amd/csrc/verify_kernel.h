@@ -30,10 +30,11 @@
 // Work decomposition (gfx950, wave64): one workgroup per (slot, head, column tile of
 // P/CS columns), S waves.  A lane owns 4 adjacent columns (16-byte loads) of ROWS
 // consecutive state rows; P/(4 CS) lanes cover a row tile, so a wave reads 64 * 16
-// bytes per load instruction.  Splitting the columns keeps ROWS (and the registers a
-// lane needs) small enough for two workgroups to share a CU, one streaming while the
-// other computes; the readout needs no exchange between tiles, since every output
-// column sums over all N rows of its own column only.  State
+// bytes per load instruction.  Whole rows per workgroup (CS = 1) where the registers
+// allow, so that each workgroup streams one contiguous block; splitting the columns keeps
+// ROWS (and the registers a lane needs) small enough for several workgroups to share a CU
+// where whole rows would not; the readout needs no exchange between tiles, since every
+// output column sums over all N rows of its own column only.  State
 // traffic is one read and at most one write per element; per-row work is in registers,
 // partial C_k . h sums are combined across the row groups of a wave with shuffles and
 // across waves through LDS, always in the same order.
