@@ -102,8 +102,9 @@ def test_graph_replays_match_eager(greedy):
             assert torch.equal(c.pos(), sets[1][li].pos()) and torch.equal(c.pending(), sets[1][li].pending())
 
 
-@pytest.mark.parametrize("kmax", [4, 8])
-def test_graph_decode_step_at_hybrid_layer_shape_matches_oracle(kmax):
+@pytest.mark.parametrize("kmax,multi", [(4, False), (8, False), (8, True)],
+                         ids=["kmax4", "kmax8", "kmax8_commit_layers"])
+def test_graph_decode_step_at_hybrid_layer_shape_matches_oracle(kmax, multi):
     """The decode step of the hybrid workload's layer shape (32 sequences, 32 heads,
     P = 128, N = 256, 8 groups, K = 4, accepted lengths ~ Geometric(0.3) capped at 4) for
     three layers, captured once and replayed for five rounds, with caches holding K or 8
@@ -112,9 +113,14 @@ def test_graph_decode_step_at_hybrid_layer_shape_matches_oracle(kmax):
     y against oracle verify from the oracle's committed state, and the stored state against
     the oracle's state through the previous round's accepted drafts where this round's
     verify wrote it back (else against the state before the verify, untouched); pending
-    counts follow the rule; replay == eager stays bit for bit on the whole layer."""
+    counts follow the rule; replay == eager stays bit for bit on the whole layer.  With
+    `multi`, every layer accepts the same lengths each round (the verifier decides after
+    the last layer) and the captured step commits all layers with one
+    mil_ssm_commit_layers launch, whose per-layer pointers travel in the captured kernel
+    arguments."""
     import oracle
     from gpu_util import BOUND, head_slice, state_err, y_err
+    from speculative_decode_amd.ssm import commit_layers
 
     rng = np.random.default_rng(5005)
     layers, Bt, H, P, N, G, K, L0 = 3, 32, 32, 128, 256, 8, 4, 256
@@ -151,7 +157,11 @@ def test_graph_decode_step_at_hybrid_layer_shape_matches_oracle(kmax):
         for li in range(layers):
             s = stat[li]
             sets[1][li].verify(s["x"], s["B"], s["C"], s["dt"], *params[li], y=s["y"])
-            sets[1][li].commit(s["j"], s["x"], s["B"], s["dt"])
+            if not multi:
+                sets[1][li].commit(s["j"], s["x"], s["B"], s["dt"])
+        if multi:  # one accepted-length buffer (layer 0's) for every layer
+            commit_layers(sets[1], stat[0]["j"], [s["x"] for s in stat], [s["B"] for s in stat],
+                          [s["dt"] for s in stat])
     torch.cuda.synchronize()
 
     pos = [np.full(Bt, L0) for _ in range(layers)]
@@ -159,9 +169,10 @@ def test_graph_decode_step_at_hybrid_layer_shape_matches_oracle(kmax):
     deferred = 0
     for rnd in range(5):
         rounds = []
+        j_shared = synth.draw_accept_geometric(rng, Bt, K) if multi else None
         for li in range(layers):
             drf = synth.draw_tokens(rng, Bt, K, H, P, N, G, dtype)
-            j = synth.draw_accept_geometric(rng, Bt, K)
+            j = j_shared if multi else synth.draw_accept_geometric(rng, Bt, K)
             x, B, C, dt = dev_tokens(drf)
             for key, t in (("x", x), ("B", B), ("C", C), ("dt", dt)):
                 stat[li][key].copy_(t)
@@ -194,13 +205,24 @@ def test_graph_decode_step_at_hybrid_layer_shape_matches_oracle(kmax):
             assert sets[1][li].pending().cpu().tolist() == pend[li].tolist()
             pos[li] = pos[li] + j
             assert sets[1][li].pos().cpu().numpy().tolist() == pos[li].tolist()
-            # the same round eagerly on the twin caches: bit for bit
+        # the same round eagerly on the twin caches: bit for bit
+        eager = []
+        for li in range(layers):
+            drf, j = rounds[li]
             c = sets[0][li]
             xe, Be, Ce, dte = dev_tokens(drf)
             ye = c.verify(xe, Be, Ce, dte, *params[li])
-            c.commit(torch.from_numpy(j).cuda(), xe, Be, dte)
-            torch.cuda.synchronize()
-            assert torch.equal(ye, stat[li]["y"]), (rnd, li)
+            if not multi:
+                c.commit(torch.from_numpy(j).cuda(), xe, Be, dte)
+            eager.append((ye, xe, Be, dte))
+        if multi:
+            commit_layers(sets[0], torch.from_numpy(rounds[0][1]).cuda(), [e[1] for e in eager],
+                          [e[2] for e in eager], [e[3] for e in eager])
+        torch.cuda.synchronize()
+        for li in range(layers):
+            c = sets[0][li]
+            assert torch.equal(eager[li][0], stat[li]["y"]), (rnd, li)
             assert torch.equal(c.state(), sets[1][li].state()), (rnd, li)
+            assert torch.equal(c.pending(), sets[1][li].pending()) and torch.equal(c.pos(), sets[1][li].pos())
     if kmax > K:
         assert deferred > 0
