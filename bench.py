@@ -46,7 +46,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
-kRounds = 8  # accepted-length draws a multi-layer step rotates through
+ACCEPT_DRAWS = 8  # accepted-length draws a multi-layer step rotates through
 KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "verify", "commit", "accept", "project", "prefill_scan"]
 PREFILL_KERNELS = ["prefill_state", "prefill_pass", "prefill_out", "prefill_scan"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -303,12 +303,12 @@ def run_gpu(args, w):
             caches, drfs, js, jns, yvs, greedy, proj, trees = [], [], [], [], [], [], [], []
             # a round accepts the same drafts in every layer (the verifier decides from the
             # last layer's output), so a multi-layer step uses one j for all its layers; the
-            # steps rotate through kRounds such draws (each verify folds the rows the step
+            # steps rotate through ACCEPT_DRAWS such draws (each verify folds the rows the step
             # before accepted)
             j_round, j_rounds = None, []
             if nlayers > 1:
                 j_rounds = [(synth.draw_accept_geometric(rng, Bt, K) if w.accept == "geometric"
-                             else synth.draw_accept_uniform(rng, Bt, K)) for _ in range(kRounds)]
+                             else synth.draw_accept_uniform(rng, Bt, K)) for _ in range(ACCEPT_DRAWS)]
                 j_round = j_rounds[0]
             for li in range(nlayers):
                 c = SSMCache(Bt, w.H, w.P, w.N, w.G, kcap, w.dtype, device=dev)
@@ -430,11 +430,11 @@ def run_gpu(args, w):
         """Time per verify launch from launches back to back: the verifies of n whole steps
         (distinct caches: every layer of n rotating sets) between two timing events, then
         their commits.  No event sits between the verify launches, so no dispatch latency is
-        added.  A multi-layer step rotates through kRounds accepted-length draws: one whole
+        added.  A multi-layer step rotates through ACCEPT_DRAWS accepted-length draws: one whole
         cycle of them runs under one hold, step after step as a decode loop would (the
         commits between the timed spans), and the spans are summed."""
         n = max(1, min(args.steps, R))
-        rounds = kRounds if nlayers > 1 else 1
+        rounds = ACCEPT_DRAWS if nlayers > 1 else 1
         marks = [(TimingEvent(), TimingEvent()) for _ in range(rounds)]
         vstats.update(on=True, rows=0, writes=0, slots=0)
         hold(n * rounds)
@@ -838,7 +838,7 @@ def mfma_counters(db, workload):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # multiples of kRounds: every phase of a multi-layer run covers whole cycles of the
+    # multiples of ACCEPT_DRAWS: every phase of a multi-layer run covers whole cycles of the
     # accepted-length draws, so each phase's verifies fold and write the same mix
     ap.add_argument("--steps", type=int, default=48)
     ap.add_argument("--warmup", type=int, default=8)
