@@ -472,7 +472,8 @@ def run_gpu(args, w):
         mask = lib.mil_ssm_prefill_kernels(ctypes.byref(sets[0]["caches"][0].desc), Bt, w.L, w.chunk)
         kernels = [k for k in PREFILL_KERNELS if mask & (1 << L.TRACE[k])] + kernels
     if w.accept == "greedy":
-        kernels = kernels + ["accept"]
+        # a greedy commit is one launch (argmax, accepted lengths, copies), traced as accept
+        kernels = [k for k in kernels if k != "commit"] + ["accept"]
     if w.d_model:
         kernels = kernels + ["project"]
     n_ev = max(args.steps, len(kernels) * 4)
@@ -621,7 +622,9 @@ def run_gpu(args, w):
             # one commit launch covers every layer of the round
             work["commit"] = (work["commit"][0] * nlayers, 0)
         if w.accept == "greedy":
-            work["accept"] = accept_work(w, Bt, K)
+            # the greedy commit's one launch: every logit read, the accepted rows copied
+            a, c = accept_work(w, Bt, K), work.pop("commit")
+            work["accept"] = (a[0] + c[0], 0)
         if w.d_model:
             work["project"] = project_work(w, Bt * K)
     jmean = float(jall.mean()) if kind in ("full", "verify") else 0.0
@@ -745,7 +748,7 @@ KERNEL_PATTERNS = {  # kernel family -> substring of its symbol
     "prefill_state": "chunk_state_", "prefill_pass": "state_pass", "prefill_out": "chunk_out_",
     "prefill_scan": "chunk_scan_",
     "verify": "ssm_verify_kernel", "commit": ("_commit_kernel", "_commit_tree_kernel", "_commit_layers_kernel"),
-    "accept": "greedy_argmax",
+    "accept": "greedy_accept",
     "project": "project_",
     "copy": "MulFunctor",  # the calibration copy: torch.mul(src, 1.0, out=dst)
 }

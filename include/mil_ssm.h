@@ -99,7 +99,9 @@ typedef struct {
  *           then stores e as the row's epoch, so the value that marks a launch lives in the
  *           buffer itself: graph replays and byte copies of a cache (mil_ssm_cache_attach)
  *           stay correct.  A buffer whose rows hold a flag of a later epoch than their own
- *           is not a cache this library wrote.
+ *           is not a cache this library wrote.  The word after the epoch in each slot's
+ *           first row (head 0, slab 0) counts the workgroups of a greedy commit that have
+ *           finished for that slot; it is 0 between calls (the last one resets it).
  *   append  int32 [batch]: the pend_* row at which the next commit puts its first accepted
  *           row: 0 when the verify before it wrote the folded state back, else that
  *           verify's pending count (written by verify, read by commit).
@@ -255,8 +257,10 @@ int mil_ssm_commit_layers(mil_ssm_cache *const *caches, int32_t n, int32_t K, co
  * ws            caller-owned device workspace of at least mil_ssm_greedy_workspace_bytes
  *               bytes, 256-byte aligned (partial maxima; no state is kept in it).
  * Everything else (x, B, dt, A, D, flags, order, K) is as for mil_ssm_commit, with
- * accepted[b] computed here instead of given; the cache ends up exactly as after
- * mil_ssm_commit with those accepted lengths.
+ * accepted[b] computed here instead of given; the cache ends up as after mil_ssm_commit
+ * with those accepted lengths (the same logical state, pos and pending; the pending rows
+ * past the new count may hold the rejected drafts, which nothing reads).  One launch does
+ * the argmax, the decision and the copies.
  */
 size_t mil_ssm_greedy_workspace_bytes(const mil_ssm_dims *dims, int32_t K, int32_t vocab);
 int mil_ssm_commit_greedy(mil_ssm_cache *cache, int32_t K, const int32_t *draft_tokens,
@@ -364,11 +368,11 @@ enum mil_trace_kernel {
     MIL_TRACE_OFF = 0,
     MIL_TRACE_VERIFY = 1,        /* verify: fold pending rows + K draft outputs */
     MIL_TRACE_FOLD = 2,          /* fold-only pass (commit with MIL_COMMIT_MATERIALIZE, prefill continue) */
-    MIL_TRACE_COMMIT = 3,        /* accepted-length bookkeeping */
+    MIL_TRACE_COMMIT = 3,        /* accepted-length bookkeeping (a greedy commit is MIL_TRACE_ACCEPT) */
     MIL_TRACE_PREFILL_STATE = 4, /* prefill phase 1: per-chunk states */
     MIL_TRACE_PREFILL_PASS = 5,  /* prefill phase 2: sequential pass across chunks */
     MIL_TRACE_PREFILL_OUT = 6,   /* prefill phase 3: per-chunk outputs */
-    MIL_TRACE_ACCEPT = 7,        /* greedy acceptance: vocabulary argmax per draft position */
+    MIL_TRACE_ACCEPT = 7,        /* greedy commit: argmax per draft position, accepted lengths and copies in one launch */
     MIL_TRACE_PREFILL_SCAN = 8   /* prefill in one launch (chunk states, handoff and outputs) */
 };
 

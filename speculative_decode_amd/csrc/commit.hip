@@ -41,8 +41,9 @@ __device__ __forceinline__ void copy_row(char *dst, const char *src, int bytes) 
 
 // grid (K, batch): workgroup (k, b) copies accepted row k of slot b (if k < j); the
 // k = 0 workgroup also does the slot's bookkeeping.  A rejected value (j outside 0..K)
-// is reported in err[b] and leaves pos and the pending rows alone; pending becomes 0
-// because the verify that preceded this commit has already folded the previous rows.
+// is reported in err[b] and leaves pos alone; pending becomes the rows still pending (0
+// after the verify wrote the state back, else its pending count): nothing of this round
+// is kept.
 // The row is read into registers before j is known, so that the two reads overlap
 // instead of the copy waiting for j first (a row past j is read and dropped); rows
 // longer than kCommitRegs vectors per thread copy their remainder afterwards.
@@ -202,12 +203,21 @@ __global__ __launch_bounds__(256) void ssm_commit_tree_kernel(const TreeCommitPa
 // The same commit with the accepted lengths decided on the device (QbitAI walkthrough:
 // keep the drafts the verifier confirms, cut at the first one it rejects; read here as
 // greedy verification, a draft being confirmed when it is the argmax of the verifier's
-// logits at its position).  Two launches:
-//   1. greedy_argmax_kernel, grid (S, K, batch): split s of row (b, k) of the logits
-//      reduces its slice to one 64-bit key, written to ws[b][k][s];
-//   2. greedy_commit_kernel, grid (K, batch): every workgroup of slot b takes the max of
-//      the S keys per position (the argmax token), compares with the drafts, finds the
-//      accepted length j, and then does what ssm_commit_kernel does with it.
+// logits at its position).  One launch, grid (S, K, batch); workgroup (s, k, b):
+//   1. reduces split s of logits row (b, k) to one 64-bit key and publishes it in
+//      ws[b][k][s];
+//   2. counts itself in the slot's arrival word;
+//   3. copies its share (1/S) of draft row k of slot b into the pending area, after the
+//      rows still pending: every draft is copied, and the rows past the accepted ones lie
+//      beyond the new pending count, where nothing reads them;
+//   4. if it was the slot's last workgroup, takes the max of the S keys per position (the
+//      argmax token), compares the drafts with them, finds the accepted length j and does
+//      the slot's bookkeeping.
+// Keys and arrival words cross workgroups through agent-coherent accesses (relaxed
+// agent-scope atomics, which bypass the non-coherent cache levels), and a key's store
+// completes before its workgroup counts itself; the last workgroup sets the word back to
+// 0, so that every call (and every replay of a captured one) starts from zero.  The
+// copies need no ordering: the verify before this commit has finished reading the area.
 // Key = (order-preserving bits of the value) << 32 | (0xFFFFFFFF - index): the largest
 // key is the largest value, ties going to the lowest index, so the result does not depend
 // on how the vocabulary is split or in which order partial maxima meet.  Integer and
@@ -250,38 +260,66 @@ __device__ __forceinline__ uint64_t block_max_key(uint64_t v, uint64_t *sred) {
     return v;
 }
 
-struct ArgmaxParams {
-    const void *logits;  // [batch][K][vocab]
-    uint64_t *part;      // [batch][K][S]
+struct GreedyParams {
+    CommitParams c;          // the drafts' rows, the pending area, pos / pending / append
+    const void *logits;      // [batch][K][vocab]
+    uint64_t *part;          // [batch][K][S] published keys
+    int32_t *arrive;         // slot b's arrival word: arrive[b * arrive_stride]
+    int64_t arrive_stride;
+    const int32_t *draft;    // [batch][K]
+    int32_t *accepted;       // [batch] out
+    int32_t *tokens;         // [batch][K] out, or null
     int64_t vocab;
-    int K, S;
-    int64_t chunk;       // elements per split, a multiple of 8
-    int vec;             // rows start on 16-byte boundaries: 16-byte loads
+    int64_t chunk;           // logits per split, a multiple of 8
+    int S;
+    int vec;                 // logits rows start on 16-byte boundaries: 16-byte loads
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void greedy_argmax_kernel(const ArgmaxParams p) {
+// Share s of S of a row of `bytes` (a multiple of sizeof(V)), one vector per thread per pass.
+template <typename V>
+__device__ __forceinline__ void copy_share(char *dst, const char *src, int bytes, int s, int S) {
+    const V *sv = reinterpret_cast<const V *>(src);
+    V *dv = reinterpret_cast<V *>(dst);
+    const int n = bytes / (int)sizeof(V), per = (n + S - 1) / S, lo = s * per, hi = min(n, lo + per);
+    for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) dv[i] = sv[i];
+}
+
+template <typename T, typename V>
+__global__ __launch_bounds__(256) void greedy_accept_kernel(const GreedyParams g) {
     __shared__ uint64_t sred[4];
-    const int s = blockIdx.x, k = blockIdx.y, b = blockIdx.z;
-    const T *row = static_cast<const T *>(p.logits) + ((int64_t)b * p.K + k) * p.vocab;
-    const int64_t lo = (int64_t)s * p.chunk, hi = min(lo + p.chunk, p.vocab);
+    __shared__ uint64_t skey[MIL_KMAX_LIMIT * kGreedySplitsMax];
+    __shared__ int32_t stok[MIL_KMAX_LIMIT], sdraft[MIL_KMAX_LIMIT];
+    __shared__ int slast;
+    const CommitParams &p = g.c;
+    const int s = blockIdx.x, k = blockIdx.y, b = blockIdx.z, K = p.K, S = g.S;
+    // the slot's draft tokens, read up front by every workgroup (a few bytes), so that the
+    // last one compares them without a global read per position
+    const int32_t mydraft = threadIdx.x < K ? g.draft[(int64_t)b * K + threadIdx.x] : 0;
+    // where this slot's rows of the round go: 0 when the verify wrote the state back, else
+    // its pending count (at most k_max - K by the verify's rule; clamped so that no value
+    // in the buffer can place a row outside the area)
+    const int base = min(max(p.append[b], 0), p.k_max - K);
+
+    // ---- 1. this split's largest logit, as a key ----
+    const T *row = static_cast<const T *>(g.logits) + ((int64_t)b * K + k) * g.vocab;
+    const int64_t lo = (int64_t)s * g.chunk, hi = min(lo + g.chunk, g.vocab);
     // this thread's largest value (order-preserving bits) and its index; each thread walks
     // its indices upwards and keeps a value only when strictly larger, so the lowest index
     // of equal values stays
     uint32_t bo = 0, bi = 0xFFFFFFFFu;
     int64_t tail = lo;
-    if (p.vec) {
+    if (g.vec) {
         constexpr int E = 16 / sizeof(T);  // lo is a multiple of 8, so of E
         constexpr int U = 4;               // 16-byte loads in flight per thread
         const uint4 *row4 = reinterpret_cast<const uint4 *>(row);
         const int64_t v0 = lo / E, v1 = hi / E;
-        for (int64_t base = v0 + threadIdx.x; base < v1; base += 256 * U) {
+        for (int64_t base4 = v0 + threadIdx.x; base4 < v1; base4 += 256 * U) {
             uint4 w[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) w[u] = row4[min(base + u * 256, v1 - 1)];
+            for (int u = 0; u < U; ++u) w[u] = row4[min(base4 + u * 256, v1 - 1)];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t i = base + u * 256;
+                const int64_t i = base4 + u * 256;
                 if (i < v1) {
 #pragma unroll
                     for (int q = 0; q < E; ++q) {
@@ -304,26 +342,38 @@ __global__ __launch_bounds__(256) void greedy_argmax_kernel(const ArgmaxParams p
         }
     }
     const uint64_t best = block_max_key(argmax_key(bo, bi), sred);
-    if (threadIdx.x == 0) p.part[((int64_t)b * p.K + k) * p.S + s] = best;
-}
 
-struct GreedyParams {
-    CommitParams c;
-    const uint64_t *part;   // [batch][K][S]
-    const int32_t *draft;   // [batch][K]
-    int32_t *accepted;      // [batch] out
-    int32_t *tokens;        // [batch][K] out, or null
-    int S;
-};
-
-template <typename V>
-__global__ __launch_bounds__(256) void greedy_commit_kernel(const GreedyParams g) {
-    __shared__ uint64_t skey[MIL_KMAX_LIMIT * kGreedySplitsMax];
-    __shared__ int32_t stok[MIL_KMAX_LIMIT];
-    __shared__ int sj;
-    const CommitParams &p = g.c;
-    const int k = blockIdx.x, b = blockIdx.y, K = p.K, S = g.S;
-    for (int i = threadIdx.x; i < K * S; i += blockDim.x) skey[i] = g.part[(int64_t)b * K * S + i];
+    // ---- 2. publish the key and count in (the key's store complete first: the wait comes
+    // before the copies below, which need no order, so it does not wait for them) ----
+    int32_t *arrive = g.arrive + (size_t)b * g.arrive_stride;
+    const size_t src = (size_t)b * K + k, dst = (size_t)b * p.k_max + base + k;
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(g.part + src * S + s, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        slast = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == K * S - 1;
+    }
+    // ---- 3. this split's share of draft row k, after the rows still pending: at once in
+    // every workgroup but the slot's last, which copies after deciding (its key reads would
+    // otherwise wait behind these stores) ----
+    auto copy = [&]() {
+        copy_share<V>(p.px + dst * p.x_row, p.x + src * p.x_row, p.x_row, s, S);
+        copy_share<V>(p.pB + dst * p.B_row, p.B + src * p.B_row, p.B_row, s, S);
+        if (s == 0) {
+            const uint16_t *ds = reinterpret_cast<const uint16_t *>(p.dt + src * p.dt_row);
+            uint16_t *dd = reinterpret_cast<uint16_t *>(p.pdt + dst * p.dt_row);
+            for (int i = threadIdx.x; i < p.dt_row / 2; i += blockDim.x) dd[i] = ds[i];
+        }
+    };
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // slast is visible
+    if (!slast) {
+        copy();
+        return;
+    }
+    // ---- 4. the slot's last workgroup decides ----
+    if (threadIdx.x == 0) __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < K * S; i += blockDim.x)
+        skey[i] = __hip_atomic_load(g.part + (size_t)b * K * S + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < K) sdraft[threadIdx.x] = mydraft;
     __syncthreads();
     if (threadIdx.x < K) {
         uint64_t m = 0;
@@ -333,30 +383,13 @@ __global__ __launch_bounds__(256) void greedy_commit_kernel(const GreedyParams g
     __syncthreads();
     if (threadIdx.x == 0) {
         int j = 0;
-        while (j < K && g.draft[(int64_t)b * K + j] == stok[j]) ++j;
-        sj = j;
+        while (j < K && sdraft[j] == stok[j]) ++j;
+        g.accepted[b] = j;
+        p.pending[b] = base + j;
+        p.pos[b] += j;
     }
-    __syncthreads();
-    const int j = sj;
-    // 0 when the verify wrote the state back, else its pending count (at most k_max - K by
-    // the verify's rule; clamped so that no value in the buffer can place a row outside it)
-    const int base = min(max(p.append[b], 0), p.k_max - p.K);
-    if (k == 0) {
-        if (threadIdx.x == 0) {
-            g.accepted[b] = j;
-            p.pending[b] = base + j;
-            p.pos[b] += j;
-        }
-        if (g.tokens && threadIdx.x < K) g.tokens[(int64_t)b * K + threadIdx.x] = stok[threadIdx.x];
-    }
-    if (k >= j) return;
-    const size_t src = (size_t)b * K + k, dst = (size_t)b * p.k_max + base + k;
-    copy_row<V>(p.px + dst * p.x_row, p.x + src * p.x_row, p.x_row);
-    copy_row<V>(p.pB + dst * p.B_row, p.B + src * p.B_row, p.B_row);
-    const char *ds = p.dt + src * p.dt_row;
-    char *dd = p.pdt + dst * p.dt_row;
-    for (int i = threadIdx.x; i < p.dt_row / 2; i += blockDim.x)
-        reinterpret_cast<uint16_t *>(dd)[i] = reinterpret_cast<const uint16_t *>(ds)[i];
+    if (g.tokens && threadIdx.x < K) g.tokens[(int64_t)b * K + threadIdx.x] = stok[threadIdx.x];
+    copy();
 }
 
 __global__ void clear_pending_kernel(int32_t *pending, int batch) {
@@ -506,36 +539,36 @@ hipError_t launch_commit_greedy(const CacheImpl &c, int K, const int32_t *draft,
     const int batch = c.dims.batch;
     const int S = greedy_splits(batch, K, vocab);
     const int le = logits_dtype == MIL_BF16 ? 2 : 4;
-    ArgmaxParams a;
-    a.logits = logits;
-    a.part = static_cast<uint64_t *>(ws);
-    a.vocab = vocab;
-    a.K = K;
-    a.S = S;
-    a.chunk = ((vocab + S - 1) / S + 7) / 8 * 8;
-    a.vec = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && ((int64_t)vocab * le % 16 == 0);
-    trace_begin(c, MIL_TRACE_ACCEPT, s);
-    if (logits_dtype == MIL_BF16)
-        hipLaunchKernelGGL(greedy_argmax_kernel<uint16_t>, dim3(S, K, batch), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(greedy_argmax_kernel<float>, dim3(S, K, batch), dim3(256), 0, s, a);
-    trace_end(c, MIL_TRACE_ACCEPT, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     GreedyParams g;
     g.c = commit_params(c, K, nullptr, x, B, dt);
-    g.part = a.part;
+    g.logits = logits;
+    g.part = static_cast<uint64_t *>(ws);
+    // slot b's arrival word: a spare word of its first prefill handoff row (head 0, slab 0)
+    g.arrive = cache_scan(c) + kGreedyArriveWord;
+    g.arrive_stride = (int64_t)c.dims.nheads * kScanSlabs * kScanRow;
     g.draft = draft;
     g.accepted = accepted;
     g.tokens = tokens;
+    g.vocab = vocab;
     g.S = S;
+    g.chunk = ((vocab + S - 1) / S + 7) / 8 * 8;
+    g.vec = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && ((int64_t)vocab * le % 16 == 0);
+    // draft rows copied 16 bytes at a time when x and B are 16-byte aligned
     const bool v16 = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-    trace_begin(c, MIL_TRACE_COMMIT, s);
-    if (v16)
-        hipLaunchKernelGGL(greedy_commit_kernel<uint4>, dim3(K, batch), dim3(256), 0, s, g);
-    else
-        hipLaunchKernelGGL(greedy_commit_kernel<uint32_t>, dim3(K, batch), dim3(256), 0, s, g);
-    trace_end(c, MIL_TRACE_COMMIT, s);
+    const dim3 grid(S, K, batch);
+    trace_begin(c, MIL_TRACE_ACCEPT, s);
+    if (logits_dtype == MIL_BF16) {
+        if (v16)
+            hipLaunchKernelGGL((greedy_accept_kernel<uint16_t, uint4>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((greedy_accept_kernel<uint16_t, uint32_t>), grid, dim3(256), 0, s, g);
+    } else {
+        if (v16)
+            hipLaunchKernelGGL((greedy_accept_kernel<float, uint4>), grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((greedy_accept_kernel<float, uint32_t>), grid, dim3(256), 0, s, g);
+    }
+    trace_end(c, MIL_TRACE_ACCEPT, s);
     return hipGetLastError();
 }
 

@@ -54,6 +54,9 @@ constexpr int kScanSlabs = 8;
 constexpr int kScanChunks = 64;  // chunks per launch of the single-launch prefill (longer prompts: more launches)
 constexpr int kScanRow = kScanChunks + 4;  // words per (slot, head, slab) row: flags, epoch, pad
 constexpr int kScanEpoch = kScanChunks;    // index of the epoch word in a row
+// the next word of each slot's first row (head 0, slab 0): the arrival count of a greedy
+// commit's workgroups for that slot, 0 between calls (the last arrival resets it)
+constexpr int kGreedyArriveWord = kScanEpoch + 1;
 inline int32_t *cache_scan(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.scan_off); }
 inline int32_t *cache_append(const CacheImpl &c) { return reinterpret_cast<int32_t *>(c.base + c.lay.append_off); }
 inline int elt_bytes(int32_t dtype) { return dtype == MIL_BF16 ? 2 : 4; }
