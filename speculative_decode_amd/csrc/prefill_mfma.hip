@@ -759,21 +759,15 @@ constexpr size_t kLdsMax = 160 * 1024;
 constexpr int kScanQ = 256;  // the single-launch kernel's chunk length
 
 // LDS of the single-launch kernel: the staged B rows and X^T, seven per-token float
-// arrays, the tile totals, the 8 x 8 tile factors and a counter; then an area that first
-// holds the partial chunk-state tiles of the token parts that their owners add (one
-// 32 x 32 fp32 tile per part other than the owner's, per state tile) and later the
-// carried state's hi / lo rows.
+// arrays, the tile totals, the 8 x 8 tile factors and a counter; then the carried state's
+// hi / lo rows for C h_in.
 constexpr size_t scan_base_lds(int Q, int N, int PC) {
     return ((size_t)Q * (N + 8) + (size_t)PC * (Q + 8)) * 2 + 7 * (size_t)Q * 4 + 8 * 4 + 64 * 4 + 16;
 }
-constexpr size_t scan_xchg_bytes(int N, int PC) {
-    return (size_t)(PC / kT) * (8 / (N / kT) - 1) * (N / kT) * kT * kT * 4 > (size_t)PC * (N * 2 + 8) * 2
-               ? (size_t)(PC / kT) * (8 / (N / kT) - 1) * (N / kT) * kT * kT * 4
-               : (size_t)PC * (N * 2 + 8) * 2;
-}
-constexpr bool scan_split_tokens(int N, int PC) {
-    return scan_base_lds(kScanQ, N, PC) + scan_xchg_bytes(N, PC) <= kLdsMax;
-}
+constexpr size_t scan_xchg_bytes(int N, int PC) { return (size_t)PC * (N * 2 + 8) * 2; }
+// Slabs too wide for a separate carried-state area stage it in X^T's area instead, once
+// every wave is done with X (one more barrier).
+constexpr bool scan_wide(int N, int PC) { return scan_base_lds(kScanQ, N, PC) + scan_xchg_bytes(N, PC) > kLdsMax; }
 
 // The published chunk states are moved 16 bytes per lane with the same cache bypass
 // (sc1) that the relaxed agent-scope atomics above use, four registers at a time.  A tile's
@@ -935,128 +929,6 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     const float Ec = __expf(ttot);
     __syncthreads();
 
-    // ---- the chunk's own state S[n][p] (this slab): S = sum_s (w_s B_s) x_s^T with
-    // A operand (w B)^T and B operand X^T (as staged).  The rows n of B^T come off the
-    // matrix cores: the product D = B_blk E with E the identity holds, per lane, one
-    // column n of a 32-token block over 16 tokens (registers r: tokens 8(r/4) + 4hf + r%4),
-    // which is the A-operand layout once scaled by w_s and split hi + lo.  The waves
-    // sharing a row tile take consecutive parts of the tokens (when LDS has room to add
-    // their partial tiles), each part over every column tile, then the partials are added
-    // in part order; otherwise each wave covers all tokens for the tiles it owns.
-    // Wave w owns tiles tl = w + 8i (row tile w % NTL, column tile tl / NTL). ----
-    static_assert(scan_split_tokens(N, PC), "the single launch splits each row tile's tokens over its waves");
-    constexpr int SP = 8 / NTL;    // token parts: the waves of one row tile
-    const int snt = wave % NTL;    // this wave's row tile
-    const int jpart = wave / NTL;  // its token part
-    f32x16 part[PT];
-#pragma unroll
-    for (int i = 0; i < PT; ++i) part[i] = f32x16{};
-    {
-        bf16x8 eye[2];  // identity: slot v of k-step kk is 1 where 16 kk + 8 hf + v = l32
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int v = 0; v < 8; ++v) eye[kk][v] = static_cast<bf16>(16 * kk + 8 * hf + v == l32 ? 1.f : 0.f);
-        // every block of the part, unrolled and without a branch; blocks past a short
-        // chunk's end add exact zeros (their B rows, X columns and weights were zeroed when
-        // staged).  Software pipeline: a block's LDS operands are read two blocks ahead and
-        // its identity products issued one block ahead, so that neither the LDS latency
-        // nor the products' latency is waited for where the values are used.
-        constexpr int BPP = (kScanQ / kT) / SP;
-        struct Ops {
-            bf16x8 bo[2];       // B rows of the block (A operand of the identity products)
-            float4 wq[4];       // w_s of the lane's 16 tokens
-            bf16x8 xv[PT][2];   // X operands of the block's products
-        };
-        auto fetch = [&](int b, Ops &o) {
-            const int s0 = (jpart * BPP + b) * kT;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                o.bo[kk] = *reinterpret_cast<const bf16x8 *>(sB + (s0 + l32) * BS + snt * kT + kk * 16 + 8 * hf);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o.wq[q] = *reinterpret_cast<const float4 *>(sWst + s0 + 8 * q + 4 * hf);
-            load_x<PT>(o.xv, sXT + l32 * XS + s0 + 4 * hf, XS);
-        };
-        auto ident = [&](const Ops &o) {
-            f32x16 tb = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) tb = mfma(o.bo[kk], eye[kk], tb);
-            return tb;
-        };
-        Ops o0, o1;
-        fetch(0, o0);
-        if (BPP > 1) fetch(1, o1);
-        f32x16 tb = ident(o0);
-#pragma unroll
-        for (int b = 0; b < BPP; ++b) {
-            const f32x16 tbn = b + 1 < BPP ? ident(o1) : f32x16{};
-            f32x16 mv;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float wv[4] = {o0.wq[q].x, o0.wq[q].y, o0.wq[q].z, o0.wq[q].w};
-#pragma unroll
-                for (int u2 = 0; u2 < 4; ++u2) mv[4 * q + u2] = tb[4 * q + u2] * wv[u2];
-            }
-            bf16x8 ah[2], al[2];
-            split16(mv, ah, al);
-            mx_products<PT>(part, ah, al, o0.xv);
-            o0 = o1;
-            if (b + 2 < BPP) fetch(b + 2, o1);
-            __builtin_amdgcn_sched_barrier(0);
-            tb = tbn;
-        }
-    }
-    // ---- the chunk's state tiles belong to the four light waves (w < 4: the waves with
-    // the short causal rows of the intra-chunk products), which publish them and raise
-    // the chunk's flag while the other four run their longer rows: tile (row tile snt,
-    // column tile pt) to wave snt + NTL (pt % LW), as its tile i = pt / LW.  The other
-    // token parts' partial tiles go through LDS, and the owner adds the parts in token
-    // order. ----
-    constexpr int LW = 4 / NTL;                   // token parts held by light waves
-    constexpr int TPWL = PT >= LW ? PT / LW : 1;  // tiles per owning wave
-    const bool light = wave < 4;
-    const bool owner = light && jpart < PT;
-    float *sXg = reinterpret_cast<float *>(lds + scan_base_lds(Q, N, PC));
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-        const int own = pt % LW;
-        if (jpart != own) {
-            const int xs = (pt * (SP - 1) + (jpart - own - 1 + SP) % SP) * NTL + snt;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sXg[(xs * 16 + r) * 64 + lane] = part[pt][r];
-        }
-    }
-    __syncthreads();
-    f32x16 sacc[TPWL];
-#pragma unroll
-    for (int i = 0; i < TPWL; ++i) sacc[i] = f32x16{};
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-        const int own = pt % LW;
-        if (jpart == own) {
-            f32x16 sum = f32x16{};
-#pragma unroll
-            for (int j = 0; j < SP; ++j) {
-                if (j == own) {
-                    sum = j == 0 ? part[pt] : sum + part[pt];
-                } else {
-                    const int xs = (pt * (SP - 1) + (j - own - 1 + SP) % SP) * NTL + snt;
-                    f32x16 v;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) v[r] = sXg[(xs * 16 + r) * 64 + lane];
-                    sum = j == 0 ? v : sum + v;
-                }
-            }
-            sacc[pt / LW] = sum;
-        }
-    }
-
-    // ---- publish.  Each chunk's record holds its own contribution S_c with its decay E_c
-    // (the aggregate) and, once known, the state after the chunk (inclusive).  Chunk 0 has
-    // its inclusive state at once, E_0 h0 + S_0 (it alone reads h0); later chunks publish
-    // their aggregate now and their inclusive state after the look-back below.  Each light
-    // wave waits for its own stores, then counts itself in LDS; the fourth raises the flag.
-    // The last chunk publishes nothing: nothing waits for it. ----
     const int slot = p.slot0 + seq;
     const size_t REC = 2 * (size_t)N * PC + 16;  // floats per chunk record: S_c tiles, E_c (16), inclusive tiles
     const size_t INC = (size_t)N * PC + 16;      // offset of the inclusive tiles in a record
@@ -1066,13 +938,150 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     float *cache = p.state + (size_t)(seq * H + h) * p.head_stride;
     const bool has_hin = p.cont || c > 0;
     const bool last = c == p.nch - 1;
+
+    // ---- the chunk's own state S[n][p] (this slab): S = sum_s (w_s B_s) x_s^T with
+    // A operand (w B)^T and B operand X^T (as staged).  The rows n of B^T come off the
+    // matrix cores: the product D = B_blk E with E the identity holds, per lane, one
+    // column n of a 32-token block over 16 tokens (registers r: tokens 8(r/4) + 4hf + r%4),
+    // which is the A-operand layout once scaled by w_s and split hi + lo.  The state tiles
+    // belong to the four light waves (w < 4: the waves with the short causal rows of the
+    // intra-chunk products): tile (row tile snt, column tile pt) to wave snt + NTL (pt % LW),
+    // as its tile i = pt / LW.  Each owner forms its tiles over all the chunk's tokens in
+    // token order, so the other four waves go straight to their longer rows and no partial
+    // tiles cross waves.  They publish the tiles and raise the chunk's flag. ----
+    constexpr int LW = 4 / NTL;                   // light waves per row tile
+    constexpr int TPWL = PT >= LW ? PT / LW : 1;  // tiles per owning wave
+    const int snt = wave % NTL;                   // this wave's row tile (light waves)
+    const int jpart = wave / NTL;                 // light waves: first owned column tile
+    const bool light = wave < 4;
+    const bool owner = light && jpart < PT;
+    constexpr bool kWide = scan_wide(N, PC);
+    static_assert(!kWide || 2 * N + 8 <= kScanQ + 8, "the carried state's rows fit in X^T's");
+    // the carried state's rows: their own area, or X^T's once the intra-chunk rows are done
+    bf16 *sH = kWide ? sXT : reinterpret_cast<bf16 *>(lds + scan_base_lds(Q, N, PC));
+    f32x16 sacc[TPWL];
+#pragma unroll
+    for (int i = 0; i < TPWL; ++i) sacc[i] = f32x16{};
+    // The wide form forms its tiles two at a time (the identity products are repeated per
+    // pair) and publishes each pair at once, so that fewer registers are in flight.
+    constexpr int CSG = kWide ? 2 : TPWL;  // tiles formed together
+    if (owner) {
+        bf16x8 eye[2];  // identity: slot v of k-step kk is 1 where 16 kk + 8 hf + v = l32
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) eye[kk][v] = static_cast<bf16>(16 * kk + 8 * hf + v == l32 ? 1.f : 0.f);
+#pragma unroll
+        for (int g0 = 0; g0 < TPWL; g0 += CSG) {
+            f32x16 pacc[CSG];
+#pragma unroll
+            for (int ii = 0; ii < CSG; ++ii) pacc[ii] = f32x16{};
+            // every block of the chunk, unrolled and without a branch; blocks past a short
+            // chunk's end add exact zeros (their B rows, X columns and weights were zeroed
+            // when staged).  Software pipeline: a block's LDS operands are read two blocks
+            // ahead and its identity products issued one block ahead, so that neither the LDS
+            // latency nor the products' latency is waited for where the values are used.
+            constexpr int NB = kScanQ / kT;
+            struct Ops {
+                bf16x8 bo[2];        // B rows of the block (A operand of the identity products)
+                float4 wq[4];        // w_s of the lane's 16 tokens
+                bf16x8 xv[CSG][2];   // X operands of the block's products, owned column tiles
+            };
+            auto fetch = [&](int b, Ops &o) {
+                const int s0 = b * kT;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    o.bo[kk] = *reinterpret_cast<const bf16x8 *>(sB + (s0 + l32) * BS + snt * kT + kk * 16 + 8 * hf);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o.wq[q] = *reinterpret_cast<const float4 *>(sWst + s0 + 8 * q + 4 * hf);
+#pragma unroll
+                for (int ii = 0; ii < CSG; ++ii)
+                    load_x<1>(&o.xv[ii], sXT + ((jpart + LW * (g0 + ii)) * kT + l32) * XS + s0 + 4 * hf, XS);
+            };
+            auto ident = [&](const Ops &o) {
+                f32x16 tb = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) tb = mfma(o.bo[kk], eye[kk], tb);
+                return tb;
+            };
+            Ops o0, o1;
+            fetch(0, o0);
+            fetch(1, o1);
+            f32x16 tb = ident(o0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const f32x16 tbn = b + 1 < NB ? ident(o1) : f32x16{};
+                f32x16 mv;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float wv[4] = {o0.wq[q].x, o0.wq[q].y, o0.wq[q].z, o0.wq[q].w};
+#pragma unroll
+                    for (int u2 = 0; u2 < 4; ++u2) mv[4 * q + u2] = tb[4 * q + u2] * wv[u2];
+                }
+                bf16x8 ah[2], al[2];
+                split16(mv, ah, al);
+                mx_products<CSG>(pacc, ah, al, o0.xv);
+                o0 = o1;
+                if (b + 2 < NB) fetch(b + 2, o1);
+                __builtin_amdgcn_sched_barrier(0);
+                tb = tbn;
+            }
+            if constexpr (kWide) {
+                // publish the pair.  Chunks c > 0: S_c in the record's aggregate area (read
+                // back when needed).  Chunk 0: its inclusive state E_0 h0 + S_0 (also when it is
+                // the last: it is then the final state), and h0 in the aggregate area, which no
+                // look-back reads for chunk 0 (the cache itself may hold the final state by the
+                // time chunk 0 needs h0 again).
+#pragma unroll
+                for (int ii = 0; ii < CSG; ++ii) {
+                    const int pt = jpart + LW * (g0 + ii);
+                    const int tl = snt + NTL * pt;
+                    f32x16 h0 = f32x16{};
+                    if (c == 0 && p.cont) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                            h0[r] = cache[(size_t)n * P + pc0 + pt * kT + l32];
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f32x4 v, s4;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            s4[u] = pacc[ii][4 * q + u];
+                            v[u] = __builtin_fmaf(Ec, h0[4 * q + u], pacc[ii][4 * q + u]);
+                        }
+                        if (c == 0) {
+                            const f32x4 h4 = {h0[4 * q], h0[4 * q + 1], h0[4 * q + 2], h0[4 * q + 3]};
+                            if (p.cont)
+                                shared_store4(agr, (int)(((size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), h4);
+                            shared_store4(agr, (int)((INC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
+                        } else {
+                            shared_store4(agr, (int)(((size_t)c * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), s4);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int ii = 0; ii < CSG; ++ii) sacc[g0 + ii] = pacc[ii];
+            }
+        }
+    }
+
+    // ---- publish.  Each chunk's record holds its own contribution S_c with its decay E_c
+    // (the aggregate) and, once known, the state after the chunk (inclusive).  Chunk 0 has
+    // its inclusive state at once, E_0 h0 + S_0 (it alone reads h0); later chunks publish
+    // their aggregate now and their inclusive state after the look-back below.  Each light
+    // wave waits for its own stores, then counts itself in LDS; the fourth raises the flag.
+    // The last chunk publishes nothing: nothing waits for it. ----
     int *sCnt = reinterpret_cast<int *>(sMid + 64);  // light waves past the first publication
     int *sCnt2 = sCnt + 1;                            // owning waves past the inclusive publication
     constexpr int NOWN = NTL * (PT < LW ? PT : LW);   // owning waves
     f32x16 hin[TPWL];
 #pragma unroll
     for (int i = 0; i < TPWL; ++i) hin[i] = f32x16{};
-    if (c == 0 && p.cont && owner) {
+    if (!kWide && c == 0 && p.cont && owner) {
 #pragma unroll
         for (int i = 0; i < TPWL; ++i) {
             const int pt = jpart + LW * i;
@@ -1084,9 +1093,10 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
     }
     if (light) {
-        if (!last) {
+        // (the wide form stored its tiles as it formed them)
+        if (!last || kWide) {
             const size_t base = (size_t)c * REC + (c == 0 ? INC : 0);
-            if (owner) {
+            if (!kWide && owner) {
 #pragma unroll
                 for (int i = 0; i < TPWL; ++i) {
                     const int tl = snt + NTL * (jpart + LW * i);
@@ -1103,7 +1113,6 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             if (c > 0 && tid == 0) shared_store(recs + (size_t)c * REC + (size_t)N * PC, Ec);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
         }
-        // this wave has also read its partial tiles: the exchange area is free of it
         if (lane == 0) {
             const int before = atomicAdd(sCnt, 1);
             if (!last && before == 3)
@@ -1192,6 +1201,20 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     // j0+1..c-1 in order, h <- E_j h + S_j.  Every inclusive record is that same fold in
     // the same order, back to chunk 0's E_0 h0 + S_0, so h_in is bit for bit the state of
     // a sequential pass over the chunks, whichever j0 the wait ends at. ----
+    // the wide form's chunk 0 reads h0 again here, from where it parked it (no registers
+    // held through the rows)
+    if (kWide && c == 0 && owner) {
+#pragma unroll
+        for (int i = 0; i < TPWL; ++i) {
+            const int tl = snt + NTL * (jpart + LW * i);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = p.cont ? shared_load4(agr, (int)(((size_t)tl * 1024 + (q * 64 + lane) * 4) * 4)) : f32x4{};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) hin[i][4 * q + u] = v[u];
+            }
+        }
+    }
     if (c > 0 && owner) {
         const long long tw0 = (long long)__builtin_amdgcn_s_memrealtime();
         int j0 = 0;
@@ -1221,47 +1244,52 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         asm volatile("" ::: "memory");  // the records are read after the flags
         // j0's inclusive tiles, then the aggregates j0+1..c-1, the next one's loads (clamped
         // to the last, so that no branch makes the compiler wait for every load) in flight
-        // while one is folded in
-        f32x16 nx[TPWL];
-        float en = 0.f;
-        const int ja = min(j0 + 1, c - 1);
+        // while one is folded in; the wide form walks the records once per pair of tiles
+        // (fewer registers in flight)
+        constexpr int LBG = kWide ? 2 : TPWL;  // tiles folded together
 #pragma unroll
-        for (int i = 0; i < TPWL; ++i) {
-            const int tl = snt + NTL * (jpart + LW * i);
+        for (int g0 = 0; g0 < TPWL; g0 += LBG) {
+            f32x16 nx[LBG];
+            float en = 0.f;
+            const int ja = min(j0 + 1, c - 1);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int lo = (q * 64 + lane) * 4 + tl * 1024;
-                const f32x4 v = shared_load4(agr, (int)(((size_t)j0 * REC + INC + lo) * 4));
-                const f32x4 a = shared_load4(agr, (int)(((size_t)ja * REC + lo) * 4));
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    hin[i][4 * q + u] = v[u];
-                    nx[i][4 * q + u] = a[u];
-                }
-            }
-        }
-        en = shared_load(recs + (size_t)ja * REC + (size_t)N * PC);
-        for (int j = j0 + 1; j < c; ++j) {
-            f32x16 cur[TPWL];
-#pragma unroll
-            for (int i = 0; i < TPWL; ++i) cur[i] = nx[i];
-            const float e = en;
-            const int jn = min(j + 1, c - 1);
-            en = shared_load(recs + (size_t)jn * REC + (size_t)N * PC);
-#pragma unroll
-            for (int i = 0; i < TPWL; ++i) {
-                const int tl = snt + NTL * (jpart + LW * i);
+            for (int ii = 0; ii < LBG; ++ii) {
+                const int tl = snt + NTL * (jpart + LW * (g0 + ii));
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = shared_load4(agr, (int)(((size_t)jn * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+                    const int lo = (q * 64 + lane) * 4 + tl * 1024;
+                    const f32x4 v = shared_load4(agr, (int)(((size_t)j0 * REC + INC + lo) * 4));
+                    const f32x4 a = shared_load4(agr, (int)(((size_t)ja * REC + lo) * 4));
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) nx[i][4 * q + u] = v[u];
+                    for (int u = 0; u < 4; ++u) {
+                        hin[g0 + ii][4 * q + u] = v[u];
+                        nx[ii][4 * q + u] = a[u];
+                    }
                 }
             }
+            en = shared_load(recs + (size_t)ja * REC + (size_t)N * PC);
+            for (int j = j0 + 1; j < c; ++j) {
+                f32x16 cur[LBG];
 #pragma unroll
-            for (int i = 0; i < TPWL; ++i)
+                for (int ii = 0; ii < LBG; ++ii) cur[ii] = nx[ii];
+                const float e = en;
+                const int jn = min(j + 1, c - 1);
+                en = shared_load(recs + (size_t)jn * REC + (size_t)N * PC);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) hin[i][r] = __builtin_fmaf(e, hin[i][r], cur[i][r]);
+                for (int ii = 0; ii < LBG; ++ii) {
+                    const int tl = snt + NTL * (jpart + LW * (g0 + ii));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v = shared_load4(agr, (int)(((size_t)jn * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) nx[ii][4 * q + u] = v[u];
+                    }
+                }
+#pragma unroll
+                for (int ii = 0; ii < LBG; ++ii)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) hin[g0 + ii][r] = __builtin_fmaf(e, hin[g0 + ii][r], cur[ii][r]);
+            }
         }
         // the state after this chunk, E_c h_in + S_c, for the chunks after it
         if (!last) {
@@ -1271,8 +1299,10 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     f32x4 v;
+                    const f32x4 s4 = kWide ? shared_load4(agr, (int)(((size_t)c * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4))
+                                           : f32x4{sacc[i][4 * q], sacc[i][4 * q + 1], sacc[i][4 * q + 2], sacc[i][4 * q + 3]};
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = __builtin_fmaf(Ec, hin[i][4 * q + u], sacc[i][4 * q + u]);
+                    for (int u = 0; u < 4; ++u) v[u] = __builtin_fmaf(Ec, hin[i][4 * q + u], s4[u]);
                     shared_store4(agr, (int)(((size_t)c * REC + INC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
                 }
             }
@@ -1292,10 +1322,24 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
 #pragma unroll
         for (int i = 0; i < TPWL; ++i) {
             const int pt = jpart + LW * i;
+            f32x16 sc;
+            if constexpr (kWide) {
+                // chunk 0: its inclusive record is the final state; later chunks: S_c
+                const int tl = snt + NTL * pt;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = shared_load4(agr, (int)(((size_t)c * REC + (c == 0 ? INC : 0) + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) sc[4 * q + u] = v[u];
+                }
+            } else {
+                sc = sacc[i];
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                cache[(size_t)n * P + pc0 + pt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
+                cache[(size_t)n * P + pc0 + pt * kT + l32] =
+                    (kWide && c == 0) ? sc[r] : __builtin_fmaf(Ec, hin[i][r], sc[r]);
             }
         }
     }
@@ -1310,14 +1354,9 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         return;
     }
     if (has_hin) {
-        // the carried state as [p][n] groups of 8 hi + 8 lo bf16, in the exchange area once
-        // all four light waves have counted themselves out of it
-        bf16 *sH = reinterpret_cast<bf16 *>(sXg);
+        // the carried state as [p][n] groups of 8 hi + 8 lo bf16
+        if constexpr (kWide) __syncthreads();  // every wave is done with X^T
         if (owner) {
-            for (int spin = 0; spin < (1 << 20); ++spin) {
-                if (__hip_atomic_load(sCnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
-                __builtin_amdgcn_s_sleep(1);
-            }
 #pragma unroll
             for (int i = 0; i < TPWL; ++i) {
                 const int pt = jpart + LW * i;
@@ -1381,7 +1420,9 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     }
 }
 
-size_t scan_lds_bytes(int Q, int N, int P) { return scan_base_lds(Q, N, P) + scan_xchg_bytes(N, P); }
+size_t scan_lds_bytes(int Q, int N, int P) {
+    return scan_base_lds(Q, N, P) + (scan_wide(N, P) ? 0 : scan_xchg_bytes(N, P));
+}
 
 size_t out_lds_bytes(int Q, int N, int P) {
     const size_t big = std::max((size_t)Q * (N + 8) + (size_t)P * (Q + 8), (size_t)P * (N * 2 + 8)) * 2;
@@ -1399,9 +1440,12 @@ int slab_width(int nseq, int nch, int H, int P) {
     return pc;
 }
 
-// Column slab width of the single launch: the output work's, at most 64 columns (wider
-// slabs leave no LDS for adding the token parts of the chunk state).
-int scan_slab(int nseq, int nch, int H, int P) { return std::min(slab_width(nseq, nch, H, P), 64); }
+// Column slab width of the single launch: the output work's, at most 128 columns where
+// N = 128 (the wide form: one workgroup forms each C B^T tile and its decay mask for all
+// 128 columns, and the carried state reuses X^T's LDS) and 64 otherwise.
+int scan_slab(int nseq, int nch, int H, int P, int N) {
+    return std::min(slab_width(nseq, nch, H, P), N == 128 ? 128 : 64);
+}
 
 // The single-launch kernel for these sizes, or null (its LDS does not fit, or a chunk other
 // than 256 tokens, which it is not built for).  One launch covers at most kScanChunks
@@ -1411,6 +1455,7 @@ const void *scan_kernel(int chunk, int N, int pc) {
 #define MIL_SCAN_CASE(n, pp) \
     if (N == n && pc == pp) return reinterpret_cast<const void *>(chunk_scan_mfma<n, pp>);
     MIL_SCAN_CASE(64, 32) MIL_SCAN_CASE(64, 64) MIL_SCAN_CASE(128, 32) MIL_SCAN_CASE(128, 64)
+    MIL_SCAN_CASE(128, 128)
 #undef MIL_SCAN_CASE
     return nullptr;
 }
@@ -1420,7 +1465,7 @@ const void *scan_kernel(int chunk, int N, int pc) {
 bool prefill_single_launch(int nseq, int L, int chunk, int H, int P, int N) {
     if (!prefill_mfma_supported(chunk, N, P)) return false;
     const int nch = (L + chunk - 1) / chunk;
-    return scan_kernel(chunk, N, scan_slab(nseq, std::min(nch, kScanChunks), H, P)) != nullptr;
+    return scan_kernel(chunk, N, scan_slab(nseq, std::min(nch, kScanChunks), H, P, N)) != nullptr;
 }
 
 // Shapes the matrix-core path covers: bf16 inputs, N and P multiples of 32 up to 256,
@@ -1478,7 +1523,7 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     // one launch for all three phases where its LDS fits (chunks of 256, 8 waves), per run
     // of at most kScanChunks chunks: each later launch continues from the state the one
     // before it wrote to the cache, and the last one does the slots' bookkeeping
-    if (scan_kernel(chunk, p.N, scan_slab(nseq, std::min(p.nch, kScanChunks), p.H, p.P))) {
+    if (scan_kernel(chunk, p.N, scan_slab(nseq, std::min(p.nch, kScanChunks), p.H, p.P, p.N))) {
         const int nch_all = p.nch;
         p.scan = cache_scan(c);
         p.err = cache_err(c);
@@ -1489,7 +1534,7 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
             p.t0 = c0 * chunk;
             p.cont = (cont || c0 > 0) ? 1 : 0;
             p.book = c0 + p.nch == nch_all ? 1 : 0;
-            const int spc = scan_slab(nseq, p.nch, p.H, p.P);
+            const int spc = scan_slab(nseq, p.nch, p.H, p.P, p.N);
             const void *kf = scan_kernel(chunk, p.N, spc);
             if (!kf) return hipErrorInvalidValue;
             hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);

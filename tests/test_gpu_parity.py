@@ -196,10 +196,11 @@ def test_prefill_back_to_back_single_launch(L):
 
 
 # The single launch's column slab follows from the number of chunk-heads (P halved until
-# there is a workgroup per compute unit, at most 64 columns), so the number of sequences
-# picks it: with P = 128, 8 heads and 4 chunks, 2 sequences give slabs of 32 columns, 4
-# give 64, and 8 give 64 with two workgroups per compute unit (the later chunks' waits
-# span dispatch rounds).
+# there is a workgroup per compute unit; at most 64 columns where N = 64, whole heads of
+# 128 where N = 128), so the number of sequences picks it: with P = 128, 8 heads and 4
+# chunks, 2 sequences give slabs of 32 columns, 4 give 64, and 8 give 64 (N = 64, two
+# workgroups per compute unit: the later chunks' waits span dispatch rounds) or whole heads
+# (N = 128).
 SCAN_CONFIGS = [(64, 2), (64, 4), (64, 8), (128, 2), (128, 4), (128, 8)]
 
 
@@ -305,6 +306,48 @@ def test_single_launch_continue(want_y):
         assert y_err(sync_np(y2), ry) <= BOUND[synth.BF16]
     assert state_err(logical_state(cache), rs) <= BOUND[synth.BF16]
     assert cache.pos().cpu().tolist() == [L1 + int(j[0]) + L2, L1 + int(j[1]) + L2]
+
+
+# Where N = 128 and the prompt has at least one workgroup per compute unit at 128 columns
+# (sequences x chunks x heads >= 256), the single launch takes whole heads (no column slabs):
+# each C B^T tile and its decay mask is formed once per head, the light waves store their
+# state tiles as they form them and read them back later, and the carried state reuses
+# X^T's LDS.  These cases reach that form: one short chunk per sequence (chunk 0 is also
+# the last), and several chunks continuing from a committed state, with y or without.
+WIDE_CASES = [("one_chunk", 8, 200, 0), ("continue_y", 2, 1000, 1), ("continue_state", 2, 1000, 2)]
+
+
+@pytest.mark.parametrize("name,Bt,L,mode", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_single_launch_whole_heads(name, Bt, L, mode):
+    from speculative_decode_amd import _lib
+    H, P, N, G, L1, K = 32, 128, 128, 8, 300, 4
+    rng = np.random.default_rng(4800 + mode)
+    layer, tok = make_layer_and_tokens(rng, Bt, L1 + K + L, H, P, N, G, synth.BF16, "tiny")
+    A, D = dev_layer(layer)
+    cache = SSMCache(Bt, H, P, N, G, K, synth.BF16)
+    assert _lib.lib().mil_ssm_prefill_kernels(ctypes.byref(cache.desc), Bt, L, 256) == \
+        1 << _lib.TRACE["prefill_scan"]
+    print(f"single-launch whole heads {name}", flush=True)
+    c = synth.slice_tokens(tok, 0, Bt, L1 + K, L1 + K + L)
+    h1 = None
+    if mode:
+        a = synth.slice_tokens(tok, 0, Bt, 0, L1)
+        d = synth.slice_tokens(tok, 0, Bt, L1, L1 + K)
+        cache.prefill(*dev_tokens(a), A, D, chunk=256)
+        dx, dB, dC, ddt = dev_tokens(d)
+        cache.verify(dx, dB, dC, ddt, A, D)
+        j = np.array([3, 0], dtype=np.int32)
+        cache.commit(torch.from_numpy(j).cuda(), dx, dB, ddt)
+        _, h1 = oracle.prefill(a.x.f64, a.B.f64, a.C.f64, a.dt.f64, layer.A.f64, layer.D.f64)
+        h1 = oracle.commit(h1, d.x.f64, d.B.f64, d.dt.f64, layer.A.f64, layer.D.f64, j)
+    y = cache.prefill(*dev_tokens(c), A, D, chunk=256, cont=bool(mode), want_y=mode != 2)
+    torch.cuda.synchronize()
+    assert cache.status() == -1
+    ry, rs = oracle.prefill(c.x.f64, c.B.f64, c.C.f64, c.dt.f64, layer.A.f64, layer.D.f64, h0=h1)
+    es = state_err(logical_state(cache), rs)
+    ey = y_err(sync_np(y), ry) if mode != 2 else 0.0
+    print(f"  y {ey:.2e} state {es:.2e}")
+    assert ey <= BOUND[synth.BF16] and es <= BOUND[synth.BF16]
 
 
 # --------------------------------------------------------------------------- verify / commit
