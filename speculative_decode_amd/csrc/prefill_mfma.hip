@@ -1201,145 +1201,258 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     // j0+1..c-1 in order, h <- E_j h + S_j.  Every inclusive record is that same fold in
     // the same order, back to chunk 0's E_0 h0 + S_0, so h_in is bit for bit the state of
     // a sequential pass over the chunks, whichever j0 the wait ends at. ----
-    // the wide form's chunk 0 reads h0 again here, from where it parked it (no registers
-    // held through the rows)
-    if (kWide && c == 0 && owner) {
+    // The whole-head form: after the rows all eight waves take part, each with two of the
+    // head's sixteen state tiles (row tile snt, column tiles 2 jpart and 2 jpart + 1), so
+    // that more of the records are in flight at once; each wave keeps several links of the
+    // fold in flight (loads clamped to the last link, the fold of a link past the end a
+    // select, so that no branch makes the compiler wait).
+    constexpr int WT = 2;  // tiles per wave
+    constexpr int LD = 2;  // links of the fold in flight
+    f32x16 hinw[WT];
 #pragma unroll
-        for (int i = 0; i < TPWL; ++i) {
-            const int tl = snt + NTL * (jpart + LW * i);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = p.cont ? shared_load4(agr, (int)(((size_t)tl * 1024 + (q * 64 + lane) * 4) * 4)) : f32x4{};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) hin[i][4 * q + u] = v[u];
+    for (int i = 0; i < WT; ++i) hinw[i] = f32x16{};
+    if constexpr (kWide) {
+        auto wtile = [&](int i) { return snt + NTL * (2 * jpart + i); };
+        auto rec4 = [&](size_t off, int tl, int q) {
+            return shared_load4(agr, (int)((off + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+        };
+        // what the light waves published (S_c; chunk 0: h0 and its inclusive state) is
+        // complete before any wave reads it back: they counted themselves after their stores
+        if (lane == 0) {
+            for (int spin = 0; spin < (1 << 20); ++spin) {
+                if (__hip_atomic_load(sCnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
+                __builtin_amdgcn_s_sleep(1);
             }
         }
-    }
-    if (c > 0 && owner) {
-        const long long tw0 = (long long)__builtin_amdgcn_s_memrealtime();
-        int j0 = 0;
-        while (true) {
-            const int f = lane < c ? scan_load(flags + (c - 1 - lane)) : 0;
-            const bool ready = lane < c && (static_cast<uint32_t>(f) >> 2) == static_cast<uint32_t>(epoch);
-            const uint64_t mi = __ballot(ready && (f & 3) == kFlagInclusive);
-            const uint64_t mr = __ballot(ready);
-            if (mi) {
-                const int d = __builtin_ctzll(mi);            // nearest inclusive: chunk c-1-d
-                const uint64_t need = (1ull << d) - 1;        // chunks c-d..c-1: aggregates at least
-                if ((mr & need) == need) {
-                    j0 = c - 1 - d;
+        asm volatile("" ::: "memory");
+        if (c == 0) {
+            if (p.cont) {
+#pragma unroll
+                for (int i = 0; i < WT; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v = rec4(0, wtile(i), q);  // h0, parked in the aggregate area
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) hinw[i][4 * q + u] = v[u];
+                    }
+            }
+        } else {
+            const long long tw0 = (long long)__builtin_amdgcn_s_memrealtime();
+            int j0 = 0;
+            while (true) {
+                const int f = lane < c ? scan_load(flags + (c - 1 - lane)) : 0;
+                const bool ready = lane < c && (static_cast<uint32_t>(f) >> 2) == static_cast<uint32_t>(epoch);
+                const uint64_t mi = __ballot(ready && (f & 3) == kFlagInclusive);
+                const uint64_t mr = __ballot(ready);
+                if (mi) {
+                    const int d = __builtin_ctzll(mi);
+                    const uint64_t need = (1ull << d) - 1;
+                    if ((mr & need) == need) {
+                        j0 = c - 1 - d;
+                        break;
+                    }
+                }
+                __builtin_amdgcn_s_sleep(2);
+                if ((long long)__builtin_amdgcn_s_memrealtime() - tw0 > kScanWaitTicks) {
+                    if (lane == 0) atomicOr(p.err + slot, MIL_DEVERR_SCAN);
                     break;
                 }
             }
-            __builtin_amdgcn_s_sleep(2);
-            if ((long long)__builtin_amdgcn_s_memrealtime() - tw0 > kScanWaitTicks) {
-                if (lane == 0) atomicOr(p.err + slot, MIL_DEVERR_SCAN);
-                break;
-            }
-        }
-        // every earlier chunk of the row has published, so has read the old epoch: this
-        // launch's epoch becomes the row's (also after a timeout, so that no flag of this
-        // launch is ever above the row's epoch)
-        if (last && wave == 0 && lane == 0) scan_store(flags + kScanEpoch, epoch);
-        asm volatile("" ::: "memory");  // the records are read after the flags
-        // j0's inclusive tiles, then the aggregates j0+1..c-1, the next one's loads (clamped
-        // to the last, so that no branch makes the compiler wait for every load) in flight
-        // while one is folded in; the wide form walks the records once per pair of tiles
-        // (fewer registers in flight)
-        constexpr int LBG = kWide ? 2 : TPWL;  // tiles folded together
+            if (last && wave == 0 && lane == 0) scan_store(flags + kScanEpoch, epoch);
+            asm volatile("" ::: "memory");  // the records are read after the flags
+            f32x16 buf[LD][WT];
+            float eb[LD];
 #pragma unroll
-        for (int g0 = 0; g0 < TPWL; g0 += LBG) {
-            f32x16 nx[LBG];
-            float en = 0.f;
-            const int ja = min(j0 + 1, c - 1);
-#pragma unroll
-            for (int ii = 0; ii < LBG; ++ii) {
-                const int tl = snt + NTL * (jpart + LW * (g0 + ii));
+            for (int i = 0; i < WT; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int lo = (q * 64 + lane) * 4 + tl * 1024;
-                    const f32x4 v = shared_load4(agr, (int)(((size_t)j0 * REC + INC + lo) * 4));
-                    const f32x4 a = shared_load4(agr, (int)(((size_t)ja * REC + lo) * 4));
+                    const f32x4 v = rec4((size_t)j0 * REC + INC, wtile(i), q);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        hin[g0 + ii][4 * q + u] = v[u];
-                        nx[ii][4 * q + u] = a[u];
-                    }
+                    for (int u = 0; u < 4; ++u) hinw[i][4 * q + u] = v[u];
                 }
-            }
-            en = shared_load(recs + (size_t)ja * REC + (size_t)N * PC);
-            for (int j = j0 + 1; j < c; ++j) {
-                f32x16 cur[LBG];
 #pragma unroll
-                for (int ii = 0; ii < LBG; ++ii) cur[ii] = nx[ii];
-                const float e = en;
-                const int jn = min(j + 1, c - 1);
-                en = shared_load(recs + (size_t)jn * REC + (size_t)N * PC);
+            for (int d = 0; d < LD; ++d) {
+                const int jj = min(j0 + 1 + d, c - 1);
 #pragma unroll
-                for (int ii = 0; ii < LBG; ++ii) {
-                    const int tl = snt + NTL * (jpart + LW * (g0 + ii));
+                for (int i = 0; i < WT; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = shared_load4(agr, (int)(((size_t)jn * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+                        const f32x4 v = rec4((size_t)jj * REC, wtile(i), q);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) nx[ii][4 * q + u] = v[u];
+                        for (int u = 0; u < 4; ++u) buf[d][i][4 * q + u] = v[u];
+                    }
+                eb[d] = shared_load(recs + (size_t)jj * REC + (size_t)N * PC);
+            }
+            for (int j = j0 + 1; j < c; j += LD) {
+#pragma unroll
+                for (int d = 0; d < LD; ++d) {
+                    const bool use = j + d < c;  // links past the end: loads clamped, fold skipped
+                    const float e = eb[d];
+#pragma unroll
+                    for (int i = 0; i < WT; ++i)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float f = __builtin_fmaf(e, hinw[i][r], buf[d][i][r]);
+                            hinw[i][r] = use ? f : hinw[i][r];
+                        }
+                    const int jj = min(j + d + LD, c - 1);
+#pragma unroll
+                    for (int i = 0; i < WT; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x4 v = rec4((size_t)jj * REC, wtile(i), q);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) buf[d][i][4 * q + u] = v[u];
+                        }
+                    eb[d] = shared_load(recs + (size_t)jj * REC + (size_t)N * PC);
+                }
+            }
+            // the state after this chunk, E_c h_in + S_c (S_c read back), for the chunks after it
+            if (!last) {
+#pragma unroll
+                for (int i = 0; i < WT; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 s4 = rec4((size_t)c * REC, wtile(i), q);
+                        f32x4 v;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) v[u] = __builtin_fmaf(Ec, hinw[i][4 * q + u], s4[u]);
+                        shared_store4(agr, (int)(((size_t)c * REC + INC + (size_t)wtile(i) * 1024 + (q * 64 + lane) * 4) * 4), v);
+                    }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                // the aggregate count (four light waves) was seen above; the eighth wave past
+                // its inclusive tiles raises the flag
+                if (lane == 0 && atomicAdd(sCnt2, 1) == 7) scan_store(flags + c, scan_flag(epoch, kFlagInclusive));
+            }
+        }
+        // the final state: chunk 0's inclusive record, or E_c h_in + S_c
+        if (last) {
+#pragma unroll
+            for (int i = 0; i < WT; ++i) {
+                const int pt = 2 * jpart + i;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = rec4((size_t)c * REC + (c == 0 ? INC : 0), wtile(i), q);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = 4 * q + u;
+                        const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                        cache[(size_t)n * P + pc0 + pt * kT + l32] = c == 0 ? v[u] : __builtin_fmaf(Ec, hinw[i][r], v[u]);
                     }
                 }
-#pragma unroll
-                for (int ii = 0; ii < LBG; ++ii)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) hin[g0 + ii][r] = __builtin_fmaf(e, hin[g0 + ii][r], cur[ii][r]);
             }
         }
-        // the state after this chunk, E_c h_in + S_c, for the chunks after it
-        if (!last) {
-#pragma unroll
+    } else {
+        if (c > 0 && owner) {
+            const long long tw0 = (long long)__builtin_amdgcn_s_memrealtime();
+            int j0 = 0;
+            while (true) {
+                const int f = lane < c ? scan_load(flags + (c - 1 - lane)) : 0;
+                const bool ready = lane < c && (static_cast<uint32_t>(f) >> 2) == static_cast<uint32_t>(epoch);
+                const uint64_t mi = __ballot(ready && (f & 3) == kFlagInclusive);
+                const uint64_t mr = __ballot(ready);
+                if (mi) {
+                    const int d = __builtin_ctzll(mi);            // nearest inclusive: chunk c-1-d
+                    const uint64_t need = (1ull << d) - 1;        // chunks c-d..c-1: aggregates at least
+                    if ((mr & need) == need) {
+                        j0 = c - 1 - d;
+                        break;
+                    }
+                }
+                __builtin_amdgcn_s_sleep(2);
+                if ((long long)__builtin_amdgcn_s_memrealtime() - tw0 > kScanWaitTicks) {
+                    if (lane == 0) atomicOr(p.err + slot, MIL_DEVERR_SCAN);
+                    break;
+                }
+            }
+            // every earlier chunk of the row has published, so has read the old epoch: this
+            // launch's epoch becomes the row's (also after a timeout, so that no flag of this
+            // launch is ever above the row's epoch)
+            if (last && wave == 0 && lane == 0) scan_store(flags + kScanEpoch, epoch);
+            asm volatile("" ::: "memory");  // the records are read after the flags
+            // j0's inclusive tiles, then the aggregates j0+1..c-1, the next one's loads (clamped
+            // to the last, so that no branch makes the compiler wait for every load) in flight
+            // while one is folded in
+            constexpr int LBG = TPWL;  // tiles folded together
+    #pragma unroll
+            for (int g0 = 0; g0 < TPWL; g0 += LBG) {
+                f32x16 nx[LBG];
+                float en = 0.f;
+                const int ja = min(j0 + 1, c - 1);
+    #pragma unroll
+                for (int ii = 0; ii < LBG; ++ii) {
+                    const int tl = snt + NTL * (jpart + LW * (g0 + ii));
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int lo = (q * 64 + lane) * 4 + tl * 1024;
+                        const f32x4 v = shared_load4(agr, (int)(((size_t)j0 * REC + INC + lo) * 4));
+                        const f32x4 a = shared_load4(agr, (int)(((size_t)ja * REC + lo) * 4));
+    #pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            hin[g0 + ii][4 * q + u] = v[u];
+                            nx[ii][4 * q + u] = a[u];
+                        }
+                    }
+                }
+                en = shared_load(recs + (size_t)ja * REC + (size_t)N * PC);
+                for (int j = j0 + 1; j < c; ++j) {
+                    f32x16 cur[LBG];
+    #pragma unroll
+                    for (int ii = 0; ii < LBG; ++ii) cur[ii] = nx[ii];
+                    const float e = en;
+                    const int jn = min(j + 1, c - 1);
+                    en = shared_load(recs + (size_t)jn * REC + (size_t)N * PC);
+    #pragma unroll
+                    for (int ii = 0; ii < LBG; ++ii) {
+                        const int tl = snt + NTL * (jpart + LW * (g0 + ii));
+    #pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x4 v = shared_load4(agr, (int)(((size_t)jn * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
+    #pragma unroll
+                            for (int u = 0; u < 4; ++u) nx[ii][4 * q + u] = v[u];
+                        }
+                    }
+    #pragma unroll
+                    for (int ii = 0; ii < LBG; ++ii)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) hin[g0 + ii][r] = __builtin_fmaf(e, hin[g0 + ii][r], cur[ii][r]);
+                }
+            }
+            // the state after this chunk, E_c h_in + S_c, for the chunks after it
+            if (!last) {
+    #pragma unroll
+                for (int i = 0; i < TPWL; ++i) {
+                    const int tl = snt + NTL * (jpart + LW * i);
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f32x4 v;
+                        const f32x4 s4 = {sacc[i][4 * q], sacc[i][4 * q + 1], sacc[i][4 * q + 2], sacc[i][4 * q + 3]};
+    #pragma unroll
+                        for (int u = 0; u < 4; ++u) v[u] = __builtin_fmaf(Ec, hin[i][4 * q + u], s4[u]);
+                        shared_store4(agr, (int)(((size_t)c * REC + INC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
+                    }
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (lane == 0) {
+                    // the aggregate flag (raised by the fourth light wave) goes up before this one
+                    for (int spin = 0; spin < (1 << 20); ++spin) {
+                        if (__hip_atomic_load(sCnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    if (atomicAdd(sCnt2, 1) == NOWN - 1) scan_store(flags + c, scan_flag(epoch, kFlagInclusive));
+                }
+            }
+        }
+        // ---- the final state, from the last chunk (nothing reads h0 after chunk 0 has) ----
+        if (last && owner) {
+    #pragma unroll
             for (int i = 0; i < TPWL; ++i) {
-                const int tl = snt + NTL * (jpart + LW * i);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f32x4 v;
-                    const f32x4 s4 = kWide ? shared_load4(agr, (int)(((size_t)c * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4))
-                                           : f32x4{sacc[i][4 * q], sacc[i][4 * q + 1], sacc[i][4 * q + 2], sacc[i][4 * q + 3]};
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) v[u] = __builtin_fmaf(Ec, hin[i][4 * q + u], s4[u]);
-                    shared_store4(agr, (int)(((size_t)c * REC + INC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
+                const int pt = jpart + LW * i;
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
+                    cache[(size_t)n * P + pc0 + pt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
                 }
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (lane == 0) {
-                // the aggregate flag (raised by the fourth light wave) goes up before this one
-                for (int spin = 0; spin < (1 << 20); ++spin) {
-                    if (__hip_atomic_load(sCnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= 4) break;
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                if (atomicAdd(sCnt2, 1) == NOWN - 1) scan_store(flags + c, scan_flag(epoch, kFlagInclusive));
-            }
-        }
-    }
-    // ---- the final state, from the last chunk (nothing reads h0 after chunk 0 has) ----
-    if (last && owner) {
-#pragma unroll
-        for (int i = 0; i < TPWL; ++i) {
-            const int pt = jpart + LW * i;
-            f32x16 sc;
-            if constexpr (kWide) {
-                // chunk 0: its inclusive record is the final state; later chunks: S_c
-                const int tl = snt + NTL * pt;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = shared_load4(agr, (int)(((size_t)c * REC + (c == 0 ? INC : 0) + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) sc[4 * q + u] = v[u];
-                }
-            } else {
-                sc = sacc[i];
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
-                cache[(size_t)n * P + pc0 + pt * kT + l32] =
-                    (kWide && c == 0) ? sc[r] : __builtin_fmaf(Ec, hin[i][r], sc[r]);
             }
         }
     }
@@ -1355,8 +1468,22 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     }
     if (has_hin) {
         // the carried state as [p][n] groups of 8 hi + 8 lo bf16
-        if constexpr (kWide) __syncthreads();  // every wave is done with X^T
-        if (owner) {
+        if constexpr (kWide) {
+            __syncthreads();  // every wave is done with X^T
+#pragma unroll
+            for (int i = 0; i < WT; ++i) {
+                bf16 *row = sH + ((2 * jpart + i) * kT + l32) * HS;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int grp = snt * 4 + q;  // n group of 8: 8 hi then 8 lo
+                    uint2 hi4, lo4;
+                    split2(hinw[i][4 * q], hinw[i][4 * q + 1], hi4.x, lo4.x);
+                    split2(hinw[i][4 * q + 2], hinw[i][4 * q + 3], hi4.y, lo4.y);
+                    *reinterpret_cast<uint2 *>(row + grp * 16 + 4 * hf) = hi4;
+                    *reinterpret_cast<uint2 *>(row + grp * 16 + 8 + 4 * hf) = lo4;
+                }
+            }
+        } else if (owner) {
 #pragma unroll
             for (int i = 0; i < TPWL; ++i) {
                 const int pt = jpart + LW * i;
