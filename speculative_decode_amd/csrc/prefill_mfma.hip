@@ -97,6 +97,7 @@ struct MParams {
     int t0;                // single launch: token index of this launch's first chunk
     int book;              // single launch: this launch sets pos / pending (the last launch of a prefill)
     int pos_add;           // single launch: the caller's continue flag (pos grows by L, every slot's pending is 0)
+    int incl_every;        // single launch: chunks c > 0 with (c + 1) % incl_every == 0 publish their inclusive state
     int32_t *err;          // [batch] device error words
     float *chain;          // [nseq][H][P/PC][nch][N*PC + 16] published chunk states (register order), E_c
 };
@@ -938,6 +939,11 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
     float *cache = p.state + (size_t)(seq * H + h) * p.head_stride;
     const bool has_hin = p.cont || c > 0;
     const bool last = c == p.nch - 1;
+    // the state after the chunk is published by the last chunk of each dispatch round only:
+    // the chunks of one round look back at the same time, so none finds another's, and a
+    // later round's look-back ends at the nearest one (any chunk's inclusive state is the
+    // same fold, so where a look-back ends changes no bit; chunk 0 always publishes)
+    const bool pub_inc = !last && (c + 1) % p.incl_every == 0;
 
     // ---- the chunk's own state S[n][p] (this slab): S = sum_s (w_s B_s) x_s^T with
     // A operand (w B)^T and B operand X^T (as staged).  The rows n of B^T come off the
@@ -1308,7 +1314,7 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                 }
             }
             // the state after this chunk, E_c h_in + S_c (S_c read back), for the chunks after it
-            if (!last) {
+            if (pub_inc) {
 #pragma unroll
                 for (int i = 0; i < WT; ++i)
 #pragma unroll
@@ -1374,20 +1380,20 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
             // to the last, so that no branch makes the compiler wait for every load) in flight
             // while one is folded in
             constexpr int LBG = TPWL;  // tiles folded together
-    #pragma unroll
+#pragma unroll
             for (int g0 = 0; g0 < TPWL; g0 += LBG) {
                 f32x16 nx[LBG];
                 float en = 0.f;
                 const int ja = min(j0 + 1, c - 1);
-    #pragma unroll
+#pragma unroll
                 for (int ii = 0; ii < LBG; ++ii) {
                     const int tl = snt + NTL * (jpart + LW * (g0 + ii));
-    #pragma unroll
+#pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int lo = (q * 64 + lane) * 4 + tl * 1024;
                         const f32x4 v = shared_load4(agr, (int)(((size_t)j0 * REC + INC + lo) * 4));
                         const f32x4 a = shared_load4(agr, (int)(((size_t)ja * REC + lo) * 4));
-    #pragma unroll
+#pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             hin[g0 + ii][4 * q + u] = v[u];
                             nx[ii][4 * q + u] = a[u];
@@ -1397,37 +1403,37 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
                 en = shared_load(recs + (size_t)ja * REC + (size_t)N * PC);
                 for (int j = j0 + 1; j < c; ++j) {
                     f32x16 cur[LBG];
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < LBG; ++ii) cur[ii] = nx[ii];
                     const float e = en;
                     const int jn = min(j + 1, c - 1);
                     en = shared_load(recs + (size_t)jn * REC + (size_t)N * PC);
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < LBG; ++ii) {
                         const int tl = snt + NTL * (jpart + LW * (g0 + ii));
-    #pragma unroll
+#pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const f32x4 v = shared_load4(agr, (int)(((size_t)jn * REC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4));
-    #pragma unroll
+#pragma unroll
                             for (int u = 0; u < 4; ++u) nx[ii][4 * q + u] = v[u];
                         }
                     }
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < LBG; ++ii)
-    #pragma unroll
+#pragma unroll
                         for (int r = 0; r < 16; ++r) hin[g0 + ii][r] = __builtin_fmaf(e, hin[g0 + ii][r], cur[ii][r]);
                 }
             }
             // the state after this chunk, E_c h_in + S_c, for the chunks after it
-            if (!last) {
-    #pragma unroll
+            if (pub_inc) {
+#pragma unroll
                 for (int i = 0; i < TPWL; ++i) {
                     const int tl = snt + NTL * (jpart + LW * i);
-    #pragma unroll
+#pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         f32x4 v;
                         const f32x4 s4 = {sacc[i][4 * q], sacc[i][4 * q + 1], sacc[i][4 * q + 2], sacc[i][4 * q + 3]};
-    #pragma unroll
+#pragma unroll
                         for (int u = 0; u < 4; ++u) v[u] = __builtin_fmaf(Ec, hin[i][4 * q + u], s4[u]);
                         shared_store4(agr, (int)(((size_t)c * REC + INC + (size_t)tl * 1024 + (q * 64 + lane) * 4) * 4), v);
                     }
@@ -1445,10 +1451,10 @@ __global__ __launch_bounds__(512) void chunk_scan_mfma(const MParams p) {
         }
         // ---- the final state, from the last chunk (nothing reads h0 after chunk 0 has) ----
         if (last && owner) {
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < TPWL; ++i) {
                 const int pt = jpart + LW * i;
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int n = snt * kT + 8 * (r / 4) + 4 * hf + (r % 4);
                     cache[(size_t)n * P + pc0 + pt * kT + l32] = __builtin_fmaf(Ec, hin[i][r], sacc[i][r]);
@@ -1561,6 +1567,19 @@ constexpr int64_t kOutItemsTarget = 256;  // output workgroups wanted (one per c
 
 // Column slab width of the output work (and of the single launch): P split until the grid
 // has a workgroup per compute unit.
+// Compute units of the current device (cached per device; 256 if the query fails).
+int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 int slab_width(int nseq, int nch, int H, int P) {
     int pc = P;
     while (pc > kT && (int64_t)nseq * nch * H * (P / pc) < kOutItemsTarget) pc /= 2;
@@ -1636,6 +1655,7 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
     p.t0 = 0;
     p.book = 1;
     p.pos_add = p.cont;
+    p.incl_every = 1;
     p.scan = nullptr;
     p.err = nullptr;
     p.chain = nullptr;
@@ -1656,12 +1676,15 @@ hipError_t launch_prefill_mfma(const CacheImpl &c, int slot0, int nseq, int L, i
         p.err = cache_err(c);
         p.chain = static_cast<float *>(ws);
         p.pos_add = cont ? 1 : 0;
+        const int cus = compute_units();
         for (int c0 = 0; c0 < nch_all; c0 += kScanChunks) {
             p.nch = std::min(kScanChunks, nch_all - c0);
             p.t0 = c0 * chunk;
             p.cont = (cont || c0 > 0) ? 1 : 0;
             p.book = c0 + p.nch == nch_all ? 1 : 0;
             const int spc = scan_slab(nseq, p.nch, p.H, p.P, p.N);
+            // one workgroup per compute unit (its LDS): a dispatch round holds this many chunks
+            p.incl_every = std::max(1, cus / (nseq * p.H * (p.P / spc)));
             const void *kf = scan_kernel(chunk, p.N, spc);
             if (!kf) return hipErrorInvalidValue;
             hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
