@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void greedy_accept_kernel(const GreedyParams g
     int64_t tail = lo;
     if (g.vec) {
         constexpr int E = 16 / sizeof(T);  // lo is a multiple of 8, so of E
-        constexpr int U = 4;               // 16-byte loads in flight per thread
+        constexpr int U = 8;               // 16-byte loads in flight per thread
         const uint4 *row4 = reinterpret_cast<const uint4 *>(row);
         const int64_t v0 = lo / E, v1 = hi / E;
         for (int64_t base4 = v0 + threadIdx.x; base4 < v1; base4 += 256 * U) {
@@ -490,10 +490,11 @@ hipError_t launch_commit(const CacheImpl &c, int K, const int32_t *accepted, con
 }
 
 // Vocabulary splits per (slot, draft) row: enough workgroups to spread over the chip
-// (about 2048 in all), each split at least 2048 logits.
+// (about 1024 in all, four per compute unit: against 2048 smaller ones, a shorter dispatch
+// ramp with as many loads in flight), each split at least 2048 logits.
 int greedy_splits(int batch, int K, int64_t vocab) {
     const int64_t rows = (int64_t)batch * K;
-    int64_t S = (2048 + rows - 1) / rows;
+    int64_t S = (1024 + rows - 1) / rows;
     S = std::min<int64_t>(S, (vocab + 2047) / 2048);
     return (int)std::max<int64_t>(1, std::min<int64_t>(S, kGreedySplitsMax));
 }
