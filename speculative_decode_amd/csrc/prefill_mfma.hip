@@ -702,24 +702,26 @@ __global__ __launch_bounds__(512) void chunk_out_mfma(const MParams p) {
 }
 
 // ------------------------------------------------------------------ single launch
-// All three phases in one launch for prompts of up to kScanChunks chunks, one workgroup per
-// (chunk, sequence, head, column slab), chunk-major.  The workgroup stages its chunk's B,
-// C, X and dt once, computes the chunk's own state contribution S_c = sum_s (w_s B_s) x_s^T
-// on the matrix cores and publishes it with the chunk's total decay E_c (chunk 0 publishes
-// its outgoing state E_0 h0 + S_0 instead, so that it alone reads h0), forms the
-// intra-chunk outputs, raises its flag, and then folds the state entering its chunk
-// through chunks 0..c-1 in order (h <- E_i h + S_i): the operations of a sequential pass in
-// its order, so the result does not depend on timing, and no workgroup waits on a chain
-// of others, only on the publications.  The last chunk writes the final state.  Flags
-// hold a per-call value that comes from the device: each (slot, head, slab) row keeps the
-// epoch its last call raised its flags to; every workgroup of this call reads it at its
-// start and raises its flag to epoch + 1, and the last chunk stores epoch + 1 as the
-// row's epoch once its wait is over, which is after every workgroup of the row has read
-// the old value (each of them publishes before the last chunk's wait can end).  So no
-// flag left by an earlier call, a graph replay or a byte copy of the cache equals this
-// call's value, and nothing needs resetting.
-// Longer prompts keep the three launches (their per-chunk reads of all earlier chunks
-// would grow with the square of the count).
+// All three phases in one launch for up to kScanChunks chunks (longer prompts take several
+// launches, each continuing from the state the one before wrote), one workgroup per
+// (chunk, sequence, head, column slab), chunk-major; the slab is 64 columns or fewer, or the
+// whole 128-column head for long prompts at N = 128.  The workgroup stages its chunk's B, C,
+// X and dt once, forms the chunk's own state contribution S_c = sum_s (w_s B_s) x_s^T on the
+// matrix cores and publishes it with the chunk's total decay E_c (the aggregate; chunk 0
+// publishes its outgoing state E_0 h0 + S_0 instead, the inclusive state, so that it alone
+// reads h0), forms the intra-chunk outputs, then finds the state entering its chunk by
+// decoupled look-back: the nearest earlier chunk that has published its inclusive state,
+// folded forward through the aggregates after it (h <- E_i h + S_i, in chunk order).  Every
+// inclusive state is that same fold back to chunk 0, so the result does not depend on where
+// a look-back ends, and no workgroup waits on a chain of others.  The last chunk of each
+// dispatch round publishes its inclusive state for the rounds after it; the last chunk of
+// the prompt writes the final state.  Flags hold a per-call value that comes from the
+// device: each (slot, head, slab) row keeps the epoch its last call raised its flags to;
+// every workgroup of this call reads it at its start and raises its flag to epoch + 1, and
+// the last chunk stores epoch + 1 as the row's epoch once its wait is over, which is after
+// every workgroup of the row has read the old value (each of them publishes before the
+// last chunk's wait can end).  So no flag left by an earlier call, a graph replay or a byte
+// copy of the cache equals this call's value, and nothing needs resetting.
 //
 // Ordering: workgroups start in chunk-major order and every one publishes before it
 // waits, so the flags a workgroup waits for are always raised; the wait is bounded in time
